@@ -1,0 +1,406 @@
+"""Pins for the fp64 oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle (optionally a separately
+built copy, passed as ``lib``) disagrees with:
+  * a library routine: torch's scaled_dot_product_attention in float64 on the CPU
+    (the dense special case tau = -inf, and the output given a key mask);
+  * brute force in numpy long double on tiny inputs;
+  * closed forms: uniform scores give exact means of V; hand-built worked examples
+    whose outputs and masks are derived by hand below;
+  * invariants: closed form == scan form, monotone skip set in tau, the first tile of
+    every scan is kept, tau = -inf skips nothing, the dropped-mass bound, split-count
+    invariance at tau = -inf.
+
+The rule being pinned (recap of "Accelerating Long-Context Inference with Skip Softmax in
+NVIDIA TensorRT-LLM", Key Points / Detailed Analysis / Skip Softmax Mechanism; news item
+"Understanding Skip Softmax"): a key tile is skipped when its local score maximum falls
+below the running maximum by more than tau, for every row of the unit.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+LN1000 = math.log(1000.0)
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------- references
+def sdpa_prefill(q, k, v, causal, scale=None, key_mask=None):
+    """torch SDPA in float64; q [B,S,Hq,d], k/v [B,S,Hkv,d] -> [B,S,Hq,d].  key_mask [B,Hq,S,S] bool."""
+    qt = torch.from_numpy(np.asarray(q, np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(np.asarray(k, np.float64)).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(np.asarray(v, np.float64)).permute(0, 2, 1, 3)
+    G = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(G, dim=1)
+    vt = vt.repeat_interleave(G, dim=1)
+    if key_mask is None:
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=scale)
+    else:
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(key_mask),
+                                                             scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def sdpa_decode(q, k, v, kv_lens, scale=None):
+    """q [B,Hq,d], k/v [B,Hkv,smax,d] -> [B,Hq,d] over keys j < kv_len[b]."""
+    B, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        n = int(kv_lens[b])
+        if n == 0:
+            continue
+        qt = torch.from_numpy(np.asarray(q[b], np.float64))[:, None, :]
+        kt = torch.from_numpy(np.asarray(k[b, :, :n], np.float64)).repeat_interleave(G, dim=0)
+        vt = torch.from_numpy(np.asarray(v[b, :, :n], np.float64)).repeat_interleave(G, dim=0)
+        out[b] = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[:, 0].numpy()
+    return out
+
+
+def brute_prefill_longdouble(q, k, v, causal):
+    """Two-pass safe softmax attention with explicit loops in numpy long double (tiny inputs only)."""
+    B, S, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    ld = np.longdouble
+    out = np.zeros((B, S, Hq, d), dtype=ld)
+    sc = ld(1) / np.sqrt(ld(d))
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(S):
+                n = i + 1 if causal else S
+                logits = [sc * sum(ld(q[b, i, h, c]) * ld(k[b, j, h // G, c]) for c in range(d)) for j in range(n)]
+                m = max(logits)
+                w = [np.exp(x - m) for x in logits]
+                z = sum(w)
+                for c in range(d):
+                    out[b, i, h, c] = sum(w[j] * ld(v[b, j, h // G, c]) for j in range(n)) / z
+    return out
+
+
+def unit_rows(res_out, B, S, Hq, tile_q):
+    """Reassemble oracle per-unit prefill output [n,Tq,d] (all units) into [B,S,Hq,d]."""
+    nqt = -(-S // tile_q)
+    d = res_out.shape[-1]
+    o = res_out.reshape(B, Hq, nqt * tile_q, d)[:, :, :S]
+    return o.transpose(0, 2, 1, 3)
+
+
+def prefill_inputs(seed, B, S, Hq, Hkv, d, planted=0, amp=12.0):
+    """Random fp64 inputs; ``planted`` key tiles (of 64) per KV head get +amp logits along a common direction."""
+    r = rng(seed)
+    q = r.standard_normal((B, S, Hq, d))
+    k = r.standard_normal((B, S, Hkv, d))
+    v = r.standard_normal((B, S, Hkv, d))
+    if planted:
+        u = r.standard_normal(d)
+        u /= np.linalg.norm(u)
+        mu = math.sqrt(d)
+        q = q - np.einsum("bshd,d->bsh", q, u)[..., None] * u + mu * u  # common mode mu along u
+        nt = -(-S // 64)
+        for b in range(B):
+            for g in range(Hkv):
+                for t in r.choice(np.arange(1, nt), size=min(planted, nt - 1), replace=False):
+                    k[b, t * 64:(t + 1) * 64, g] += amp * math.sqrt(d) / mu * u
+    return q, k, v
+
+
+# ----------------------------------------------------------------- pins
+def pin_dense_prefill(lib=None):
+    """tau = -inf equals dense softmax attention (SDPA float64), causal and not, GQA, ragged S."""
+    cases = [(1, 1, 1, 1, 64, 64, 64), (1, 63, 2, 1, 64, 64, 64), (1, 65, 4, 2, 64, 128, 64),
+             (2, 130, 4, 1, 128, 128, 64), (1, 200, 8, 2, 64, 64, 64), (1, 64, 2, 2, 16, 64, 64)]
+    for seed, (B, S, Hq, Hkv, d, Tq, Tk) in enumerate(cases):
+        q, k, v = prefill_inputs(seed, B, S, Hq, Hkv, d)
+        for causal in (True, False):
+            r = oracle.prefill(q, k, v, causal=causal, tau=-math.inf, tile_q=Tq, tile_k=Tk, lib=lib)
+            got = unit_rows(r["out"], B, S, Hq, Tq)
+            ref = sdpa_prefill(q, k, v, causal)
+            err = np.abs(got - ref).max()
+            assert err < 1e-12, f"dense prefill mismatch {err} case {(B, S, Hq, Hkv, d, causal)}"
+            assert (r["state"] != oracle.SKIPPED).all()
+
+
+def pin_dense_decode(lib=None):
+    """tau = -inf decode equals dense single-query attention for every split count, incl. kv_len edge cases."""
+    r0 = rng(7)
+    B, Hq, Hkv, d, smax = 6, 8, 2, 64, 200
+    q = r0.standard_normal((B, Hq, d))
+    k = r0.standard_normal((B, Hkv, smax, d))
+    v = r0.standard_normal((B, Hkv, smax, d))
+    lens = np.array([0, 1, 63, 64, 65, 200], np.int32)
+    ref = sdpa_decode(q, k, v, lens)
+    for P in (1, 3, 16):
+        r = oracle.decode(q, k, v, lens, tau=-math.inf, num_splits=P, lib=lib)
+        got = r["out"].reshape(B, Hq, d)
+        err = np.abs(got - ref).max()
+        assert err < 1e-12, f"dense decode mismatch {err} P={P}"
+        lse = r["lse"].reshape(B, Hq)
+        assert np.isneginf(lse[0]).all() and np.all(got[0] == 0), "kv_len = 0 must give 0 and lse = -inf"
+
+
+def pin_longdouble_bruteforce(lib=None):
+    """Dense oracle vs explicit-loop long double softmax on tiny inputs."""
+    q, k, v = prefill_inputs(11, 1, 9, 2, 1, 4)
+    for causal in (True, False):
+        r = oracle.prefill(q, k, v, causal=causal, tau=-math.inf, tile_q=4, tile_k=4, lib=lib)
+        got = unit_rows(r["out"], 1, 9, 2, 4)
+        ref = brute_prefill_longdouble(q, k, v, causal).astype(np.float64)
+        assert np.abs(got - ref).max() < 1e-13
+
+
+def pin_forms_agree(lib=None):
+    """Closed form and scan form: identical masks and gammas, outputs within 1e-12 (prefill and split decode)."""
+    for seed, (S, Hq, Hkv, d, causal, tau) in enumerate([(512, 4, 1, 64, True, -LN1000), (300, 4, 2, 32, False, -4.0),
+                                                          (640, 8, 2, 64, True, -2.0)]):
+        q, k, v = prefill_inputs(100 + seed, 1, S, Hq, Hkv, d, planted=2)
+        a = oracle.prefill(q, k, v, causal=causal, tau=tau, tile_q=128, tile_k=64, lib=lib)
+        b = oracle.prefill(q, k, v, causal=causal, tau=tau, tile_q=128, tile_k=64, form="scan", lib=lib)
+        assert np.array_equal(a["state"], b["state"]), "closed vs scan mask"
+        vis = a["state"] > 0
+        assert np.array_equal(a["gamma"][vis], b["gamma"][vis])
+        assert np.abs(a["out"] - b["out"]).max() < 1e-12
+        assert np.abs(a["lse"][np.isfinite(a["lse"])] - b["lse"][np.isfinite(b["lse"])]).max() < 1e-12
+    q, k, v, lens = decode_planted(5)
+    for P in (1, 4, 16):
+        a = oracle.decode(q, k, v, lens, tau=-LN1000, num_splits=P, lib=lib)
+        b = oracle.decode(q, k, v, lens, tau=-LN1000, num_splits=P, form="scan", lib=lib)
+        assert np.array_equal(a["state"], b["state"]), f"decode closed vs scan mask P={P}"
+        assert np.abs(a["out"] - b["out"]).max() < 1e-12
+
+
+def decode_planted(seed, B=3, Hq=16, Hkv=2, d=64, smax=4096):
+    """Decode inputs with a sink tile (+16 logits) and 10% relevant tiles (+10 logits)."""
+    r = rng(seed)
+    q = r.standard_normal((B, Hq, d))
+    k = r.standard_normal((B, Hkv, smax, d))
+    v = r.standard_normal((B, Hkv, smax, d))
+    G = Hq // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            qh = q[b, g * G:(g + 1) * G].sum(0)
+            qh /= np.linalg.norm(qh)
+            k[b, g, :64] += 4 * math.sqrt(d) * qh
+            for t in range(1, smax // 64):
+                if r.random() < 0.1:
+                    k[b, g, t * 64:(t + 1) * 64] += 2.5 * math.sqrt(d) * qh
+    lens = np.array([smax, smax - 100, 1000][:B], np.int32)
+    return q, k, v, lens
+
+
+def pin_mask_invariants(lib=None):
+    """Monotone in tau, tau=-inf skips nothing, first tile of each scan kept, tau=0 keeps tiles with Gamma>=0."""
+    q, k, v = prefill_inputs(21, 1, 768, 4, 1, 64, planted=3)
+    taus = [-math.inf, -20.0, -LN1000, -4.0, -1.0, -0.1, 0.0]
+    prev = None
+    for tau in taus:
+        r = oracle.prefill(q, k, v, causal=True, tau=tau, tile_q=128, tile_k=64, lib=lib)
+        sk = r["state"] == oracle.SKIPPED
+        if tau == -math.inf:
+            assert not sk.any()
+        if prev is not None:
+            assert not (prev & ~sk).any(), f"skip set not monotone at tau={tau}"
+        assert not sk[:, 0].any(), "first tile of a scan skipped"
+        if tau == 0.0:
+            assert not (sk & (r["gamma"] >= 0)).any()
+        prev = sk
+    assert prev.any(), "the planted input must skip something at tau = 0"
+    qd, kd, vd, lens = decode_planted(22)
+    P = 4
+    for tau in (-LN1000, -2.0):
+        r = oracle.decode(qd, kd, vd, lens, tau=tau, num_splits=P, lib=lib)
+        for u in range(r["state"].shape[0]):
+            b = u // kd.shape[1]
+            nt = -(-int(lens[b]) // 64)
+            tps = -(-nt // P)
+            for s in range(P):
+                if s * tps < nt:
+                    assert r["state"][u, s * tps] == oracle.EXECUTED, "first tile of a split skipped"
+            assert (r["state"][u, nt:] == oracle.UNVISITED).all()
+            assert (r["state"][u, :nt] != oracle.UNVISITED).all()
+
+
+def pin_uniform_scores(lib=None):
+    """q = 0 gives logits 0, so nothing is skipped and each output is the exact mean of the visible V rows."""
+    r0 = rng(31)
+    S, d = 200, 64
+    q = np.zeros((1, S, 2, d))
+    k = r0.standard_normal((1, S, 1, d))
+    v = r0.standard_normal((1, S, 1, d))
+    for tau in (0.0, -1.0, -LN1000):
+        r = oracle.prefill(q, k, v, causal=True, tau=tau, tile_q=64, tile_k=64, lib=lib)
+        assert not (r["state"] == oracle.SKIPPED).any()
+        got = unit_rows(r["out"], 1, S, 2, 64)
+        prefix_mean = np.cumsum(v[0, :, 0], axis=0) / np.arange(1, S + 1)[:, None]
+        for h in range(2):
+            assert np.abs(got[0, :, h] - prefix_mean).max() < 1e-12
+    qd = np.zeros((2, 4, d))
+    kd = r0.standard_normal((2, 1, 300, d))
+    vd = r0.standard_normal((2, 1, 300, d))
+    lens = np.array([300, 129], np.int32)
+    r = oracle.decode(qd, kd, vd, lens, tau=0.0, num_splits=16, lib=lib)
+    for b in range(2):
+        m = vd[b, 0, :lens[b]].mean(0)
+        assert np.abs(r["out"][b] - m).max() < 1e-12
+
+
+def pin_dropped_mass(lib=None):
+    """Each skipped tile drops at most tile_k*e^tau of a row's kept mass; the output moves by at most
+    2*delta/(1+delta)*max|v| from dense attention."""
+    q, k, v = prefill_inputs(41, 1, 1024, 4, 1, 64, planted=4)
+    for tau in (-LN1000, -4.0, -1.0):
+        r = oracle.prefill(q, k, v, causal=True, tau=tau, tile_q=128, tile_k=64, lib=lib)
+        dense = oracle.prefill(q, k, v, causal=True, tau=-math.inf, tile_q=128, tile_k=64, lib=lib)
+        nskip = (r["state"] == oracle.SKIPPED).sum(1)
+        bound = nskip[:, None] * 64 * math.exp(tau)
+        assert (r["dropped"] <= bound * (1 + 1e-12) + 1e-300).all()
+        delta = r["dropped"]
+        dev = np.abs(r["out"] - dense["out"]).max(-1)
+        vmax = np.abs(v).max()
+        assert (dev <= 2 * delta / (1 + delta) * vmax + 1e-12).all()
+        assert nskip.sum() > 0
+
+
+def pin_split_invariance(lib=None):
+    """At tau = -inf the split-K combine is exact: the output does not depend on the split count."""
+    q, k, v, lens = decode_planted(51)
+    base = oracle.decode(q, k, v, lens, tau=-math.inf, num_splits=1, lib=lib)
+    for P in (2, 7, 16, 64):
+        r = oracle.decode(q, k, v, lens, tau=-math.inf, num_splits=P, lib=lib)
+        assert np.abs(r["out"] - base["out"]).max() < 1e-12
+        assert np.abs(r["lse"] - base["lse"]).max() < 1e-12
+
+
+def pin_output_given_mask(lib=None):
+    """With the oracle's own mask, the output equals softmax restricted to the kept keys (SDPA + boolean mask)."""
+    B, S, Hq, Hkv, d = 1, 384, 4, 2, 32
+    q, k, v = prefill_inputs(61, B, S, Hq, Hkv, d, planted=2)
+    Tq, Tk = 128, 64
+    r = oracle.prefill(q, k, v, causal=True, tau=-2.0, tile_q=Tq, tile_k=Tk, lib=lib)
+    nqt = S // Tq
+    mask = np.zeros((B, Hq, S, S), bool)
+    for h in range(Hq):
+        for qt in range(nqt):
+            st = r["state"][h * nqt + qt]
+            for i in range(qt * Tq, (qt + 1) * Tq):
+                for t in range(S // Tk):
+                    if st[t] == oracle.EXECUTED:
+                        mask[0, h, i, t * Tk:min((t + 1) * Tk, i + 1)] = True
+    assert (r["state"] == oracle.SKIPPED).any()
+    ref = sdpa_prefill(q, k, v, False, key_mask=mask)
+    got = unit_rows(r["out"], B, S, Hq, Tq)
+    assert np.abs(got - ref).max() < 1e-12
+    # forcing a mask through the override gives the same restricted softmax
+    ov = np.full(r["state"].shape, -1, np.int8)
+    ov[:, 1] = 1
+    r2 = oracle.prefill(q, k, v, causal=True, tau=-math.inf, tile_q=Tq, tile_k=Tk, override=ov, lib=lib)
+    mask2 = np.tril(np.ones((S, S), bool))[None, None].repeat(Hq, 1)
+    mask2[:, :, :, Tk:2 * Tk] = False
+    mask2[:, :, :Tk, :Tk] = np.tril(np.ones((Tk, Tk), bool))
+    ref2 = sdpa_prefill(q, k, v, False, key_mask=mask2)
+    got2 = unit_rows(r2["out"], B, S, Hq, Tq)
+    assert np.abs(got2 - ref2).max() < 1e-12
+
+
+# ----------------------------------------------------------------- worked examples
+def _w1_inputs():
+    """d=2, S=128, q_i=(1,0); tile-0 keys (0,0) -> logit 0; tile-1 keys (-10,0) -> logit -10 (scale 1).
+    v_j = (j, 1) on tile 0 and (1000, -1) on tile 1."""
+    S, d = 128, 2
+    q = np.zeros((1, S, 1, d)); q[..., 0] = 1.0
+    k = np.zeros((1, S, 1, d)); k[0, 64:, 0, 0] = -10.0
+    v = np.zeros((1, S, 1, d))
+    v[0, :64, 0, 0] = np.arange(64); v[0, :64, 0, 1] = 1.0
+    v[0, 64:, 0, 0] = 1000.0; v[0, 64:, 0, 1] = -1.0
+    return q, k, v
+
+
+def pin_worked_examples(lib=None):
+    """Hand-built examples with outputs derived by hand."""
+    # W1: tile 1 trails the running max by exactly 10.
+    q, k, v = _w1_inputs()
+    e = math.exp(-10.0)
+    dense = np.array([(31.5 + 1000 * e) / (1 + e), (1 - e) / (1 + e)])
+    for tau, skipped in ((-LN1000, True), (-10.0, False), (-11.0, False), (-math.inf, False), (-9.999, True)):
+        r = oracle.prefill(q, k, v, causal=False, tau=tau, tile_q=64, tile_k=64, scale=1.0, lib=lib)
+        want = np.array([31.5, 1.0]) if skipped else dense
+        assert np.abs(r["out"][:, :, :] - want).max() < 1e-12, f"W1 tau={tau}"
+        assert list(r["state"][0]) == [1, 2 if skipped else 1], f"W1 mask tau={tau}"
+        assert abs(r["gamma"][0, 1] - (-10.0)) == 0.0
+        if skipped:
+            assert np.abs(r["dropped"] - e).max() < 1e-15
+    # W1 in decode form: the 128 keys as one sequence, G=2 identical query heads, one split.
+    qd = np.zeros((1, 2, 2)); qd[..., 0] = 1.0
+    kd = k[0, :, 0][None, None]; vd = v[0, :, 0][None, None]
+    r = oracle.decode(qd, kd, vd, np.array([128], np.int32), tau=-LN1000, num_splits=1, scale=1.0, lib=lib)
+    assert np.abs(r["out"] - np.array([31.5, 1.0])).max() < 1e-12 and list(r["state"][0]) == [1, 2]
+    # W1 with two splits: tile 1 starts its own scan, so it is never skipped.
+    r = oracle.decode(qd, kd, vd, np.array([128], np.int32), tau=-LN1000, num_splits=2, scale=1.0, lib=lib)
+    assert np.abs(r["out"] - dense).max() < 1e-12 and list(r["state"][0]) == [1, 1]
+
+    # W2: the comparison is against the running maximum, not against tile 0.
+    # Tile logits: tile0 = 0, tile1 = 8 (new max, kept), tile2 = 3 (5 below the running max 8).
+    S = 192
+    q = np.zeros((1, S, 1, 2)); q[..., 0] = 1.0
+    k = np.zeros((1, S, 1, 2)); k[0, 64:128, 0, 0] = 8.0; k[0, 128:, 0, 0] = 3.0
+    v = np.zeros((1, S, 1, 2)); v[0, :64, 0, 0] = 1.0; v[0, 64:128, 0, 1] = 1.0; v[0, 128:, 0, :] = -1.0
+    r = oracle.prefill(q, k, v, causal=False, tau=-4.0, tile_q=64, tile_k=64, scale=1.0, lib=lib)
+    assert list(r["state"][0]) == [1, 1, 2], "W2 mask"
+    z = 1 + math.exp(8)
+    assert np.abs(r["out"][0] - np.array([1 / z, math.exp(8) / z])).max() < 1e-12
+    r = oracle.prefill(q, k, v, causal=False, tau=-6.0, tile_q=64, tile_k=64, scale=1.0, lib=lib)
+    assert list(r["state"][0]) == [1, 1, 1], "W2 kept at tau=-6"
+
+    # W3: every row must agree.  Row 0 trails by 10 on tile 1, row 1 gains 2: the tile is kept.
+    q = np.zeros((1, 128, 1, 2)); q[0, :, 0, 0] = 1.0; q[0, 1, 0] = (0.0, 1.0)
+    k = np.zeros((1, 128, 1, 2)); k[0, 64:, 0] = (-10.0, 2.0)
+    v = np.ones((1, 128, 1, 2))
+    r = oracle.prefill(q, k, v, causal=False, tau=-LN1000, tile_q=64, tile_k=64, scale=1.0, lib=lib)
+    assert list(r["state"][0]) == [1, 1], "W3 agreement rule"
+    assert r["gamma"][0, 1] == 2.0
+    q[0, 1, 0] = (1.0, 0.0)
+    r = oracle.prefill(q, k, v, causal=False, tau=-LN1000, tile_q=64, tile_k=64, scale=1.0, lib=lib)
+    assert list(r["state"][0]) == [1, 2], "W3 skipped once all rows trail"
+
+    # W4: causal abstention.  Tq=128, Tk=64, S=128: rows 0..63 have no valid key in tile 1 and abstain;
+    # rows 64..127 trail the running max by 10 there, so the tile is skipped and those rows attend
+    # only to tile 0 (keys 0..63, logit 0): output = mean of v over keys 0..63.
+    q = np.zeros((1, 128, 1, 2)); q[..., 0] = 1.0
+    k = np.zeros((1, 128, 1, 2)); k[0, 64:, 0, 0] = -10.0
+    v = np.zeros((1, 128, 1, 2)); v[0, :, 0, 0] = np.arange(128); v[0, :, 0, 1] = 1.0
+    r = oracle.prefill(q, k, v, causal=True, tau=-LN1000, tile_q=128, tile_k=64, scale=1.0, lib=lib)
+    assert list(r["state"][0]) == [1, 2], "W4 mask"
+    assert r["gamma"][0, 1] == -10.0
+    rows = np.arange(64, 128)
+    assert np.abs(r["out"][0, rows, 0] - 31.5).max() < 1e-12
+    assert np.abs(r["out"][0, :64, 0] - np.arange(64) / 2.0).max() < 1e-12  # row i: mean of 0..i
+
+    # W5: the first tile of a scan is kept even when its logits are far below tau.
+    q = np.zeros((1, 128, 1, 2)); q[..., 0] = 1.0
+    k = np.zeros((1, 128, 1, 2)); k[0, :64, 0, 0] = -30.0; k[0, 64:, 0, 0] = -45.0
+    v = np.zeros((1, 128, 1, 2)); v[0, :64, 0, 0] = 2.0; v[0, 64:, 0, 0] = 5.0
+    r = oracle.prefill(q, k, v, causal=False, tau=-LN1000, tile_q=64, tile_k=64, scale=1.0, lib=lib)
+    assert list(r["state"][0]) == [1, 2], "W5 mask"
+    assert np.abs(r["out"][0, :, 0] - 2.0).max() < 1e-12
+
+
+ALL_PINS = [pin_dense_prefill, pin_dense_decode, pin_longdouble_bruteforce, pin_forms_agree, pin_mask_invariants,
+            pin_uniform_scores, pin_dropped_mass, pin_split_invariance, pin_output_given_mask, pin_worked_examples]
+
+
+def run_all(lib=None):
+    """Run every pin; return the names of those that failed."""
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError) as e:  # ValueError: the oracle refused or crashed a case
+            failed.append((pin.__name__, str(e)[:200]))
+    return failed

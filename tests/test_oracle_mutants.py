@@ -1,0 +1,59 @@
+"""Planted mistakes in the oracle must fail at least one pin (CPU only).
+
+Each case copies oracle/oracle.c, applies one textual mutation (a dropped term, a flipped
+sign or comparison, a wrong index, a transposed operand, a wrong scale, ...), builds the
+mutant with gcc into a temporary directory and runs every pin from oracle_pins against it.
+The unmodified oracle passes all pins (test_oracle.py); every mutant must fail one.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, replacement, expected number of occurrences)
+MUTANTS = [
+    ("gap_sign_flipped", "return tile_max - running_max;", "return running_max - tile_max;", 1),
+    ("skip_comparison_flipped", "unit_gap < u->tau", "unit_gap > u->tau", 1),
+    ("skip_comparison_not_strict", "unit_gap < u->tau", "unit_gap <= u->tau", 1),
+    ("unit_gap_min_over_rows", "if (g > G) G = g;", "if (voters == 1 || g < G) G = g;", 2),
+    ("first_tile_gap_not_infinite", "return INFINITY;  /* first tile", "return tile_max;  /* first tile", 1),
+    ("causal_off_by_one", "(s->causal ? i + 1 : s->S)", "(s->causal ? i : s->S)", 1),
+    ("gqa_head_map_modulo", "g = h / G,", "g = h % s->Hkv,", 1),
+    ("scale_1_over_d", "1.0 / sqrt((double)s->d)", "1.0 / (double)s->d", 2),
+    ("values_read_from_keys", "load_row(u, u->v, j, row);", "load_row(u, u->k, j, row);", 2),
+    ("normaliser_drops_first_key", "if (m > -INFINITY)\n      for (int j = 0;", "if (m > -INFINITY)\n      for (int j = 1;", 1),
+    ("no_rescale_in_scan", "l[r] *= c;", "l[r] *= 1.0;", 1),
+    ("running_max_not_reset_per_split", "for (int r = 0; r < nr; ++r) R[r] = -INFINITY;", "if (s == 0) for (int r = 0; r < nr; ++r) R[r] = -INFINITY;", 1),
+    ("combine_equal_weights", "double w = exp(ls[(int64_t)s * nr + r] - big);", "double w = ls[(int64_t)s * nr + r] > -INFINITY ? 1.0 : 0.0;", 1),
+    ("tile_max_includes_next_key", "j < (t + 1) * T && j < nk", "j <= (t + 1) * T && j < nk", 1),
+    ("split_size_floor", "const int tps = (nt + P - 1) / P;", "const int tps = nt / P > 0 ? nt / P : 1;", 1),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir(tmp_path_factory):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("name,orig,repl,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(workdir, name, orig, repl, count):
+    src = open(SRC).read()
+    assert src.count(orig) == count, f"mutation site for {name} not found as expected"
+    d = workdir / name
+    d.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(SRC), "oracle.h"), d / "oracle.h")
+    (d / "oracle.c").write_text(src.replace(orig, repl))
+    so = str(d / "liboracle_mutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", str(d / "oracle.c"), "-o", so,
+                    "-lpthread", "-lm"], check=True)
+    lib = oracle.load(so)
+    failed = oracle_pins.run_all(lib)
+    assert failed, f"mutant {name} passed every pin"
