@@ -1,0 +1,135 @@
+/*
+ * ssm.h -- C ABI of libssm.so: Skip Softmax attention forward on AMD MI355X (gfx950).
+ *
+ * Skip Softmax is a FlashAttention-style forward pass with an online (running
+ * maximum) softmax over streamed key tiles.  For each key tile the local score
+ * maximum is compared with the running maximum of the earlier tiles; when it
+ * trails by more than a threshold tau, for every row of the unit, the tile's
+ * exponentials and its P*V product are skipped.  Sources: the recap of
+ * "Accelerating Long-Context Inference with Skip Softmax in NVIDIA
+ * TensorRT-LLM" (Key Points; Detailed Analysis; Skip Softmax Mechanism;
+ * Impact on Accuracy vs. Speed) and the NVIDIA Skip Softmax news item
+ * (Understanding Skip Softmax; Benefits and Implementation).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers inside descriptors are DEVICE pointers unless noted; descriptor
+ *    structs themselves live in host memory and are read during the call only.
+ *  - The caller owns every buffer.  The library never allocates device memory
+ *    and keeps no state between calls.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  No call synchronises or reads device memory on the
+ *    host.  Outputs and statistics are valid once the stream has passed them.
+ *  - Return codes: SSM_OK, or an error code; on any error nothing is launched
+ *    and ssm_last_error() (thread-local) holds a message.
+ *  - Units of tau: natural-log ratio of softmax weights (tau = -ln 1000 skips a
+ *    tile whose best weight is below 1/1000 of the running best).  tau = -inf
+ *    disables skipping (dense attention).  tau must be -inf or in (-inf, 0];
+ *    tau > 0 or NaN is SSM_EINVAL (a skipped tile could then hold a new maximum).
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+enum {
+  SSM_OK = 0,
+  SSM_EINVAL = 1,        /* NULL pointer, shape/stride/dtype mismatch, bad tau, Hq % Hkv != 0, ... */
+  SSM_EUNSUPPORTED = 2,  /* valid request outside what the kernels implement (head_dim, tiles, alignment) */
+  SSM_EWORKSPACE = 3,    /* decode workspace missing or too small */
+  SSM_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+};
+
+enum { SSM_BF16 = 0, SSM_FP32 = 1 };
+
+/* Strided tensor view.  stride[] is in elements; the last dimension must be
+ * contiguous (stride 1).  data must be 16-byte aligned and every other stride
+ * a multiple of 8 elements, so rows can be moved in 16-byte pieces. */
+typedef struct {
+  void* data;
+  int32_t dtype;    /* SSM_BF16 or SSM_FP32 */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} ssm_tensor;
+
+/* Decode KV cache.
+ *   contiguous: page_table == NULL, pool = [B, Hkv, Smax, d]
+ *   paged:      pool = [num_pages, Hkv, page_size, d]; page_table is a device
+ *               int32 [B, max_pages] row-major array; logical key tile t of
+ *               sequence b lives in page page_table[b*max_pages + t].  Only
+ *               entries t < ceil(kv_len[b]/page_size) are read and they must be
+ *               in [0, num_pages).  page_size must equal the key tile (64). */
+typedef struct {
+  ssm_tensor pool;
+  const int32_t* page_table;
+  int32_t page_size;
+  int32_t max_pages;
+} ssm_kv_cache;
+
+/* Optional skip statistics (every member may be NULL / 0).
+ *   tile_state: uint8 per (unit, key tile): 0 not visited, 1 executed, 2 skipped.
+ *     prefill: unit = (b*Hq + h)*ceil(S/tile_q) + q_tile, row length ceil(S/tile_k)
+ *     decode:  unit = b*Hkv + g, row length = max key tiles (Smax/64 or max_pages)
+ *   unit_gap:   float per (unit, key tile), same indexing: the unit gap (max
+ *     over the unit's rows of tile max minus running max, natural-log units);
+ *     +inf on the first tile of a scan, NaN where not visited.
+ *   counters:   uint64 [4] = visited tiles, skipped tiles, QK^T tiles issued,
+ *     P*V tiles issued.  Accumulated with atomics: zero them before the call. */
+typedef struct {
+  uint8_t* tile_state;
+  int64_t tile_state_len;       /* elements available at tile_state */
+  float* unit_gap;
+  int64_t unit_gap_len;         /* elements available at unit_gap */
+  unsigned long long* counters;
+} ssm_skip_stats;
+
+/* Optional tuning / workspace (NULL selects every default). */
+typedef struct {
+  float scale;             /* softmax scale; 0 selects 1/sqrt(d) */
+  int32_t tile_q;          /* prefill query tile: 0 -> 128; 64 or 128 */
+  int32_t tile_k;          /* key tile: 0 -> 64; only 64 */
+  int32_t num_splits;      /* decode split-K chunks: 0 -> 16; 1..64 */
+  void* workspace;         /* decode: device buffer of >= ssm_decode_workspace_bytes() bytes */
+  size_t workspace_bytes;
+} ssm_opts;
+
+/* Causal or full prefill (self-attention, S_q = S_k = seqlen).
+ *   q   [B, S, Hq, d]  bf16    k, v [B, S, Hkv, d] bf16    out [B, S, Hq, d] bf16
+ *   d in {64, 128}; Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv).
+ *   causal != 0: query i attends to keys j <= i (top-left aligned).
+ * The unit of the skip decision is one query tile of one head (tile_q rows);
+ * its key tiles are scanned in ascending order and the first is never skipped. */
+int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, int32_t seqlen, int32_t causal,
+                float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream, const ssm_opts* opts);
+
+/* Single-token GQA decode with split-K and a log-sum-exp combine.
+ *   q [B, Hq, d] bf16; out [B, Hq, d] bf16; kv_lens device int32 [B], each in [0, Smax or
+ *   max_pages*page_size]; query b attends to keys j < kv_lens[b].  kv_len 0 gives 0.
+ * The unit of the skip decision is one KV group (its Hq/Hkv query heads vote
+ * together).  The unit's n = ceil(kv_len/64) key tiles are cut into num_splits
+ * chunks of ceil(n/num_splits) tiles; each chunk is an independent scan whose
+ * running maximum starts at -inf, so the first tile of every chunk is kept.
+ * Needs opts->workspace (see ssm_decode_workspace_bytes). */
+int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+               const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+               const ssm_opts* opts);
+
+/* Bytes of device workspace ssm_decode needs (fp32 partial outputs and
+ * log-sum-exps per (b, query head, split)).  0 for invalid arguments. */
+size_t ssm_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int32_t num_splits);
+
+const char* ssm_strerror(int code);   /* static text for a return code */
+const char* ssm_last_error(void);     /* thread-local detail of the last failed call on this thread */
+int ssm_abi_version(void);            /* SSM_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,235 @@
+"""Skip Softmax attention on AMD MI355X: thin Python binding of libssm.so.
+
+Every computation runs in the HIP kernels of ``libssm.so``; this module only turns
+torch tensors into the C descriptors of ``include/ssm.h`` (pointers, shapes, strides),
+allocates outputs/workspace with torch, and raises on error codes.  There is no
+fallback path: if the library is missing or a call fails, an exception is raised.
+
+Entry points (same names as the C ABI):
+    ssm_prefill(q, k, v, causal=True, tau=-ln(1000), ...)       -> out [B,S,Hq,d] bf16
+    ssm_decode(q, k_cache, v_cache, kv_lens, tau=..., ...)      -> out [B,Hq,d] bf16
+    ssm_decode_workspace_bytes(B, Hq, d, num_splits)
+    ssm_strerror(code), ssm_last_error(), ssm_abi_version()
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm.so")
+
+SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
+SSM_BF16, SSM_FP32 = 0, 1
+EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_decode", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
+                    "ssm_abi_version")
+
+
+class SsmError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class KvCache(ctypes.Structure):
+    _fields_ = [("pool", Tensor), ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32)]
+
+
+class SkipStatsC(ctypes.Structure):
+    _fields_ = [("tile_state", ctypes.c_void_p), ("tile_state_len", ctypes.c_int64), ("unit_gap", ctypes.c_void_p),
+                ("unit_gap_len", ctypes.c_int64), ("counters", ctypes.c_void_p)]
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+                ("num_splits", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libssm.so (built by ``python -m long_context_flash_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m long_context_flash_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.ssm_prefill.restype = ctypes.c_int
+    L.ssm_prefill.argtypes = [P(Tensor), P(Tensor), P(Tensor), ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                              P(Tensor), P(SkipStatsC), ctypes.c_void_p, P(Opts)]
+    L.ssm_decode.restype = ctypes.c_int
+    L.ssm_decode.argtypes = [P(Tensor), P(KvCache), P(KvCache), ctypes.c_void_p, ctypes.c_float, P(Tensor),
+                             P(SkipStatsC), ctypes.c_void_p, P(Opts)]
+    L.ssm_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.ssm_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 4
+    L.ssm_strerror.restype = ctypes.c_char_p
+    L.ssm_strerror.argtypes = [ctypes.c_int]
+    L.ssm_last_error.restype = ctypes.c_char_p
+    L.ssm_last_error.argtypes = []
+    L.ssm_abi_version.restype = ctypes.c_int
+    L.ssm_abi_version.argtypes = []
+    _lib = L
+    return L
+
+
+def describe(t: Optional[torch.Tensor]) -> Tensor:
+    """ssm_tensor descriptor of a torch tensor (no copy)."""
+    d = Tensor()
+    if t is None:
+        return d
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d.data = t.data_ptr()
+    d.dtype = SSM_BF16 if t.dtype == torch.bfloat16 else (SSM_FP32 if t.dtype == torch.float32 else -1)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(rc: int):
+    if rc != SSM_OK:
+        raise SsmError(rc, f"{ssm_strerror(rc)}: {ssm_last_error()}")
+
+
+@dataclass
+class SkipStats:
+    """Device buffers for the optional skip statistics (see ssm_skip_stats in include/ssm.h)."""
+    tile_state: Optional[torch.Tensor] = None   # uint8
+    unit_gap: Optional[torch.Tensor] = None     # float32
+    counters: Optional[torch.Tensor] = None     # int64 [4]: visited, skipped, qk tiles, pv tiles
+
+    def c(self) -> SkipStatsC:
+        s = SkipStatsC()
+        if self.tile_state is not None:
+            s.tile_state = self.tile_state.data_ptr()
+            s.tile_state_len = self.tile_state.numel()
+        if self.unit_gap is not None:
+            s.unit_gap = self.unit_gap.data_ptr()
+            s.unit_gap_len = self.unit_gap.numel()
+        if self.counters is not None:
+            s.counters = self.counters.data_ptr()
+        return s
+
+    @staticmethod
+    def alloc(units: int, tiles: int, device, gaps: bool = False) -> "SkipStats":
+        return SkipStats(tile_state=torch.zeros(units, tiles, dtype=torch.uint8, device=device),
+                         unit_gap=torch.empty(units, tiles, dtype=torch.float32, device=device) if gaps else None,
+                         counters=torch.zeros(4, dtype=torch.int64, device=device))
+
+
+def prefill_stats_shape(B, S, Hq, tile_q=128, tile_k=64):
+    """(units, tiles) of the prefill statistics: unit = (b*Hq + h)*ceil(S/tile_q) + q_tile."""
+    return B * Hq * (-(-S // tile_q)), -(-S // tile_k)
+
+
+def ssm_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+                tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
+                skip_stats: Optional[SkipStats] = None, stream=None, tile_q: int = 128, tile_k: int = 64,
+                scale: float = 0.0) -> torch.Tensor:
+    """Skip Softmax prefill: q [B,S,Hq,d], k/v [B,S,Hkv,d] bf16 on the GPU -> out [B,S,Hq,d] bf16."""
+    if out is None:
+        out = torch.empty_like(q)
+    qd, kd, vd, od = describe(q), describe(k), describe(v), describe(out)
+    opts = Opts(float(scale), int(tile_q), int(tile_k), 0, None, 0)
+    st = skip_stats.c() if skip_stats is not None else None
+    rc = lib().ssm_prefill(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), int(q.shape[1]) if q.dim() == 4 else 0,
+                           int(bool(causal)), float(tau), ctypes.byref(od), ctypes.byref(st) if st else None,
+                           _stream_handle(stream), ctypes.byref(opts))
+    _check(rc)
+    return out
+
+
+def ssm_decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:
+    return int(lib().ssm_decode_workspace_bytes(B, Hq, d, num_splits))
+
+
+def decode_workspace(B, Hq, d, num_splits, device) -> torch.Tensor:
+    n = ssm_decode_workspace_bytes(B, Hq, d, num_splits)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_lens: torch.Tensor,
+               tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
+               page_table: Optional[torch.Tensor] = None, v_page_table: Optional[torch.Tensor] = None,
+               num_splits: int = 16, workspace: Optional[torch.Tensor] = None,
+               skip_stats: Optional[SkipStats] = None, stream=None, scale: float = 0.0) -> torch.Tensor:
+    """Skip Softmax split-K decode.
+
+    q [B,Hq,d] bf16; k_cache/v_cache contiguous [B,Hkv,Smax,d] (page_table None) or paged pools
+    [pages,Hkv,64,d] with page_table int32 [B,max_pages]; kv_lens int32 [B] on the GPU."""
+    if out is None:
+        out = torch.empty_like(q)
+    B, Hq, d = q.shape
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, d, num_splits, q.device)
+    vpt = page_table if v_page_table is None else v_page_table
+
+    def cache(t, pt):
+        c = KvCache()
+        c.pool = describe(t)
+        if pt is not None:
+            if pt.dtype != torch.int32 or pt.dim() != 2 or not pt.is_contiguous():
+                raise ValueError("page_table must be a contiguous int32 [B, max_pages] tensor")
+            c.page_table = pt.data_ptr()
+            c.page_size = t.shape[2]
+            c.max_pages = pt.shape[1]
+        return c
+
+    if kv_lens.dtype != torch.int32 or not kv_lens.is_contiguous():
+        raise ValueError("kv_lens must be a contiguous int32 tensor")
+    kc, vc = cache(k_cache, page_table), cache(v_cache, vpt)
+    qd, od = describe(q), describe(out)
+    opts = Opts(float(scale), 0, 64, int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    st = skip_stats.c() if skip_stats is not None else None
+    rc = lib().ssm_decode(ctypes.byref(qd), ctypes.byref(kc), ctypes.byref(vc), kv_lens.data_ptr(), float(tau),
+                          ctypes.byref(od), ctypes.byref(st) if st else None, _stream_handle(stream),
+                          ctypes.byref(opts))
+    _check(rc)
+    return out
+
+
+def ssm_strerror(code: int) -> str:
+    return lib().ssm_strerror(code).decode()
+
+
+def ssm_last_error() -> str:
+    return lib().ssm_last_error().decode()
+
+
+def ssm_abi_version() -> int:
+    return int(lib().ssm_abi_version())
+
+
+def bf16_from_bits(a, device=None) -> torch.Tensor:
+    """numpy uint16 bf16 bit patterns -> torch.bfloat16 tensor (optionally moved to ``device``)."""
+    t = torch.from_numpy(a.view("int16")).view(torch.bfloat16)
+    return t.to(device) if device is not None else t
+
+
+__all__ = ["ssm_prefill", "ssm_decode", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
+           "ssm_abi_version", "SkipStats", "SsmError", "prefill_stats_shape", "decode_workspace", "bf16_from_bits",
+           "lib", "describe", "LIB_PATH", "EXPORTED_SYMBOLS"]

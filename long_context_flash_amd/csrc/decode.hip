@@ -1,0 +1,330 @@
+// decode.hip -- Skip Softmax single-token GQA decode for gfx950: split-K + log-sum-exp combine.
+//
+// Method: the online-softmax forward of the recap "Accelerating Long-Context
+// Inference with Skip Softmax in NVIDIA TensorRT-LLM" (Key Points, Detailed
+// Analysis, Skip Softmax Mechanism) applied to the generation phase; the news
+// item (Benefits and Implementation) attributes the decode gain to lower memory
+// traffic, so here a skipped tile's V rows are never read from HBM.
+//
+// Unit = (batch b, KV group g): the G query heads of the group vote together.
+// The unit's ceil(kv_len/64) key tiles are cut into num_splits consecutive
+// chunks; each chunk is an independent scan (running maximum starts at -inf)
+// handled by one workgroup that writes a partial (o_s, lse_s).  A second
+// kernel combines the partials per (b, query head).
+//
+// Workgroup = 4 waves.  Tiles of the split are processed four at a time, one
+// per wave.  Skipping depends only on the prefix maximum of the tile maxima
+// (tau <= 0 means a skipped tile never raises it), so the four tiles' S = Q.K^T
+// are computed in parallel, their per-query maxima exchanged through LDS, and
+// each wave decides its own tile against max(previous chunks, earlier waves).
+//
+// Per wave and tile (64 keys):
+//   S^T (16 keys x 16 query columns, G <= 16 used) = K . Q^T on
+//   v_mfma_f32_16x16x32_bf16, four key blocks.  K comes straight from HBM into
+//   the A operand (16 bytes per lane per MFMA, no LDS).  Each lane owns one
+//   query column.
+//   O^T += V^T . P^T on the same MFMA: P^T is the S^T accumulator converted to
+//   bf16 in place.  For the V^T operand each lane loads 8 keys x 8 channels
+//   (eight 16-byte rows) and transposes them in registers; MFMA j uses channel
+//   j of each loaded chunk, so its 16 output rows are channels 8m + j.
+//   V is loaded only after the vote keeps the tile.
+#include "ssm_device.h"
+#include "ssm_launch.h"
+
+namespace ssm {
+
+constexpr int kDecTK = 64;
+constexpr int kDecWaves = 4;
+constexpr int kDecMaxG = 16;
+
+struct TileAddr {
+  const uint16_t* k;  // first key row of the tile (nullptr: page id out of range)
+  const uint16_t* v;
+};
+
+__device__ __forceinline__ TileAddr decode_tile_addr(const DecodeArgs& a, int b, int g, int t, int64_t k_pool_rows,
+                                                     int64_t v_pool_rows) {
+  TileAddr r;
+  if (a.k_pages) {
+    const int pk = a.k_pages[(int64_t)b * a.k_max_pages + t];
+    const int pv = a.v_pages[(int64_t)b * a.v_max_pages + t];
+    r.k = (pk >= 0 && pk < k_pool_rows) ? a.k + (int64_t)pk * a.k_sb + (int64_t)g * a.k_sh : nullptr;
+    r.v = (pv >= 0 && pv < v_pool_rows) ? a.v + (int64_t)pv * a.v_sb + (int64_t)g * a.v_sh : nullptr;
+  } else {
+    r.k = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)t * kDecTK * a.k_ss;
+    r.v = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)t * kDecTK * a.v_ss;
+  }
+  return r;
+}
+
+// kv_cap: keys the cache can hold (contiguous Smax, paged max_pages*64);
+// pool_rows: number of pages in the pools (paged only).
+template <int D>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a, int kv_cap, int64_t k_pool_rows,
+                                                           int64_t v_pool_rows) {
+  constexpr int KS = D / 32;            // k-steps of the QK^T MFMA
+  __shared__ float mt[2][kDecWaves][kDecMaxG];  // per-chunk tile maxima (double-buffered by chunk parity)
+  __shared__ float cm[kDecWaves][kDecMaxG];
+  __shared__ float cl[kDecWaves][kDecMaxG];
+  __shared__ __attribute__((aligned(16))) float cacc[kDecWaves][kDecMaxG][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qc = lane & 15, grp = lane >> 4;  // query column, lane group (key group for operands)
+  const int P = a.num_splits;
+  const int split = blockIdx.x % P;
+  const int bg = blockIdx.x / P;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int G = a.G;
+
+  int len = a.kv_lens[b];
+  len = len < 0 ? 0 : (len > kv_cap ? kv_cap : len);
+  const int nt = (len + kDecTK - 1) / kDecTK;
+  const int tps = (nt + P - 1) / P;
+  const int s_begin = min(nt, split * tps), s_end = min(nt, s_begin + tps);
+  const int64_t srow = (int64_t)bg * a.max_tiles;
+
+  // statistics rows: this split owns tiles [split*tps, split*tps + tps); the last split also owns the tail
+  if (tid == 0) {
+    const int own_lo = min(a.max_tiles, split * tps);
+    const int own_hi = split == P - 1 ? a.max_tiles : min(a.max_tiles, split * tps + tps);
+    for (int t = max(own_lo, s_end); t < own_hi; ++t) {
+      if (a.tile_state) a.tile_state[srow + t] = 0;
+      if (a.unit_gap) a.unit_gap[srow + t] = __builtin_nanf("");
+    }
+  }
+
+  const int64_t part_row = ((int64_t)b * a.Hq + g * G) * P + split;  // + q*P for query q of the group
+  if (s_begin >= s_end) {  // empty split: lse = -inf, o = 0
+    for (int i = tid; i < G * D; i += 256) {
+      const int q = i / D, c = i - q * D;
+      a.part_o[(part_row + (int64_t)q * P) * D + c] = 0.f;
+      if (c == 0) a.part_lse[part_row + (int64_t)q * P] = neg_inf();
+    }
+    return;
+  }
+
+  // Q^T operand: lane (qc, grp) holds Q[qc][ks*32 + grp*8 .. +8]; columns >= G are zero
+  bf16x8 qreg[KS];
+  {
+    const bool ok = qc < G;
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)(g * G + (ok ? qc : 0)) * a.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(ok ? ld_global_16(qp + ks * 32 + grp * 8) : u32x4{0, 0, 0, 0});
+  }
+
+  const int nchunks = (s_end - s_begin + kDecWaves - 1) / kDecWaves;
+  u32x4 kreg[4][KS];  // A operand of the QK^T MFMAs: key block kb, k-step ks
+  auto load_k = [&](int t) {
+    const TileAddr ta = decode_tile_addr(a, b, g, t, k_pool_rows, v_pool_rows);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int j = t * kDecTK + kb * 16 + qc;
+      const bool ok = ta.k != nullptr && j < len;
+      const uint16_t* p = ta.k + (int64_t)(kb * 16 + qc) * a.k_ss + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kreg[kb][ks] = ok ? ld_global_16(p + ks * 32) : u32x4{0, 0, 0, 0};
+    }
+  };
+
+  // V^T operand source: lane (m = qc, grp) loads keys f(st, e) = st*32 + 16*(e/4) + 4*grp + (e%4),
+  // channels 8m .. 8m+7 (zero for channels >= D)
+  u32x4 vreg[2][8];
+  auto load_v = [&](int t) {
+    const TileAddr ta = decode_tile_addr(a, b, g, t, k_pool_rows, v_pool_rows);
+    const bool ch_ok = qc * 8 < D && ta.v != nullptr;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int f = st * 32 + 16 * (e >> 2) + 4 * grp + (e & 3);
+        const bool ok = ch_ok && t * kDecTK + f < len;
+        vreg[st][e] = ok ? ld_global_16(ta.v + (int64_t)f * a.v_ss + qc * 8) : u32x4{0, 0, 0, 0};
+      }
+  };
+
+  f32x4 acc[8];  // acc[j][i] = O[query qc][channel 32*grp + 8*i + j]
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{};
+  float m_run = neg_inf(), l_part = 0.f;
+  float r_prev = neg_inf();  // prefix max of tile maxima over earlier chunks (this lane's query)
+  unsigned n_exec = 0, n_vis = 0;
+
+  {
+    const int t0 = s_begin + w;
+    if (t0 < s_end) load_k(t0);
+  }
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int t = s_begin + c * kDecWaves + w;
+    const bool has = t < s_end;
+    f32x4 s[4];
+    float mx = neg_inf();
+    if (has) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4 x = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[kb][ks]), qreg[ks], x, 0, 0, 0);
+        s[kb] = x;
+      }
+      // s[kb][i] = S^T[key t*64 + kb*16 + 4*grp + i][query qc]
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = t * kDecTK + kb * 16 + 4 * grp + i;
+          if (qc >= G || j >= len) s[kb][i] = neg_inf();
+          mx = fmaxf(mx, s[kb][i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    if (lane < kDecMaxG) mt[c & 1][w][lane] = mx;
+    __syncthreads();
+    float r = r_prev, r_all = r_prev;
+#pragma unroll
+    for (int w2 = 0; w2 < kDecWaves; ++w2) {
+      const float x = mt[c & 1][w2][qc];
+      if (w2 < w) r = fmaxf(r, x);
+      r_all = fmaxf(r_all, x);
+    }
+    r_prev = r_all;
+
+    const bool abstain = mx == neg_inf();
+    const float gap = mx - r;  // +inf on the scan's first tile
+    const bool keep = has && wave_ballot(!abstain && !(gap < a.tau_raw)) != 0;
+    if (has) {
+      ++n_vis;
+      if (a.unit_gap) {
+        float gg = abstain ? neg_inf() : gap;
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) gg = fmaxf(gg, __shfl_xor(gg, off, 64));
+        if (lane == 0) a.unit_gap[srow + t] = gg == __builtin_inff() ? gg : gg * a.scale;
+      }
+      if (lane == 0 && a.tile_state) a.tile_state[srow + t] = keep ? 1 : 2;
+    }
+    if (keep) load_v(t);
+    {
+      const int tn = t + kDecWaves;
+      if (c + 1 < nchunks && tn < s_end) load_k(tn);
+    }
+    if (keep) {
+      ++n_exec;
+      const float m_new = fmaxf(m_run, mx);
+      if (wave_ballot(m_new > m_run)) {
+        const float alpha = m_new > m_run ? exp2_fast((m_run - m_new) * a.scale_log2) : 1.f;
+        l_part *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+        m_run = m_new;
+      }
+      const float moff = (m_run == neg_inf() ? 0.f : m_run) * a.scale_log2;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        // P^T operand: keys st*32 + 16*(e/4) + 4*grp + (e%4) = s[2st + e/4][e%4]
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = exp2_fast(s[2 * st + (e >> 2)][e & 3] * a.scale_log2 - moff);
+          l_part += p[e];
+        }
+        const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // A_j: channel 8m + j of the 8 loaded key rows, packed two keys per dword
+          const int dw = j >> 1;
+          u32x4 av;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t x0 = vreg[st][2 * u][dw], x1 = vreg[st][2 * u + 1][dw];
+            av[u] = (j & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+          }
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pb, acc[j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- combine the four waves' partial softmax states
+  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (grp == 0) {
+    cm[w][qc] = m_run;
+    cl[w][qc] = l_tot;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = 32 * grp + 8 * i + j;
+      if (ch < D) cacc[w][qc][ch] = acc[j][i];
+    }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int q = idx / D, ch = idx - q * D;
+    float mstar = neg_inf();
+#pragma unroll
+    for (int w2 = 0; w2 < kDecWaves; ++w2) mstar = fmaxf(mstar, cm[w2][q]);
+    float lsum = 0.f, o = 0.f;
+    if (mstar != neg_inf()) {
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) {
+        const float f = cm[w2][q] == neg_inf() ? 0.f : exp2_fast((cm[w2][q] - mstar) * a.scale_log2);
+        lsum += f * cl[w2][q];
+        o += f * cacc[w2][q][ch];
+      }
+    }
+    const bool ok = lsum > 0.f;
+    a.part_o[(part_row + (int64_t)q * P) * D + ch] = ok ? o / lsum : 0.f;
+    if (ch == 0) a.part_lse[part_row + (int64_t)q * P] = ok ? mstar * a.scale_log2 + __builtin_log2f(lsum) : neg_inf();
+  }
+  if (a.counters && lane == 0) {
+    atomicAdd(&a.counters[0], (unsigned long long)n_vis);
+    atomicAdd(&a.counters[1], (unsigned long long)(n_vis - n_exec));
+    atomicAdd(&a.counters[2], (unsigned long long)n_vis);
+    atomicAdd(&a.counters[3], (unsigned long long)n_exec);
+  }
+}
+
+// out[b, h, :] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M); 0 when every split is empty.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x, ch = threadIdx.x;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  const int P = a.num_splits;
+  const float* lse = a.part_lse + (int64_t)bh * P;
+  const float* po = a.part_o + (int64_t)bh * P * D;
+  float M = neg_inf();
+  for (int s = 0; s < P; ++s) M = fmaxf(M, lse[s]);
+  float wsum = 0.f, o = 0.f;
+  if (M != neg_inf())
+    for (int s = 0; s < P; ++s) {
+      const float wgt = exp2_fast(lse[s] - M);
+      wsum += wgt;
+      o += wgt * po[(int64_t)s * D + ch];
+    }
+  const float r = wsum > 0.f ? o / wsum : 0.f;
+  const __bf16 x = (__bf16)r;
+  a.o[(int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ch] = __builtin_bit_cast(uint16_t, x);
+}
+
+hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
+                              hipStream_t stream) {
+  const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv * a.num_splits);
+  const unsigned cgrid = (unsigned)((int64_t)a.B * a.Hq);
+  if (grid == 0) return hipSuccess;
+  if (d == 128) {
+    hipLaunchKernelGGL((decode_split_kernel<128>), dim3(grid), dim3(256), 0, stream, a, kv_cap, k_pool_rows, v_pool_rows);
+    hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(cgrid), dim3(128), 0, stream, a);
+  } else if (d == 64) {
+    hipLaunchKernelGGL((decode_split_kernel<64>), dim3(grid), dim3(256), 0, stream, a, kv_cap, k_pool_rows, v_pool_rows);
+    hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(cgrid), dim3(64), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ssm

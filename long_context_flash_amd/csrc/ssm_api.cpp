@@ -1,0 +1,252 @@
+// ssm_api.cpp -- C ABI of libssm.so: argument validation, defaults, launch.
+//
+// Every check runs on the host before any HIP call, so invalid requests return
+// an error code without touching the device.  Nothing here allocates device
+// memory, synchronises, or reads device data.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ssm.h"
+#include "ssm_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_tensor(const ssm_tensor* t, const char* name, int ndim, int dtype) {
+  if (!t) return fail(SSM_EINVAL, "%s: NULL descriptor", name);
+  if (!t->data) return fail(SSM_EINVAL, "%s: NULL data pointer", name);
+  if (t->ndim != ndim) return fail(SSM_EINVAL, "%s: expected %d dims, got %d", name, ndim, (int)t->ndim);
+  if (t->dtype != dtype) return fail(SSM_EUNSUPPORTED, "%s: dtype %d not supported (bf16 required)", name, (int)t->dtype);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(SSM_EINVAL, "%s: negative extent in dim %d", name, i);
+  if (t->stride[ndim - 1] != 1) return fail(SSM_EINVAL, "%s: last dimension must be contiguous", name);
+  for (int i = 0; i < ndim - 1; ++i)
+    if (t->stride[i] < 0 || t->stride[i] % 8 != 0)
+      return fail(SSM_EUNSUPPORTED, "%s: stride[%d]=%lld must be a non-negative multiple of 8 elements", name, i,
+                  (long long)t->stride[i]);
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0) return fail(SSM_EUNSUPPORTED, "%s: data must be 16-byte aligned", name);
+  return SSM_OK;
+}
+
+int check_tau(float tau) {
+  if (std::isnan(tau)) return fail(SSM_EINVAL, "tau is NaN");
+  if (tau > 0.f) return fail(SSM_EINVAL, "tau must be -inf or <= 0 (got %g)", (double)tau);
+  return SSM_OK;
+}
+
+int resolve_scale(const ssm_opts* opts, int d, float* scale) {
+  float s = opts ? opts->scale : 0.f;
+  if (std::isnan(s) || s < 0.f || std::isinf(s)) return fail(SSM_EINVAL, "scale must be finite and >= 0");
+  *scale = s > 0.f ? s : 1.f / std::sqrt((float)d);
+  return SSM_OK;
+}
+
+int launch_status(hipError_t e) {
+  if (e != hipSuccess) return fail(SSM_EHIP, "HIP launch failed: %s", hipGetErrorString(e));
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_strerror(int code) {
+  switch (code) {
+    case SSM_OK: return "ok";
+    case SSM_EINVAL: return "invalid argument";
+    case SSM_EUNSUPPORTED: return "unsupported configuration";
+    case SSM_EWORKSPACE: return "workspace missing or too small";
+    case SSM_EHIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+const char* ssm_last_error(void) { return g_last_error; }
+
+size_t ssm_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int32_t num_splits) {
+  if (B < 0 || Hq < 0 || d <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)B * (size_t)Hq * (size_t)num_splits;
+  const size_t o_bytes = rows * (size_t)d * sizeof(float);
+  const size_t lse_off = (o_bytes + 255) & ~(size_t)255;
+  return lse_off + rows * sizeof(float);
+}
+
+int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, int32_t seqlen, int32_t causal,
+                float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream, const ssm_opts* opts) {
+  int rc;
+  if ((rc = check_tensor(q, "q", 4, SSM_BF16)) || (rc = check_tensor(k, "k", 4, SSM_BF16)) ||
+      (rc = check_tensor(v, "v", 4, SSM_BF16)) || (rc = check_tensor(out, "out", 4, SSM_BF16)))
+    return rc;
+  if ((rc = check_tau(tau))) return rc;
+  const int64_t B = q->shape[0], S = q->shape[1], Hq = q->shape[2], d = q->shape[3];
+  const int64_t Hkv = k->shape[2];
+  if (seqlen != S) return fail(SSM_EINVAL, "seqlen %d != q.shape[1] %lld", (int)seqlen, (long long)S);
+  for (int i = 0; i < 4; ++i) {
+    const int64_t want_kv = i == 2 ? Hkv : q->shape[i];
+    if (k->shape[i] != want_kv || v->shape[i] != want_kv)
+      return fail(SSM_EINVAL, "k/v shape mismatch in dim %d", i);
+    if (out->shape[i] != q->shape[i]) return fail(SSM_EINVAL, "out shape mismatch in dim %d", i);
+  }
+  if (Hkv <= 0 || Hq % Hkv != 0) return fail(SSM_EINVAL, "Hq (%lld) must be a positive multiple of Hkv (%lld)",
+                                             (long long)Hq, (long long)Hkv);
+  if (d != 64 && d != 128) return fail(SSM_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  const int tile_q = (opts && opts->tile_q) ? opts->tile_q : 128;
+  const int tile_k = (opts && opts->tile_k) ? opts->tile_k : 64;
+  if (tile_q != 64 && tile_q != 128) return fail(SSM_EUNSUPPORTED, "tile_q %d not supported (64 or 128)", tile_q);
+  if (tile_k != 64) return fail(SSM_EUNSUPPORTED, "tile_k %d not supported (64)", tile_k);
+  float scale;
+  if ((rc = resolve_scale(opts, (int)d, &scale))) return rc;
+  if (B > INT32_MAX || S > (1 << 30) || Hq > 65536) return fail(SSM_EUNSUPPORTED, "problem too large");
+  const int64_t nqt = (S + tile_q - 1) / tile_q, nkt = (S + tile_k - 1) / tile_k;
+  const int64_t units = B * Hq * nqt;
+  if (units > INT32_MAX) return fail(SSM_EUNSUPPORTED, "too many query tiles");
+  if (skip_stats) {
+    if (skip_stats->tile_state && skip_stats->tile_state_len < units * nkt)
+      return fail(SSM_EINVAL, "tile_state needs %lld elements", (long long)(units * nkt));
+    if (skip_stats->unit_gap && skip_stats->unit_gap_len < units * nkt)
+      return fail(SSM_EINVAL, "unit_gap needs %lld elements", (long long)(units * nkt));
+  }
+  if (B == 0 || S == 0 || Hq == 0) return SSM_OK;
+
+  ssm::PrefillArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.k = static_cast<const uint16_t*>(k->data);
+  a.v = static_cast<const uint16_t*>(v->data);
+  a.o = static_cast<uint16_t*>(out->data);
+  a.q_sb = q->stride[0]; a.q_ss = q->stride[1]; a.q_sh = q->stride[2];
+  a.k_sb = k->stride[0]; a.k_ss = k->stride[1]; a.k_sh = k->stride[2];
+  a.v_sb = v->stride[0]; a.v_ss = v->stride[1]; a.v_sh = v->stride[2];
+  a.o_sb = out->stride[0]; a.o_ss = out->stride[1]; a.o_sh = out->stride[2];
+  a.B = (int)B; a.S = (int)S; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv);
+  a.nqt = (int)nqt; a.nkt = (int)nkt;
+  a.causal = causal != 0;
+  const int64_t groups = B * Hkv;
+  a.xcd_groups = groups % 8 == 0 ? (int)(groups / 8) : 0;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tau_raw = std::isinf(tau) ? tau : tau / scale;
+  if (skip_stats) {
+    a.tile_state = skip_stats->tile_state;
+    a.unit_gap = skip_stats->unit_gap;
+    a.counters = skip_stats->counters;
+  }
+  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, static_cast<hipStream_t>(stream)));
+}
+
+static int check_cache(const ssm_kv_cache* c, const char* name, int64_t B, int64_t d, int* kv_cap, int64_t* pool_rows,
+                       int64_t* heads) {
+  if (!c) return fail(SSM_EINVAL, "%s: NULL descriptor", name);
+  int rc = check_tensor(&c->pool, name, 4, SSM_BF16);
+  if (rc) return rc;
+  if (c->pool.shape[3] != d) return fail(SSM_EINVAL, "%s: head_dim mismatch", name);
+  *heads = c->pool.shape[1];
+  if (c->page_table) {
+    if (c->page_size != 64) return fail(SSM_EUNSUPPORTED, "%s: page_size must equal the key tile (64)", name);
+    if (c->pool.shape[2] != 64) return fail(SSM_EINVAL, "%s: pool dim 2 must equal page_size", name);
+    if (c->max_pages <= 0) return fail(SSM_EINVAL, "%s: max_pages must be positive", name);
+    if ((int64_t)c->max_pages * 64 > INT32_MAX) return fail(SSM_EUNSUPPORTED, "%s: too many pages", name);
+    *kv_cap = c->max_pages * 64;
+    *pool_rows = c->pool.shape[0];
+  } else {
+    if (c->pool.shape[0] != B) return fail(SSM_EINVAL, "%s: contiguous cache dim 0 must equal batch", name);
+    if (c->pool.shape[2] > INT32_MAX) return fail(SSM_EUNSUPPORTED, "%s: cache too long", name);
+    *kv_cap = (int)c->pool.shape[2];
+    *pool_rows = 0;
+  }
+  return SSM_OK;
+}
+
+int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+               const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+               const ssm_opts* opts) {
+  int rc;
+  if ((rc = check_tensor(q, "q", 3, SSM_BF16)) || (rc = check_tensor(out, "out", 3, SSM_BF16))) return rc;
+  if (!kv_lens) return fail(SSM_EINVAL, "kv_lens: NULL");
+  if ((rc = check_tau(tau))) return rc;
+  const int64_t B = q->shape[0], Hq = q->shape[1], d = q->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(SSM_EINVAL, "out shape mismatch in dim %d", i);
+  int kcap, vcap;
+  int64_t krows, vrows, hk, hv;
+  if ((rc = check_cache(k_cache, "k_cache", B, d, &kcap, &krows, &hk)) ||
+      (rc = check_cache(v_cache, "v_cache", B, d, &vcap, &vrows, &hv)))
+    return rc;
+  if ((k_cache->page_table == nullptr) != (v_cache->page_table == nullptr))
+    return fail(SSM_EINVAL, "k_cache and v_cache must both be paged or both contiguous");
+  if (hk != hv) return fail(SSM_EINVAL, "k/v head counts differ");
+  const int64_t Hkv = hk;
+  if (Hkv <= 0 || Hq % Hkv != 0) return fail(SSM_EINVAL, "Hq (%lld) must be a positive multiple of Hkv (%lld)",
+                                             (long long)Hq, (long long)Hkv);
+  if (d != 64 && d != 128) return fail(SSM_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  if (Hq / Hkv > 16) return fail(SSM_EUNSUPPORTED, "query heads per KV head must be <= 16");
+  const int tile_k = (opts && opts->tile_k) ? opts->tile_k : 64;
+  if (tile_k != 64) return fail(SSM_EUNSUPPORTED, "tile_k %d not supported (64)", tile_k);
+  const int P = (opts && opts->num_splits) ? opts->num_splits : 16;
+  if (P < 1 || P > 64) return fail(SSM_EUNSUPPORTED, "num_splits %d not supported (1..64)", P);
+  float scale;
+  if ((rc = resolve_scale(opts, (int)d, &scale))) return rc;
+  if (B > 65535 || Hq > 65536 || B * Hkv * P > INT32_MAX) return fail(SSM_EUNSUPPORTED, "problem too large");
+  const int kv_cap = kcap < vcap ? kcap : vcap;
+  const int64_t max_tiles = k_cache->page_table ? k_cache->max_pages : ((int64_t)kcap + 63) / 64;
+  if (skip_stats) {
+    const int64_t need = B * Hkv * max_tiles;
+    if (skip_stats->tile_state && skip_stats->tile_state_len < need)
+      return fail(SSM_EINVAL, "tile_state needs %lld elements", (long long)need);
+    if (skip_stats->unit_gap && skip_stats->unit_gap_len < need)
+      return fail(SSM_EINVAL, "unit_gap needs %lld elements", (long long)need);
+  }
+  const size_t ws = ssm_decode_workspace_bytes((int)B, (int)Hq, (int)d, P);
+  if (!opts || !opts->workspace) return fail(SSM_EWORKSPACE, "decode needs opts->workspace of %zu bytes", ws);
+  if (opts->workspace_bytes < ws) return fail(SSM_EWORKSPACE, "workspace has %zu bytes, needs %zu", opts->workspace_bytes, ws);
+  if (reinterpret_cast<uintptr_t>(opts->workspace) % 256 != 0) return fail(SSM_EINVAL, "workspace must be 256-byte aligned");
+  if (B == 0 || Hq == 0) return SSM_OK;
+
+  ssm::DecodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.k = static_cast<const uint16_t*>(k_cache->pool.data);
+  a.v = static_cast<const uint16_t*>(v_cache->pool.data);
+  a.kv_lens = kv_lens;
+  a.k_pages = k_cache->page_table;
+  a.v_pages = v_cache->page_table;
+  a.q_sb = q->stride[0]; a.q_sh = q->stride[1];
+  a.k_sb = k_cache->pool.stride[0]; a.k_sh = k_cache->pool.stride[1]; a.k_ss = k_cache->pool.stride[2];
+  a.v_sb = v_cache->pool.stride[0]; a.v_sh = v_cache->pool.stride[1]; a.v_ss = v_cache->pool.stride[2];
+  a.k_max_pages = k_cache->max_pages; a.v_max_pages = v_cache->max_pages;
+  a.B = (int)B; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv);
+  a.max_tiles = (int)max_tiles;
+  a.num_splits = P;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tau_raw = std::isinf(tau) ? tau : tau / scale;
+  char* ws_base = static_cast<char*>(opts->workspace);
+  const size_t rows = (size_t)B * Hq * P;
+  a.part_o = reinterpret_cast<float*>(ws_base);
+  a.part_lse = reinterpret_cast<float*>(ws_base + ((rows * d * sizeof(float) + 255) & ~(size_t)255));
+  a.o = static_cast<uint16_t*>(out->data);
+  a.o_sb = out->stride[0]; a.o_sh = out->stride[1];
+  if (skip_stats) {
+    a.tile_state = skip_stats->tile_state;
+    a.unit_gap = skip_stats->unit_gap;
+    a.counters = skip_stats->counters;
+  }
+  return launch_status(ssm::launch_decode_impl(a, (int)d, kv_cap, krows, vrows, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// ssm_launch.h -- kernel argument blocks and launchers (internal to libssm.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int64_t q_sb, q_ss, q_sh;  // element strides of batch, position, head (last dim contiguous)
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int32_t B, S, Hq, Hkv, G;
+  int32_t nqt, nkt;          // query tiles, key tiles
+  int32_t causal;
+  int32_t xcd_groups;        // > 0: KV groups per XCD for the XCD-aware unit order; 0: plain order
+  float scale;               // softmax scale (natural-log logits = scale * q.k)
+  float scale_log2;          // scale * log2(e)
+  float tau_raw;             // tau / scale: threshold on raw q.k gaps; -inf never skips
+  uint8_t* tile_state;       // nullable [units, nkt]
+  float* unit_gap;           // nullable [units, nkt]
+  unsigned long long* counters;  // nullable [4]
+};
+
+struct DecodeArgs {
+  const uint16_t* q;         // [B, Hq, d]
+  const uint16_t* k;         // pool
+  const uint16_t* v;
+  const int32_t* kv_lens;    // [B]
+  const int32_t* k_pages;    // nullable: paged
+  const int32_t* v_pages;
+  int64_t q_sb, q_sh;
+  // contiguous: element offset of key j of (b, g) = b*sb + g*sh + j*ss
+  // paged:      element offset = page*sb + g*sh + (j % 64)*ss, page = table[b*max_pages + j/64]
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int32_t k_max_pages, v_max_pages;
+  int32_t B, Hq, Hkv, G;
+  int32_t max_tiles;         // row length of tile_state / unit_gap
+  int32_t num_splits;
+  float scale, scale_log2, tau_raw;
+  float* part_o;             // workspace [B, Hq, P, d] fp32
+  float* part_lse;           // workspace [B, Hq, P] fp32 (base-2 log-sum-exp of raw-scaled logits)
+  uint16_t* o;               // [B, Hq, d]
+  int64_t o_sb, o_sh;
+  uint8_t* tile_state;
+  float* unit_gap;
+  unsigned long long* counters;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, hipStream_t stream);
+hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
+                              hipStream_t stream);
+
+}  // namespace ssm

@@ -1,0 +1,193 @@
+"""GPU-vs-oracle comparison helpers for the parity tests.
+
+The parity bar (stated for this method's bf16-in / fp32-accumulate kernels):
+  * outputs: max-abs error <= 1e-2 and relative L2 error <= 3e-3 against the fp64 oracle;
+  * skip masks: identical on every tile whose oracle unit gap is at least 1e-3 away from tau.
+    Tiles closer than that are ambiguous (fp32 rounding of the scores may flip them); where the
+    GPU decided such a tile differently, the oracle is re-evaluated with the GPU's decision on
+    exactly those tiles (its mask override) before the outputs are compared.
+"""
+from __future__ import annotations
+
+import math
+import time
+
+import numpy as np
+import torch
+
+import long_context_flash_amd as ssm
+import oracle
+
+MAX_ABS = 1e-2
+REL_L2 = 3e-3
+AMBIGUOUS = 1e-3
+GAP_TOL = 2e-3  # fp32 scores from bf16 inputs vs fp64: |gap error| well below this
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    diff = got - ref
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    denom = float(np.linalg.norm(ref.ravel()))
+    rel = float(np.linalg.norm(diff.ravel()) / denom) if denom > 0 else float(np.linalg.norm(diff.ravel()))
+    return max_abs, rel
+
+
+def compare_masks(st_gpu, st_ref, gamma_ref, tau, where=""):
+    """Assert mask agreement off the ambiguous band; return (flip mask, ambiguous count)."""
+    st_gpu = np.asarray(st_gpu)
+    st_ref = np.asarray(st_ref)
+    if math.isinf(tau):
+        amb = np.zeros(st_ref.shape, bool)
+    else:
+        with np.errstate(invalid="ignore"):
+            amb = np.abs(gamma_ref - tau) < AMBIGUOUS
+    diff = st_gpu != st_ref
+    hard = diff & ~amb
+    if hard.any():
+        idx = np.argwhere(hard)[:5]
+        raise AssertionError(f"{where}: {int(hard.sum())} mask mismatches off the ambiguous band, e.g. "
+                             f"{[(tuple(i), int(st_gpu[tuple(i)]), int(st_ref[tuple(i)]), float(gamma_ref[tuple(i)])) for i in idx]}")
+    return diff & amb, int(amb.sum())
+
+
+def compare_gaps(gap_gpu, gamma_ref, st_ref, where=""):
+    vis = st_ref > 0
+    g = gap_gpu[vis].astype(np.float64)
+    r = gamma_ref[vis]
+    both_inf = np.isinf(g) & np.isinf(r) & (np.sign(g) == np.sign(r))
+    fin = np.isfinite(r)
+    assert (both_inf | fin).all() and np.isfinite(g[fin]).all(), f"{where}: gap infinities differ"
+    err = np.abs(g[fin] - r[fin])
+    assert err.size == 0 or err.max() < GAP_TOL, f"{where}: unit gap error {err.max()}"
+    assert (~vis == np.isnan(gap_gpu)).all(), f"{where}: unvisited tiles must hold NaN gaps"
+
+
+def unit_ids(B, Hq, nqt, units):
+    units = np.asarray(units, np.int64)
+    return units // (Hq * nqt), (units // nqt) % Hq, units % nqt
+
+
+def run_prefill_gpu(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, device="cuda"):
+    q = ssm.bf16_from_bits(data["q"], device)
+    k = ssm.bf16_from_bits(data["k"], device)
+    v = ssm.bf16_from_bits(data["v"], device)
+    units, nkt = ssm.prefill_stats_shape(B, S, Hq, tile_q)
+    stats = ssm.SkipStats.alloc(units, nkt, device, gaps=True)
+    out = ssm.ssm_prefill(q, k, v, causal=causal, tau=tau, skip_stats=stats, tile_q=tile_q)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
+            stats.counters.cpu().numpy())
+
+
+def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, where="prefill", threads=None):
+    """Run the GPU prefill on the whole input and compare the listed units (all when None) with the oracle."""
+    log(f"{where}: GPU prefill B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} tau={tau} tile_q={tile_q}")
+    out, st, gap, cnt = run_prefill_gpu(data, B=B, S=S, Hq=Hq, Hkv=Hkv, d=d, causal=causal, tau=tau, tile_q=tile_q)
+    nqt = -(-S // tile_q)
+    vis = int((st > 0).sum())
+    skipped = int((st == 2).sum())
+    assert list(cnt) == [vis, skipped, vis, vis - skipped], f"{where}: counters {list(cnt)} vs tile_state"
+    if units is None:
+        units = np.arange(B * Hq * nqt)
+    units = np.asarray(units, np.int64)
+    log(f"{where}: oracle on {len(units)} units")
+    ref = oracle.prefill(data["q"], data["k"], data["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
+                         units=units, threads=threads)
+    flips, n_amb = compare_masks(st[units], ref["state"], ref["gamma"], tau, where)
+    compare_gaps(gap[units], ref["gamma"], ref["state"], where)
+    if flips.any():
+        ov = np.where(flips, np.where(st[units] == 2, 1, 0), -1).astype(np.int8)
+        ref = oracle.prefill(data["q"], data["k"], data["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
+                             units=units, override=ov, threads=threads)
+    bb, hh, qq = unit_ids(B, Hq, nqt, units)
+    got = np.zeros_like(ref["out"])
+    for n in range(len(units)):
+        r0 = qq[n] * tile_q
+        r1 = min(S, r0 + tile_q)
+        got[n, :r1 - r0] = out[bb[n], r0:r1, hh[n]]
+    max_abs, rel = errors(got, ref["out"])
+    sparsity = skipped / max(vis, 1)
+    log(f"{where}: max_abs={max_abs:.3e} rel_l2={rel:.3e} ambiguous={n_amb} flips={int(flips.sum())} "
+        f"gpu sparsity={sparsity:.3f}")
+    assert max_abs <= MAX_ABS and rel <= REL_L2, f"{where}: max_abs {max_abs} rel_l2 {rel}"
+    return {"max_abs": max_abs, "rel_l2": rel, "sparsity": sparsity, "state": st, "out": out}
+
+
+def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda"):
+    q = ssm.bf16_from_bits(data["q"], device)
+    lens = torch.from_numpy(data["kv_lens"]).to(device)
+    B, Hq, d = data["q"].shape
+    if paged:
+        kc = ssm.bf16_from_bits(data["k_pool"], device)
+        vc = ssm.bf16_from_bits(data["v_pool"], device)
+        pt = torch.from_numpy(data["page_table"]).to(device)
+        Hkv, max_tiles = kc.shape[1], pt.shape[1]
+    else:
+        kc = ssm.bf16_from_bits(data["k_cache"], device)
+        vc = ssm.bf16_from_bits(data["v_cache"], device)
+        pt = None
+        Hkv, max_tiles = kc.shape[1], -(-kc.shape[2] // 64)
+    stats = ssm.SkipStats.alloc(B * Hkv, max_tiles, device, gaps=True)
+    out = ssm.ssm_decode(q, kc, vc, lens, tau=tau, page_table=pt, num_splits=num_splits, skip_stats=stats)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
+            stats.counters.cpu().numpy())
+
+
+def contiguous_from_pages(pool, page_table, kv_lens, batches):
+    """Gather sequences ``batches`` of a paged pool [pages,Hkv,64,d] into [len(batches),Hkv,smax,d] (layout only)."""
+    nt = -(-kv_lens[batches] // 64)
+    smax = int(max(nt.max(), 1)) * 64
+    Hkv, d = pool.shape[1], pool.shape[3]
+    out = np.zeros((len(batches), Hkv, smax, d), pool.dtype)
+    for i, b in enumerate(batches):
+        pages = page_table[b, :nt[i]]
+        out[i, :, :nt[i] * 64] = pool[pages].transpose(1, 0, 2, 3).reshape(Hkv, nt[i] * 64, d)
+    return out
+
+
+def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", threads=None):
+    """GPU decode on the whole batch vs the oracle on the listed sequences (all when None)."""
+    B, Hq, d = data["q"].shape
+    log(f"{where}: GPU decode B={B} Hq={Hq} d={d} tau={tau} P={num_splits} paged={paged}")
+    out, st, gap, cnt = run_decode_gpu(data, tau=tau, num_splits=num_splits, paged=paged)
+    vis = int((st > 0).sum())
+    skipped = int((st == 2).sum())
+    assert list(cnt) == [vis, skipped, vis, vis - skipped], f"{where}: counters {list(cnt)} vs tile_state"
+    lens = data["kv_lens"]
+    nt = -(-lens // 64)
+    Hkv = st.shape[0] // B
+    assert vis == int(nt.sum()) * Hkv, f"{where}: visited {vis} != {int(nt.sum()) * Hkv}"
+    if batches is None:
+        batches = np.arange(B)
+    batches = np.asarray(batches)
+    if paged:
+        kc = contiguous_from_pages(data["k_pool"], data["page_table"], lens, batches)
+        vc = contiguous_from_pages(data["v_pool"], data["page_table"], lens, batches)
+    else:
+        kc, vc = data["k_cache"][batches], data["v_cache"][batches]
+    log(f"{where}: oracle on {len(batches)} sequences")
+    ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits, threads=threads)
+    mt = ref["state"].shape[1]
+    rows = (batches[:, None] * Hkv + np.arange(Hkv)[None]).ravel()
+    st_g = st[rows][:, :mt]
+    assert not st[rows][:, mt:].any(), f"{where}: tiles past the sequence marked visited"
+    flips, n_amb = compare_masks(st_g, ref["state"], ref["gamma"], tau, where)
+    compare_gaps(gap[rows][:, :mt], ref["gamma"], ref["state"], where)
+    if flips.any():
+        ov = np.where(flips, np.where(st_g == 2, 1, 0), -1).astype(np.int8)
+        ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits,
+                            override=ov, threads=threads)
+    got = out[batches].reshape(ref["out"].shape)
+    max_abs, rel = errors(got, ref["out"])
+    sparsity = skipped / max(vis, 1)
+    log(f"{where}: max_abs={max_abs:.3e} rel_l2={rel:.3e} ambiguous={n_amb} flips={int(flips.sum())} "
+        f"gpu sparsity={sparsity:.3f}")
+    assert max_abs <= MAX_ABS and rel <= REL_L2, f"{where}: max_abs {max_abs} rel_l2 {rel}"
+    return {"max_abs": max_abs, "rel_l2": rel, "sparsity": sparsity, "state": st, "out": out}

@@ -1,0 +1,193 @@
+"""The C ABI library loads, exports every symbol include/ssm.h declares, and rejects invalid
+arguments before touching the device (CPU only: no compute call is made)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_context_flash_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssm.LIB_PATH):
+        pytest.fail("libssm.so is not built (run __graft_entry__.build())")
+    return ssm.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(ssm.EXPORTED_SYMBOLS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", ssm.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (ssm_\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, f"{n} not exported"
+        assert hasattr(lib, n)
+
+
+def test_version_and_strings(lib):
+    assert ssm.ssm_abi_version() == 1
+    for code in range(5):
+        assert ssm.ssm_strerror(code)
+    assert "unknown" in ssm.ssm_strerror(99)
+
+
+def test_workspace_bytes(lib):
+    n = ssm.ssm_decode_workspace_bytes(32, 64, 128, 16)
+    o_bytes = 32 * 64 * 16 * 128 * 4
+    assert n >= o_bytes + 32 * 64 * 16 * 4
+    assert ssm.ssm_decode_workspace_bytes(1, 1, 128, 0) == 0
+
+
+FAKE = 0x10000  # never dereferenced: validation fails first
+
+
+def desc(shape, dtype=ssm.SSM_BF16, data=FAKE, stride=None):
+    d = ssm.Tensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if stride is None:
+        stride, acc = [], 1
+        for s in reversed(shape):
+            stride.insert(0, acc)
+            acc *= s
+    for i, s in enumerate(shape):
+        d.shape[i] = s
+        d.stride[i] = stride[i]
+    return d
+
+
+def call_prefill(lib, q=None, k=None, v=None, o=None, seqlen=256, causal=1, tau=-6.9, opts=None):
+    q = q or desc([1, 256, 8, 128])
+    k = k or desc([1, 256, 2, 128])
+    v = v or desc([1, 256, 2, 128])
+    o = o or desc([1, 256, 8, 128])
+    return lib.ssm_prefill(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), seqlen, causal, tau, ctypes.byref(o),
+                           None, None, ctypes.byref(opts) if opts else None)
+
+
+@pytest.mark.parametrize("case,code", [
+    ("nan_tau", ssm.SSM_EINVAL), ("pos_tau", ssm.SSM_EINVAL), ("null_q", ssm.SSM_EINVAL),
+    ("seqlen", ssm.SSM_EINVAL), ("gqa", ssm.SSM_EINVAL), ("head_dim", ssm.SSM_EUNSUPPORTED),
+    ("dtype", ssm.SSM_EUNSUPPORTED), ("stride", ssm.SSM_EINVAL), ("align", ssm.SSM_EUNSUPPORTED),
+    ("tile_q", ssm.SSM_EUNSUPPORTED), ("tile_k", ssm.SSM_EUNSUPPORTED), ("out_shape", ssm.SSM_EINVAL),
+])
+def test_prefill_rejects(lib, case, code):
+    kw = {}
+    if case == "nan_tau":
+        kw["tau"] = math.nan
+    elif case == "pos_tau":
+        kw["tau"] = 0.5
+    elif case == "null_q":
+        kw["q"] = desc([1, 256, 8, 128], data=0)
+    elif case == "seqlen":
+        kw["seqlen"] = 255
+    elif case == "gqa":
+        kw["k"] = desc([1, 256, 3, 128])
+        kw["v"] = desc([1, 256, 3, 128])
+    elif case == "head_dim":
+        kw["q"], kw["k"], kw["v"], kw["o"] = (desc([1, 256, h, 96]) for h in (8, 2, 2, 8))
+    elif case == "dtype":
+        kw["q"] = desc([1, 256, 8, 128], dtype=ssm.SSM_FP32)
+    elif case == "stride":
+        kw["q"] = desc([1, 256, 8, 128], stride=[256 * 8 * 128, 8 * 128, 128, 2])
+    elif case == "align":
+        kw["q"] = desc([1, 256, 8, 128], data=FAKE + 2)
+    elif case == "tile_q":
+        kw["opts"] = ssm.Opts(0.0, 32, 0, 0, None, 0)
+    elif case == "tile_k":
+        kw["opts"] = ssm.Opts(0.0, 0, 128, 0, None, 0)
+    elif case == "out_shape":
+        kw["o"] = desc([1, 256, 4, 128])
+    rc = call_prefill(lib, **kw)
+    assert rc == code, (rc, ssm.ssm_last_error())
+    assert ssm.ssm_last_error()
+
+
+def test_prefill_stats_too_small(lib):
+    q, k, v, o = desc([1, 256, 8, 128]), desc([1, 256, 2, 128]), desc([1, 256, 2, 128]), desc([1, 256, 8, 128])
+    st = ssm.SkipStatsC()
+    st.tile_state = FAKE
+    st.tile_state_len = 10
+    rc = lib.ssm_prefill(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 256, 1, -6.9, ctypes.byref(o),
+                         ctypes.byref(st), None, None)
+    assert rc == ssm.SSM_EINVAL and "tile_state" in ssm.ssm_last_error()
+
+
+def cache(shape, paged=False, max_pages=0):
+    c = ssm.KvCache()
+    c.pool = desc(shape)
+    if paged:
+        c.page_table = FAKE
+        c.page_size = shape[2]
+        c.max_pages = max_pages
+    return c
+
+
+def call_decode(lib, q=None, kc=None, vc=None, lens=FAKE, tau=-6.9, o=None, opts="default"):
+    q = q or desc([2, 16, 128])
+    o = o or desc([2, 16, 128])
+    kc = kc or cache([2, 2, 1024, 128])
+    vc = vc or cache([2, 2, 1024, 128])
+    if opts == "default":
+        opts = ssm.Opts(0.0, 0, 0, 16, 256 * 1024, 1 << 30)
+    return lib.ssm_decode(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(vc), lens, tau, ctypes.byref(o), None,
+                          None, ctypes.byref(opts) if opts else None)
+
+
+@pytest.mark.parametrize("case,code", [
+    ("no_workspace", ssm.SSM_EWORKSPACE), ("small_workspace", ssm.SSM_EWORKSPACE), ("null_lens", ssm.SSM_EINVAL),
+    ("pos_tau", ssm.SSM_EINVAL), ("page_size", ssm.SSM_EUNSUPPORTED), ("mixed_paging", ssm.SSM_EINVAL),
+    ("group_too_big", ssm.SSM_EUNSUPPORTED), ("splits", ssm.SSM_EUNSUPPORTED), ("batch", ssm.SSM_EINVAL),
+    ("head_dim", ssm.SSM_EUNSUPPORTED),
+])
+def test_decode_rejects(lib, case, code):
+    kw = {}
+    if case == "no_workspace":
+        kw["opts"] = None
+    elif case == "small_workspace":
+        kw["opts"] = ssm.Opts(0.0, 0, 0, 16, 256 * 1024, 100)
+    elif case == "null_lens":
+        kw["lens"] = None
+    elif case == "pos_tau":
+        kw["tau"] = 1.0
+    elif case == "page_size":
+        kw["kc"] = cache([100, 2, 32, 128], paged=True, max_pages=64)
+        kw["vc"] = cache([100, 2, 32, 128], paged=True, max_pages=64)
+    elif case == "mixed_paging":
+        kw["kc"] = cache([100, 2, 64, 128], paged=True, max_pages=64)
+    elif case == "group_too_big":
+        kw["q"], kw["o"] = desc([2, 64, 128]), desc([2, 64, 128])
+        kw["kc"], kw["vc"] = cache([2, 2, 1024, 128]), cache([2, 2, 1024, 128])
+    elif case == "splits":
+        kw["opts"] = ssm.Opts(0.0, 0, 0, 65, 256 * 1024, 1 << 30)
+    elif case == "batch":
+        kw["kc"], kw["vc"] = cache([3, 2, 1024, 128]), cache([3, 2, 1024, 128])
+    elif case == "head_dim":
+        kw["q"], kw["o"] = desc([2, 16, 80]), desc([2, 16, 80])
+        kw["kc"], kw["vc"] = cache([2, 2, 1024, 80]), cache([2, 2, 1024, 80])
+    rc = call_decode(lib, **kw)
+    assert rc == code, (rc, ssm.ssm_last_error())
+
+
+def test_product_does_not_import_oracle():
+    """The binding and the HIP sources never reference the oracle package."""
+    pkg = os.path.join(ROOT, "long_context_flash_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text), f"{f} mentions the oracle"

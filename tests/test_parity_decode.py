@@ -1,0 +1,68 @@
+"""HIP split-K decode vs the fp64 oracle (GPU)."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from parity import check_decode, run_decode_gpu, errors
+
+LN1000 = math.log(1000.0)
+pytestmark = pytest.mark.gpu
+
+
+def _small(**kw):
+    base = dict(B=3, Hq=16, Hkv=2, d=128, kv_len=0, kv_len_lo=900, kv_len_hi=5000, seed=9)
+    base.update(kw)
+    return synth.replace(synth.DECODE_32K, **base)
+
+
+@pytest.mark.parametrize("P", [1, 4, 16])
+@pytest.mark.parametrize("tau", [-LN1000, -math.inf, -4.0])
+def test_small_contiguous(P, tau):
+    data = synth.gen_decode(_small(), contiguous=True, paged=False)
+    check_decode(data, tau=tau, num_splits=P, paged=False, where=f"small contig P={P} tau={tau}")
+
+
+@pytest.mark.parametrize("P", [1, 16])
+def test_small_paged_matches_contiguous(P):
+    data = synth.gen_decode(_small(), contiguous=True, paged=True)
+    a = check_decode(data, tau=-LN1000, num_splits=P, paged=True, where=f"small paged P={P}")
+    b = run_decode_gpu(data, tau=-LN1000, num_splits=P, paged=False)
+    assert np.array_equal(a["out"], b[0]), "paged and contiguous layouts must give identical outputs"
+    assert np.array_equal(a["state"][:, :b[1].shape[1]], b[1])
+
+
+def test_kv_len_edge_cases():
+    """kv_len 0, 1, 63, 64, 65, 129 with 16 splits (many empty splits)."""
+    w = _small(B=6, Hq=8, Hkv=1)
+    lens = np.array([0, 1, 63, 64, 65, 129], np.int32)
+    data = synth.gen_decode(w, kv_lens=lens, contiguous=True, paged=True)
+    for paged in (False, True):
+        r = check_decode(data, tau=-LN1000, num_splits=16, paged=paged, where=f"edge paged={paged}")
+        assert np.all(r["out"][0] == 0), "kv_len 0 gives a zero output"
+
+
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
+def test_group_sizes_d64(G):
+    w = _small(Hq=2 * G, Hkv=2, d=64, seed=10 + G)
+    data = synth.gen_decode(w, contiguous=True, paged=False)
+    check_decode(data, tau=-LN1000, num_splits=8, paged=False, where=f"d64 G={G}")
+
+
+def test_decode_32k_full():
+    """The 32K workload at full size, split-K (16) and the sequential definition (1 split)."""
+    w = synth.DECODE_32K
+    data = synth.gen_decode(w)
+    for P in (16, 1):
+        check_decode(data, tau=w.taus[0], num_splits=P, paged=False, where=f"32k P={P}")
+
+
+def test_decode_128k_paged_sampled():
+    """The 128K paged workload (random page table, variable lengths) at the calibrated taus; the oracle
+    checks four sequences."""
+    w = synth.DECODE_128K
+    data = synth.gen_decode(w)
+    batches = np.array([0, 7, 19, 31])
+    for tau in w.taus:
+        check_decode(data, tau=tau, num_splits=w.num_splits, paged=True, batches=batches, where=f"128k tau={tau}")

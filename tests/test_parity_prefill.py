@@ -1,0 +1,65 @@
+"""HIP prefill vs the fp64 oracle, element by element (GPU)."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from parity import check_prefill, log
+
+LN1000 = math.log(1000.0)
+pytestmark = pytest.mark.gpu
+
+
+def _data(w, **kw):
+    return synth.gen_prefill(synth.replace(w, **kw) if kw else w)
+
+
+@pytest.mark.parametrize("tau", [-LN1000, -math.inf])
+@pytest.mark.parametrize("tile_q", [64, 128])
+def test_tiny_prefill(tau, tile_q):
+    w = synth.TINY_PREFILL
+    r = check_prefill(_data(w), B=w.B, S=w.S, Hq=w.Hq, Hkv=w.Hkv, d=w.d, causal=True, tau=tau, tile_q=tile_q,
+                      where=f"tiny tq{tile_q}")
+    if tau == -LN1000 and tile_q == 64:
+        assert r["sparsity"] > 0
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("S", [1, 63, 65, 200, 1000])
+def test_ragged_lengths(d, causal, S):
+    """Sequence lengths that leave partial query and key tiles, incl. a single token."""
+    w = synth.replace(synth.PREFILL_16K, S=S, Hq=8, Hkv=2, d=d, rank=8, seed=77)
+    for tile_q in (64, 128):
+        check_prefill(_data(w), B=1, S=S, Hq=8, Hkv=2, d=d, causal=causal, tau=-LN1000, tile_q=tile_q,
+                      where=f"ragged S={S} d={d} causal={causal} tq={tile_q}")
+
+
+@pytest.mark.parametrize("tau", [-math.inf, -math.log(100.0), -LN1000, -2.0, 0.0])
+def test_llama_shape_2k(tau):
+    """64 query heads / 8 KV heads (exercises the XCD-aware unit order), several dozen key tiles."""
+    w = synth.replace(synth.PREFILL_16K, S=2048, seed=2048)
+    check_prefill(_data(w), B=1, S=2048, Hq=64, Hkv=8, d=128, causal=True, tau=tau, tile_q=128,
+                  where=f"llama 2k tau={tau}")
+
+
+def test_batch2_noncausal_gqa4():
+    w = synth.replace(synth.PREFILL_16K, B=2, S=777, Hq=16, Hkv=4, d=128, seed=5)
+    check_prefill(_data(w), B=2, S=777, Hq=16, Hkv=4, d=128, causal=False, tau=-4.0, tile_q=128,
+                  where="b2 noncausal")
+
+
+def test_prefill_16k_sampled():
+    """The 16K workload at full size; the oracle checks sampled units (first, last and spread q-tiles)."""
+    w = synth.PREFILL_16K
+    data = synth.gen_prefill(w)
+    nqt = w.S // 128
+    rng = np.random.default_rng(3)
+    heads = rng.choice(w.Hq, 6, replace=False)
+    qts = [0, 1, nqt // 2, nqt - 1]
+    units = np.array([h * nqt + qt for h in heads for qt in qts])
+    for tau in w.taus:
+        r = check_prefill(data, B=1, S=w.S, Hq=w.Hq, Hkv=w.Hkv, d=w.d, causal=True, tau=tau, tile_q=128, units=units,
+                          where=f"16k tau={tau}")
+        log(f"16k tau={tau}: sparsity {r['sparsity']:.3f}")
