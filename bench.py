@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Skip Softmax hot path on one MI355X: causal prefill at 128K + paged split-K decode at 128K.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only prefill|decode]
+
+One step = one ssm_prefill call (batch 1, 64 query / 8 KV heads, d 128, S = 131072, causal,
+tau = -ln 1000, ~50% skipped tiles) followed by one ssm_decode call (batch 32, 64/8 heads,
+d 128, paged KV cache with kv_len ~ U[64K, 128K], 16 splits + log-sum-exp combine, tau
+calibrated for ~50% skipped tiles).  Inputs are seeded synthetic tensors with
+Llama-3.3-70B attention shapes, resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is the prefill's dense-equivalent TFLOP/s
+(4*Hq*d*S*(S+1)/2 FLOP over the prefill kernel's event-timed duration); the decode's
+KV GB/s is reported beside it.  ``roofline`` is the prefill kernel against the bf16 MFMA
+peak; ``roofline_decode`` is the decode path against HBM.  ``cpu_baseline`` is the fp64
+oracle timed on a bounded sample of the same prefill work on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dense-equiv attn TFLOP/s (prefill 128K) + decode KV GB/s, at ~50% tile sparsity"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops(w, visited, kept):
+    dense = 4.0 * w.B * w.Hq * w.d * (w.S * (w.S + 1) / 2 if w.causal else w.S * w.S)
+    per_tile = 2.0 * w.tile_q * w.tile_k * w.d
+    return dense, per_tile * (visited + kept)
+
+
+def decode_bytes(w, lens, state, P):
+    """Algorithmic HBM bytes of one decode call (see the design notes for the accounting)."""
+    import numpy as np
+    d, Hkv, Hq, B = w.d, w.Hkv, w.Hq, w.B
+    k_bytes = float(lens.astype(np.int64).sum()) * Hkv * d * 2
+    nt = -(-lens // 64)
+    kept_rows = 0
+    for b in range(B):
+        last_rows = int(lens[b]) - (int(nt[b]) - 1) * 64
+        st = state[b * Hkv:(b + 1) * Hkv, :nt[b]]
+        kept = st == 1
+        kept_rows += int(kept[:, :-1].sum()) * 64 + int(kept[:, -1].sum()) * last_rows
+    v_kept = float(kept_rows) * d * 2
+    v_all = float(lens.astype(np.int64).sum()) * Hkv * d * 2
+    small = 2 * B * Hq * d * 2 + 2 * float(nt.sum()) * 4 + 2 * B * Hq * P * (d + 1) * 4
+    return k_bytes, v_kept, v_all, small
+
+
+def cpu_baseline_prefill(w, data, threads, n_units=256):
+    """Time the fp64 oracle on a bounded sample of prefill units; dense-equivalent TFLOP/s."""
+    import numpy as np
+    import oracle
+    nqt = -(-w.S // w.tile_q)
+    qts = np.linspace(0, nqt - 1, n_units).round().astype(np.int64)
+    heads = (np.arange(n_units) * 11) % w.Hq
+    units = heads * nqt + qts
+    rows_keys = 0.0
+    for qt in qts:  # dense-equivalent work of these units: sum over rows of visible keys
+        r0, r1 = qt * w.tile_q, min(w.S, (qt + 1) * w.tile_q)
+        rows_keys += sum(i + 1 for i in range(r0, r1))
+    flops = 4.0 * w.d * rows_keys
+    t0 = time.perf_counter()
+    oracle.prefill(data["q"], data["k"], data["v"], causal=True, tau=w.taus[0], tile_q=w.tile_q, tile_k=w.tile_k,
+                   units=units, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_units} prefill units (q-tiles spread evenly over 0..{nqt - 1}, heads rotating) of the "
+                      f"128K prefill, {flops / 1e9:.1f} dense-equiv GFLOP in {dt:.1f} s",
+            "seconds": dt}
+
+
+def cpu_baseline_decode(w, data, tau, threads, batches=(0, 1)):
+    import numpy as np
+    import oracle
+    b = np.array(batches)
+    lens = data["kv_lens"]
+    nt = -(-lens[b] // 64)
+    smax = int(nt.max()) * 64
+    kc = np.zeros((len(b), w.Hkv, smax, w.d), np.uint16)
+    vc = np.zeros_like(kc)
+    for i, bb in enumerate(b):
+        pages = data["page_table"][bb, :nt[i]]
+        kc[i, :, :nt[i] * 64] = data["k_pool"][pages].transpose(1, 0, 2, 3).reshape(w.Hkv, -1, w.d)
+        vc[i, :, :nt[i] * 64] = data["v_pool"][pages].transpose(1, 0, 2, 3).reshape(w.Hkv, -1, w.d)
+    t0 = time.perf_counter()
+    r = oracle.decode(data["q"][b], kc, vc, lens[b], tau=tau, num_splits=w.num_splits, threads=threads)
+    dt = time.perf_counter() - t0
+    kept = r["state"] == 1
+    kv = float(lens[b].astype(np.int64).sum()) * w.Hkv * w.d * 2 + float(kept.sum()) * 64 * w.d * 2
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(b)} of {w.B} decode sequences, all 8 KV groups", "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_flash_amd as ssm
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    threads = synth.default_threads()
+    run_prefill = args.only in (None, "prefill")
+    run_decode = args.only in (None, "decode")
+
+    pw = synth.PREFILL_128K
+    dw = synth.DECODE_128K
+    tau_p = pw.taus[0]
+    tau_d = dw.taus[2]  # oracle-calibrated for ~50% skipped tiles
+
+    if run_prefill:
+        log(f"generating {pw.name} (threads={threads})")
+        pdata = synth.gen_prefill(pw, threads=threads)
+        q, k, v = (ssm.bf16_from_bits(pdata[x], dev) for x in ("q", "k", "v"))
+        pout = torch.empty_like(q)
+        pcnt = torch.zeros(4, dtype=torch.int64, device=dev)
+        pstats = ssm.SkipStats(counters=pcnt)
+    if run_decode:
+        log(f"generating {dw.name}")
+        ddata = synth.gen_decode(dw, threads=threads)
+        dq = ssm.bf16_from_bits(ddata["q"], dev)
+        kp, vp = ssm.bf16_from_bits(ddata["k_pool"], dev), ssm.bf16_from_bits(ddata["v_pool"], dev)
+        pt = torch.from_numpy(ddata["page_table"]).to(dev)
+        lens = torch.from_numpy(ddata["kv_lens"]).to(dev)
+        dout = torch.empty_like(dq)
+        ws = ssm.decode_workspace(dw.B, dw.Hq, dw.d, dw.num_splits, dev)
+        dstate = torch.zeros(dw.B * dw.Hkv, pt.shape[1], dtype=torch.uint8, device=dev)
+        dcnt = torch.zeros(4, dtype=torch.int64, device=dev)
+        dstats = ssm.SkipStats(tile_state=dstate, counters=dcnt)
+    torch.cuda.synchronize()
+
+    def step(i, ev):
+        ev[i][0].record()
+        if run_prefill:
+            ssm.ssm_prefill(q, k, v, causal=True, tau=tau_p, out=pout, skip_stats=pstats, tile_q=pw.tile_q)
+        ev[i][1].record()
+        if run_decode:
+            ssm.ssm_decode(dq, kp, vp, lens, tau=tau_d, out=dout, page_table=pt, num_splits=dw.num_splits,
+                           workspace=ws, skip_stats=dstats)
+        ev[i][2].record()
+
+    mk = lambda n: [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    log(f"warmup {args.warmup}")
+    wev = mk(max(args.warmup, 1))
+    for i in range(args.warmup):
+        step(i, wev)
+    torch.cuda.synchronize()
+    if run_prefill:
+        pcnt.zero_()
+    if run_decode:
+        dcnt.zero_()
+    ev = mk(args.steps)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    d_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    step_ms = wall * 1e3 / args.steps
+    log(f"prefill ms {['%.2f' % x for x in p_ms]}  decode ms {['%.3f' % x for x in d_ms]}  wall/step {step_ms:.2f}")
+
+    res = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(step_ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic: seeded GEN-A prefill / GEN-B decode inputs with Llama-3.3-70B "
+                                    "attention shapes (no weights, no dataset)"}
+    cfg = {"workload": ("prefill_s128k+decode_b32_kv128k_paged" if args.only is None else
+                        (pw.name if run_prefill else dw.name))}
+    if run_prefill:
+        c = pcnt.cpu().numpy() / args.steps
+        visited, skipped = float(c[0]), float(c[1])
+        kept = visited - skipped
+        dense, executed = prefill_flops(pw, visited, kept)
+        t = float(np.mean(p_ms)) / 1e3
+        res["value"] = round(dense / t / 1e12, 2)
+        res["prefill_ms"] = round(t * 1e3, 3)
+        res["prefill_executed_tflops"] = round(executed / t / 1e12, 2)
+        res["prefill_sparsity"] = round(skipped / visited, 4)
+        cfg["prefill"] = {"batch": pw.B, "seq_len": pw.S, "q_heads": pw.Hq, "kv_heads": pw.Hkv, "head_dim": pw.d,
+                          "causal": True, "tau": round(tau_p, 4), "tile_q": pw.tile_q, "tile_k": pw.tile_k,
+                          "relevant_tile_frac": pw.rel_frac, "seed": pw.seed}
+        res["roofline"] = {"bound": "mfma", "achieved": round(executed / t / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(executed / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "traffic": None, "kernel": "prefill_kernel<128,128>",
+                           "per_launch_flop": executed, "note": "executed = 2*128*64*128 FLOP per visited "
+                           "tile (QK^T) + the same per kept tile (PV)"}
+    if run_decode:
+        c = dcnt.cpu().numpy() / args.steps
+        state = dstate.cpu().numpy()
+        lens_np = ddata["kv_lens"]
+        kb, vk, va, small = decode_bytes(dw, lens_np, state, dw.num_splits)
+        t = float(np.mean(d_ms)) / 1e3
+        res["decode_ms"] = round(t * 1e3, 4)
+        res["decode_kv_gbps"] = round((kb + vk) / t / 1e9, 1)
+        res["decode_total_gbps"] = round((kb + vk + small) / t / 1e9, 1)
+        res["decode_dense_equiv_kv_gbps"] = round((kb + va) / t / 1e9, 1)
+        res["decode_sparsity"] = round(float(c[1]) / float(c[0]), 4)
+        cfg["decode"] = {"batch": dw.B, "q_heads": dw.Hq, "kv_heads": dw.Hkv, "head_dim": dw.d, "paged": True,
+                         "page": 64, "kv_len_range": [dw.kv_len_lo, dw.kv_len_hi],
+                         "kv_len_mean": float(lens_np.mean()), "num_splits": dw.num_splits, "tau": tau_d,
+                         "seed": dw.seed}
+        res["roofline_decode"] = {"bound": "hbm", "achieved": round((kb + vk + small) / t / 1e9, 1),
+                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                  "frac": round((kb + vk + small) / t / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                                  "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                                  "per_launch_bytes": kb + vk + small}
+        if "value" not in res:
+            res["value"] = res["decode_kv_gbps"]
+            res["unit"] = "GB/s"
+    res["config"] = cfg
+    if not args.no_cpu_baseline:
+        if run_prefill:
+            log("cpu baseline: oracle on sampled prefill units")
+            res["cpu_baseline"] = cpu_baseline_prefill(pw, pdata, threads)
+            if run_decode:
+                res["cpu_baseline_decode"] = cpu_baseline_decode(dw, ddata, tau_d, threads)
+        elif run_decode:
+            res["cpu_baseline"] = cpu_baseline_decode(dw, ddata, tau_d, threads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

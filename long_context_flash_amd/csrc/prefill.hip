@@ -61,7 +61,7 @@ __device__ __forceinline__ void map_prefill_unit(int bid, const PrefillArgs& a, 
 }
 
 template <int D, int TQ>
-__global__ __launch_bounds__(TQ * 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = TQ / 32;          // waves per workgroup
   constexpr int NT = NW * 64;          // threads
   constexpr int KROW = D + 8;          // K tile row stride in LDS (elements); +16 B avoids bank conflicts

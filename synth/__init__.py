@@ -138,14 +138,15 @@ DECODE_32K = DecodeWorkload("decode_b8_kv32k", seed=1002, B=8, Hq=64, Hkv=8, d=1
                             paged=False, num_splits=16)
 PREFILL_16K = PrefillWorkload("prefill_s16k", seed=1003, B=1, S=16384, Hq=64, Hkv=8, d=128,
                               taus=(float("-inf"), -math.log(100.0), -math.log(1000.0)))
-# rel_frac calibrated with the oracle's mask on sampled units for ~50% skipped tiles at
+# rel_frac calibrated with the oracle's mask on sampled units for >= 50% skipped tiles at
 # tau = -ln 1000 (oracle/calibrate.py writes tests/golden/calibration.json).
 PREFILL_128K = PrefillWorkload("prefill_s128k", seed=1004, B=1, S=131072, Hq=64, Hkv=8, d=128,
-                               rel_frac=0.45, taus=(-math.log(1000.0),))
-# taus calibrated with the oracle for about 0/30/50/70% skipped tiles (same calibration file).
+                               rel_frac=0.4906, taus=(-math.log(1000.0),))
+# taus calibrated with the oracle for about 0/30/50/70% skipped tiles with 16 split-local scans
+# (same calibration file); taus[2] is the ~50% operating point.
 DECODE_128K = DecodeWorkload("decode_b32_kv128k_paged", seed=1005, B=32, Hq=64, Hkv=8, d=128,
                              kv_len_lo=65536, kv_len_hi=131072, paged=True, num_splits=16,
-                             taus=(float("-inf"), -7.0, -6.4, -5.8))
+                             taus=(float("-inf"), -7.518, -6.523, -5.267))
 
 WORKLOADS = {w.name: w for w in (TINY_PREFILL, DECODE_32K, PREFILL_16K, PREFILL_128K, DECODE_128K)}
 

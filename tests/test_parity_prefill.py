@@ -63,3 +63,16 @@ def test_prefill_16k_sampled():
         r = check_prefill(data, B=1, S=w.S, Hq=w.Hq, Hkv=w.Hkv, d=w.d, causal=True, tau=tau, tile_q=128, units=units,
                           where=f"16k tau={tau}")
         log(f"16k tau={tau}: sparsity {r['sparsity']:.3f}")
+
+
+def test_prefill_128k_sampled():
+    """The 128K benchmark workload in the launch configuration the benchmark times; the oracle checks
+    sampled units including the first and the longest query tiles."""
+    w = synth.PREFILL_128K
+    data = synth.gen_prefill(w)
+    nqt = w.S // 128
+    units = np.array([0 * nqt + 0, 9 * nqt + 1, 17 * nqt + 255, 33 * nqt + 512, 40 * nqt + 777, 63 * nqt + nqt - 1,
+                      5 * nqt + nqt - 2, 58 * nqt + 1000])
+    r = check_prefill(data, B=1, S=w.S, Hq=w.Hq, Hkv=w.Hkv, d=w.d, causal=True, tau=w.taus[0], tile_q=128,
+                      units=units, where="128k")
+    assert r["sparsity"] >= 0.45, "the calibrated workload skips about half of its tiles"
