@@ -14,7 +14,7 @@
 //   S^T (64 keys x 32 queries) = K_tile . Q^T on v_mfma_f32_32x32x16_bf16,
 //   so each lane holds ONE query column: the row statistics (max, sum, the
 //   rescale factor) are per-lane scalars and the only cross-lane step is the
-//   exchange with lane^32 that holds the other 32 keys of the same query.
+//   swap with lane^32 (v_permlane32_swap) that holds the other 32 keys.
 //   O^T (d x 32 queries) += V^T . P^T on the same MFMA.  The accumulator layout
 //   of S^T is consumed directly as the P^T operand (converted to bf16 in
 //   registers); V is staged in LDS transposed ([channel][key]) with the keys of
@@ -24,17 +24,29 @@
 // Skip vote: every lane votes "keep" unless its row abstains (no valid key in
 // the tile) or its gap (tile max - running max) is below tau; a wave ballot
 // and one LDS word per wave give the unit's decision at the tile barrier.  The
-// running maximum only advances on kept tiles, which equals the prefix maximum
-// over all visited tiles because tau <= 0 (a skipped tile is below it).
+// running maximum only advances on kept tiles; because tau <= 0 a skipped tile
+// never holds a new maximum, so this equals the prefix maximum over all
+// visited tiles.
 //
-// Pipeline: K and V tiles are double-buffered in LDS; the global loads of tile
-// t+1 are issued before tile t's MFMAs and written to LDS after them.
+// Pipeline: K and V tiles are double-buffered in LDS; the buffer loads of tile
+// t+1 are issued before tile t's MFMAs and written to LDS after them.  Rows
+// past the sequence end fall outside the buffer resource and read as zero, so
+// loads carry no predication.  Tiles wholly inside the causal triangle run a
+// step without any masking code; only the diagonal/ragged tiles mask.
+//
+// Exponentials use a lazily moved reference maximum: P = 2^(S*c - m_ref*c) with
+// m_ref only raised when the true running maximum exceeds it by more than 8
+// (log2 units), which bounds P by 256 and makes the rescale of the output
+// accumulator rare.  The row sums add the same bf16-rounded P that enters the
+// P*V product (v_dot2 against (1, 1)).  The skip vote always uses the true
+// running maximum.
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
 namespace ssm {
 
 constexpr int kTK = 64;
+constexpr float kRefSlack = 8.f;  // log2 units the reference max may trail the true max
 
 __device__ __forceinline__ void map_prefill_unit(int bid, const PrefillArgs& a, int& b, int& h, int& qt) {
   int level, rem;
@@ -62,12 +74,12 @@ __device__ __forceinline__ void map_prefill_unit(int bid, const PrefillArgs& a, 
 
 template <int D, int TQ>
 __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr int NW = TQ / 32;          // waves per workgroup
-  constexpr int NT = NW * 64;          // threads
-  constexpr int KROW = D + 8;          // K tile row stride in LDS (elements); +16 B avoids bank conflicts
-  constexpr int VROW = kTK + 8;        // V^T row stride in LDS (elements)
-  constexpr int KSTEPS = D / 16;       // k-steps of the QK^T MFMA
-  constexpr int CB = D / 32;           // 32-channel blocks of the output
+  constexpr int NW = TQ / 32;             // waves per workgroup
+  constexpr int NT = NW * 64;             // threads
+  constexpr int KROW = D + 8;             // K tile row stride in LDS (elements); +16 B avoids bank conflicts
+  constexpr int VROW = kTK + 8;           // V^T row stride in LDS (elements)
+  constexpr int KSTEPS = D / 16;          // k-steps of the QK^T MFMA
+  constexpr int CB = D / 32;              // 32-channel blocks of the output
   constexpr int KPT = kTK * D / 8 / NT;   // 16-byte K chunks per thread per tile
   constexpr int CPT = kTK * D / (NT * 4); // V channels per thread (4 keys each)
   constexpr int VW = CPT / 2;             // dwords per key row per thread
@@ -75,8 +87,8 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTK * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VROW];
-  __shared__ uint32_t votes[NW];
-  __shared__ float wave_gap[NW];
+  __shared__ uint32_t votes[2][NW];
+  __shared__ float wave_gap[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -87,68 +99,71 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const int S = a.S;
   const int q0 = qt * TQ;
   const int q_end = min(S, q0 + TQ);
-  const int t_last = a.causal ? (q_end - 1) / kTK : a.nkt - 1;
+  const int T = (a.causal ? (q_end - 1) / kTK : a.nkt - 1) + 1;  // visited key tiles
+  // tiles [0, T_in) have every (row, key) pair valid: no masking code runs for them
+  const int full_tiles = S / kTK;
+  const int T_in = q_end < q0 + TQ ? 0 : min(T, a.causal ? min(q0 / kTK, full_tiles) : full_tiles);
   const int64_t unit = ((int64_t)b * a.Hq + h) * a.nqt + qt;
+  const float c2 = a.scale_log2;
+
+  // ---- buffer resources: one (b, head) slice each; bytes past the last row read as zero
+  const rsrc_t rq = make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D));
+  const rsrc_t rk = make_rsrc(a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh, rows_bytes(S, a.k_ss, D));
+  const rsrc_t rv = make_rsrc(a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh, rows_bytes(S, a.v_ss, D));
 
   // ---- Q operand: lane (col, half) holds Q[row][ks*16 + half*8 .. +8] for every k-step
   const int iq = q0 + w * 32 + col;
   const bool row_ok = iq < S;
   bf16x8 qreg[KSTEPS];
   {
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)(row_ok ? iq : 0) * a.q_ss + (int64_t)h * a.q_sh;
+    const uint32_t qoff = row_ok ? (uint32_t)iq * (uint32_t)(a.q_ss * 2) + half * 16 : 0xffffffffu;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 x = row_ok ? ld_global_16(qp + ks * 16 + half * 8) : u32x4{0, 0, 0, 0};
-      qreg[ks] = as_bf16x8(x);
-    }
+    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = as_bf16x8(buffer_load_16(rq, row_ok ? qoff + ks * 32 : qoff));
   }
-  const int wave_q_lo = q0 + w * 32, wave_q_hi = min(q0 + w * 32 + 31, S - 1);
 
-  // ---- tile staging (global -> registers -> LDS)
-  const uint16_t* kb_ptr = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
-  const uint16_t* vb_ptr = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
+  // ---- tile staging: per-thread byte offsets inside a tile never change; tile t adds t*64 rows.
+  // K: thread tid moves 16-byte chunk (tid % (D/8)) of key rows tid/(D/8) + i*KSTRIDE, i < KPT.
+  constexpr int KSTRIDE = NT / (D / 8);
+  const int key0 = tid / (D / 8), ch0 = (tid % (D / 8)) * 8;
+  const uint32_t koff0 = (uint32_t)(key0 * a.k_ss * 2 + ch0 * 2), kstep = (uint32_t)(KSTRIDE * a.k_ss * 2);
+  const int klds0 = key0 * KROW + ch0;
+  const uint32_t k_tile_bytes = (uint32_t)(kTK * a.k_ss * 2), v_tile_bytes = (uint32_t)(kTK * a.v_ss * 2);
+  // V: thread moves keys 4*vkq .. 4*vkq+3 x channels vcg*CPT .. +CPT and writes them transposed;
+  // within each 16-key group the 4-key chunks are stored as 0, 2, 1, 3 (the P^T operand order)
+  const int vkq = tid & 15, vcg = tid >> 4;
+  const uint32_t voff = (uint32_t)(4 * vkq * a.v_ss * 2 + vcg * CPT * 2), vrow = (uint32_t)(a.v_ss * 2);
+  const int vpos = 16 * (vkq >> 2) + 4 * (((vkq & 1) << 1) | ((vkq >> 1) & 1));
   u32x4 kst[KPT];
   uint32_t vst[4][VW];
-  const int vkq = tid & 15, vcg = tid >> 4;  // 4-key group, channel group
-  // keys 4*vkq..4*vkq+3 go to V^T positions in the order the P^T operand expects:
-  // within each 16-key group the 4-key chunks are stored as 0, 2, 1, 3
-  const int vpos = 16 * (vkq >> 2) + 4 * (((vkq & 1) << 1) | ((vkq >> 1) & 1));
 
   auto load_tile = [&](int t) {
+    const uint32_t kb = koff0 + (uint32_t)t * k_tile_bytes;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT, key = c / (D / 8), ch = (c % (D / 8)) * 8;
-      const int j = t * kTK + key;
-      kst[i] = j < S ? ld_global_16(kb_ptr + (int64_t)j * a.k_ss + ch) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < KPT; ++i) kst[i] = buffer_load_16(rk, kb + i * kstep);
+    const uint32_t vb = voff + (uint32_t)t * v_tile_bytes;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = t * kTK + 4 * vkq + r;
-      const uint16_t* p = vb_ptr + (int64_t)(j < S ? j : 0) * a.v_ss + vcg * CPT;
       if constexpr (VW % 4 == 0) {
 #pragma unroll
         for (int c4 = 0; c4 < VW; c4 += 4) {
-          u32x4 x = j < S ? ld_global_16(p + c4 * 2) : u32x4{0, 0, 0, 0};
+          const u32x4 x = buffer_load_16(rv, vb + r * vrow + c4 * 4);
           vst[r][c4] = x[0]; vst[r][c4 + 1] = x[1]; vst[r][c4 + 2] = x[2]; vst[r][c4 + 3] = x[3];
         }
       } else {
         static_assert(VW == 2, "4 channels per thread use one 8-byte load");
-        u32x2 x = j < S ? ld_global_8(p) : u32x2{0, 0};
+        const u32x2 x = buffer_load_8(rv, vb + r * vrow);
         vst[r][0] = x[0]; vst[r][1] = x[1];
       }
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT, key = c / (D / 8), ch = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][key * KROW + ch]) = kst[i];
-    }
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(&k_lds[buf][klds0 + i * KSTRIDE * KROW]) = kst[i];
 #pragma unroll
     for (int p = 0; p < VW; ++p) {
       const int c0 = vcg * CPT + 2 * p;
-      u32x2 even = {(vst[0][p] & 0xffffu) | (vst[1][p] << 16), (vst[2][p] & 0xffffu) | (vst[3][p] << 16)};
-      u32x2 odd = {(vst[0][p] >> 16) | (vst[1][p] & 0xffff0000u), (vst[2][p] >> 16) | (vst[3][p] & 0xffff0000u)};
+      const u32x2 even = {(vst[0][p] & 0xffffu) | (vst[1][p] << 16), (vst[2][p] & 0xffffu) | (vst[3][p] << 16)};
+      const u32x2 odd = {(vst[0][p] >> 16) | (vst[1][p] & 0xffff0000u), (vst[2][p] >> 16) | (vst[3][p] & 0xffff0000u)};
       *reinterpret_cast<u32x2*>(&v_lds[buf][c0 * VROW + vpos]) = even;
       *reinterpret_cast<u32x2*>(&v_lds[buf][(c0 + 1) * VROW + vpos]) = odd;
     }
@@ -158,120 +173,122 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   f32x16 acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
-  float m_run = neg_inf();  // running max of raw scores over kept tiles
-  float l_part = 0.f;       // this lane's half of the softmax denominator
+  float m_true = neg_inf();  // running max of raw scores over kept tiles (the skip rule's m_{i-1})
+  float m_ref = neg_inf();   // reference max of the exponentials (trails m_true by at most 8/c2)
+  float l_part = 0.f;        // this lane's half of the softmax denominator
   int n_exec = 0;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t <= t_last; ++t) {
+  auto step = [&](int t, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     const int buf = t & 1;
-    if (t < t_last) load_tile(t + 1);
+    if (t + 1 < T) load_tile(t + 1);
 
-    // S^T for this wave: keys t*64 .. t*64+63 (two 32-key blocks) x 32 query columns
-    const int key0 = t * kTK;
-    const bool wave_dead = !(wave_q_lo < S) || (a.causal && key0 > wave_q_hi);
+    // S^T for keys t*64 .. t*64+63 (two 32-key blocks) x this wave's 32 query columns
     f32x16 s[2];
-    float mx = neg_inf();
-    if (!wave_dead) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 c = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 c = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          u32x4 x = *reinterpret_cast<const u32x4*>(&k_lds[buf][(kb * 32 + col) * KROW + ks * 16 + half * 8]);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x), qreg[ks], c, 0, 0, 0);
-        }
-        s[kb] = c;
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&k_lds[buf][(kb * 32 + col) * KROW + ks * 16 + half * 8]);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x), qreg[ks], c, 0, 0, 0);
       }
-      // masking: causal diagonal tiles, the ragged last tile, padding rows
-      const bool need_mask = (a.causal && key0 + kTK - 1 > wave_q_lo) || (key0 + kTK > S) || (wave_q_lo + 31 >= S);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool ok = row_ok && j < S && (!a.causal || j <= iq);
-            if (!ok) s[kb][i] = neg_inf();
-          }
-      }
+      s[kb] = c;
+    }
+    if constexpr (MASK) {
+      // key offset o inside the tile is valid for this row iff o <= lim
+      const int key_base = t * kTK;
+      const int lim = !row_ok ? -1 : (a.causal ? min(iq, S - 1) - key_base : S - 1 - key_base);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, swap_halves(mx));
+        for (int i = 0; i < 16; ++i) {
+          const int o = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          s[kb][i] = o <= lim ? s[kb][i] : neg_inf();
+        }
     }
+    float mx = neg_inf();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmax3(mx, s[kb][i], s[kb][i + 1]);
+    mx = pair_max(mx);
 
-    // ---- the skip vote
+    // ---- the skip vote against the running max of the kept tiles so far
     const bool abstain = mx == neg_inf();
-    const float gap = mx - m_run;  // +inf on the first tile with a valid key
-    const bool keep_vote = !abstain && !(gap < a.tau_raw);
-    const uint64_t ball = wave_ballot(keep_vote);
-    if (lane == 0) votes[w] = ball != 0;
+    const float gap = mx - m_true;  // +inf while the row has seen no valid key
+    const uint64_t ball = wave_ballot(!abstain && !(gap < a.tau_raw));
+    if (lane == 0) votes[buf][w] = ball != 0;
     if (a.unit_gap) {
       float gg = abstain ? neg_inf() : gap;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) gg = fmaxf(gg, __shfl_xor(gg, off, 64));
-      if (lane == 0) wave_gap[w] = gg;
+      if (lane == 0) wave_gap[buf][w] = gg;
     }
     __syncthreads();
     bool keep = false;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) keep |= votes[i] != 0;
+    for (int i = 0; i < NW; ++i) keep |= votes[buf][i] != 0;
     if (tid == 0) {
       if (a.tile_state) a.tile_state[unit * a.nkt + t] = keep ? 1 : 2;
       if (a.unit_gap) {
-        float gg = wave_gap[0];
+        float gg = wave_gap[buf][0];
 #pragma unroll
-        for (int i = 1; i < NW; ++i) gg = fmaxf(gg, wave_gap[i]);
+        for (int i = 1; i < NW; ++i) gg = fmaxf(gg, wave_gap[buf][i]);
         a.unit_gap[unit * a.nkt + t] = gg == __builtin_inff() ? gg : gg * a.scale;
       }
     }
 
     if (keep) {
       ++n_exec;
-      if (!wave_dead) {
-        // online softmax update; rescale only when some row's maximum moved
-        const float m_new = fmaxf(m_run, mx);
-        if (wave_ballot(m_new > m_run)) {
-          const float alpha = m_new > m_run ? exp2_fast((m_run - m_new) * a.scale_log2) : 1.f;
-          l_part *= alpha;
+      // online softmax: advance the true max; move the reference max (and rescale) only when it trails by > 8
+      m_true = fmaxf(m_true, mx);
+      const bool move = (m_true - m_ref) * c2 > kRefSlack;  // also true while m_ref = -inf and m_true finite
+      if (wave_ballot(move)) {
+        const float alpha = move ? exp2_fast((m_ref - m_true) * c2) : 1.f;  // 0 when m_ref = -inf
+        l_part *= alpha;
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
-          m_run = m_new;
+        for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
+        m_ref = move ? m_true : m_ref;
+      }
+      const float moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = exp2_fast(fmaf(s[st >> 1][8 * (st & 1) + e], c2, -moff));
+          const float p1 = exp2_fast(fmaf(s[st >> 1][8 * (st & 1) + e + 1], c2, -moff));
+          pk[e >> 1] = pack_bf16x2(p0, p1);
+          l_part = dot2_bf16_sum(pk[e >> 1], l_part);
         }
-        const float moff = (m_run == neg_inf() ? 0.f : m_run) * a.scale_log2;
-        bf16x8 pb[4];
+        pb[st] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+      }
+      // O^T += V^T . P^T
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = exp2_fast(s[st >> 1][8 * (st & 1) + e] * a.scale_log2 - moff);
-            l_part += p[e];
-          }
-          u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-          pb[st] = as_bf16x8(pk);
+          const u32x4 x = *reinterpret_cast<const u32x4*>(&v_lds[buf][(cb * 32 + col) * VROW + 16 * st + 8 * half]);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x), pb[st], acc[cb], 0, 0, 0);
         }
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            u32x4 x = *reinterpret_cast<const u32x4*>(&v_lds[buf][(cb * 32 + col) * VROW + 16 * st + 8 * half]);
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x), pb[st], acc[cb], 0, 0, 0);
-          }
-      }
     }
-    if (t < t_last) store_tile(buf ^ 1);
+    if (t + 1 < T) store_tile(buf ^ 1);
     __syncthreads();
-  }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  // every load issued so far (Q operand, tile 0) has landed: without this the wait-count pass treats
+  // the Q registers as pending inside the loop and stalls each QK^T MFMA on the next tile's prefetch
+  wait_vmem_all();
+  __syncthreads();
+  for (int t = 0; t < T_in; ++t) step(t, false_type{});
+  for (int t = T_in; t < T; ++t) step(t, true_type{});
 
   // ---- epilogue: O = acc / l, bf16
-  const float l_tot = l_part + swap_halves(l_part);
+  const float l_tot = pair_sum(l_part);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
     uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)iq * a.o_ss + (int64_t)h * a.o_sh;
@@ -280,18 +297,18 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int ch = cb * 32 + 8 * gq + 4 * half;
-        u32x2 x = {pack_bf16x2(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv),
-                   pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv)};
+        const u32x2 x = {pack_bf16x2(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv),
+                         pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + ch) = x;
       }
   }
   if (tid == 0) {
-    for (int t = t_last + 1; t < a.nkt; ++t) {
+    for (int t = T; t < a.nkt; ++t) {
       if (a.tile_state) a.tile_state[unit * a.nkt + t] = 0;
       if (a.unit_gap) a.unit_gap[unit * a.nkt + t] = __builtin_nanf("");
     }
     if (a.counters) {
-      const unsigned long long visited = t_last + 1;
+      const unsigned long long visited = T;
       atomicAdd(&a.counters[0], visited);
       atomicAdd(&a.counters[1], visited - n_exec);
       atomicAdd(&a.counters[2], visited);

@@ -115,6 +115,12 @@ int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, i
   const int64_t nqt = (S + tile_q - 1) / tile_q, nkt = (S + tile_k - 1) / tile_k;
   const int64_t units = B * Hq * nqt;
   if (units > INT32_MAX) return fail(SSM_EUNSUPPORTED, "too many query tiles");
+  // the kernels address each (batch, head) slice with 32-bit byte offsets
+  for (const ssm_tensor* t : {q, k, v}) {
+    if ((S + 128) * t->stride[1] * 2 + d * 2 > (int64_t)UINT32_MAX)
+      return fail(SSM_EUNSUPPORTED, "sequence too long for 32-bit slice offsets (S=%lld, row stride %lld)",
+                  (long long)S, (long long)t->stride[1]);
+  }
   if (skip_stats) {
     if (skip_stats->tile_state && skip_stats->tile_state_len < units * nkt)
       return fail(SSM_EINVAL, "tile_state needs %lld elements", (long long)(units * nkt));

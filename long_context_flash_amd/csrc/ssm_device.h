@@ -5,6 +5,9 @@
 
 namespace ssm {
 
+struct true_type { static constexpr bool value = true; };
+struct false_type { static constexpr bool value = false; };
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -31,7 +34,48 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 // Value held by lane (lane ^ 32): the two halves of a wave swap.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// v_permlane32_swap with both operands equal to x: lanes < 32 get {x[l], x[l+32]},
+// lanes >= 32 get {x[l-32], x[l]}, so each lane sees the value of lane ^ 32 without LDS.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// acc + lo(pk) + hi(pk) for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float dot2_bf16_sum(uint32_t pk, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+}
+
+// ---- buffer loads: a resource covers [base, base + num_bytes); dwords outside read as 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data format)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, kRsrcWord3);
+}
+// bytes spanned by rows [0, n) of a [n, ...] slice with row stride `stride` elements and d contiguous bf16
+__device__ __forceinline__ uint32_t rows_bytes(int n, int64_t stride, int d) {
+  return n <= 0 ? 0u : (uint32_t)((int64_t)(n - 1) * stride * 2 + d * 2);
+}
+__device__ __forceinline__ u32x4 buffer_load_16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buffer_load_8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): all vector memory loads of this wave done.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 __device__ __forceinline__ u32x4 ld_global_16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld_global_8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
