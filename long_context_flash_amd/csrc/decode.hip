@@ -37,31 +37,28 @@ constexpr int kDecTK = 64;
 constexpr int kDecWaves = 4;
 constexpr int kDecMaxG = 16;
 
-struct TileAddr {
-  const uint16_t* k;  // first key row of the tile (nullptr: page id out of range)
-  const uint16_t* v;
-};
-
-__device__ __forceinline__ TileAddr decode_tile_addr(const DecodeArgs& a, int b, int g, int t, int64_t k_pool_rows,
-                                                     int64_t v_pool_rows) {
-  TileAddr r;
-  if (a.k_pages) {
-    const int pk = a.k_pages[(int64_t)b * a.k_max_pages + t];
-    const int pv = a.v_pages[(int64_t)b * a.v_max_pages + t];
-    r.k = (pk >= 0 && pk < k_pool_rows) ? a.k + (int64_t)pk * a.k_sb + (int64_t)g * a.k_sh : nullptr;
-    r.v = (pv >= 0 && pv < v_pool_rows) ? a.v + (int64_t)pv * a.v_sb + (int64_t)g * a.v_sh : nullptr;
+// Buffer resource over the valid rows of key tile t of (b, g): rows past kv_len, and every row of a
+// tile whose page id is outside the pool, read as zero.
+__device__ __forceinline__ rsrc_t decode_tile_rsrc(const uint16_t* pool, const int32_t* pages, int max_pages,
+                                                   int64_t pool_pages, int64_t sb, int64_t sh, int64_t ss, int b,
+                                                   int g, int t, int len, int d) {
+  const int rows = min(kDecTK, len - t * kDecTK);
+  const uint16_t* base;
+  if (pages) {
+    const int pg = pages[(int64_t)b * max_pages + t];
+    if (pg < 0 || pg >= pool_pages) return make_rsrc(pool, 0u);
+    base = pool + (int64_t)pg * sb + (int64_t)g * sh;
   } else {
-    r.k = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)t * kDecTK * a.k_ss;
-    r.v = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)t * kDecTK * a.v_ss;
+    base = pool + (int64_t)b * sb + (int64_t)g * sh + (int64_t)t * kDecTK * ss;
   }
-  return r;
+  return make_rsrc(base, rows_bytes(rows, ss, d));
 }
 
 // kv_cap: keys the cache can hold (contiguous Smax, paged max_pages*64);
-// pool_rows: number of pages in the pools (paged only).
+// pool_pages: number of pages in the pools (paged only).
 template <int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a, int kv_cap, int64_t k_pool_rows,
-                                                           int64_t v_pool_rows) {
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int kv_cap, int64_t k_pool_pages,
+                                                              int64_t v_pool_pages) {
   constexpr int KS = D / 32;            // k-steps of the QK^T MFMA
   __shared__ float mt[2][kDecWaves][kDecMaxG];  // per-chunk tile maxima (double-buffered by chunk parity)
   __shared__ float cm[kDecWaves][kDecMaxG];
@@ -106,40 +103,44 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a, int kv_
   // Q^T operand: lane (qc, grp) holds Q[qc][ks*32 + grp*8 .. +8]; columns >= G are zero
   bf16x8 qreg[KS];
   {
-    const bool ok = qc < G;
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)(g * G + (ok ? qc : 0)) * a.q_sh;
+    const rsrc_t rq = make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)g * G * a.q_sh, rows_bytes(G, a.q_sh, D));
+    const uint32_t qoff = qc < G ? (uint32_t)(qc * a.q_sh * 2 + grp * 16) : 0xffffffffu;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(ok ? ld_global_16(qp + ks * 32 + grp * 8) : u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(buffer_load_16(rq, qc < G ? qoff + ks * 64 : qoff));
   }
+
+  // lane offsets inside a tile (bytes), fixed for the whole scan
+  uint32_t kvo[4];  // K: row kb*16 + qc, channels grp*8 + ks*32 (+ ks*64 bytes as an immediate)
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) kvo[kb] = (uint32_t)((kb * 16 + qc) * a.k_ss * 2 + grp * 16);
+  // V: lane (m = qc, grp) loads keys st*32 + 16*(e/4) + 4*grp + (e%4), channels 8m .. 8m+7 (zero for 8m >= D)
+  const bool v_ch_ok = qc * 8 < D;
+  uint32_t vvo[2][2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int eh = 0; eh < 2; ++eh)
+      vvo[st][eh] = v_ch_ok ? (uint32_t)((st * 32 + 16 * eh + 4 * grp) * a.v_ss * 2 + qc * 16) : 0xffffffffu;
+  const uint32_t vrow = (uint32_t)(a.v_ss * 2);
 
   const int nchunks = (s_end - s_begin + kDecWaves - 1) / kDecWaves;
   u32x4 kreg[4][KS];  // A operand of the QK^T MFMAs: key block kb, k-step ks
   auto load_k = [&](int t) {
-    const TileAddr ta = decode_tile_addr(a, b, g, t, k_pool_rows, v_pool_rows);
+    const rsrc_t r = decode_tile_rsrc(a.k, a.k_pages, a.k_max_pages, k_pool_pages, a.k_sb, a.k_sh, a.k_ss, b, g, t,
+                                      len, D);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int j = t * kDecTK + kb * 16 + qc;
-      const bool ok = ta.k != nullptr && j < len;
-      const uint16_t* p = ta.k + (int64_t)(kb * 16 + qc) * a.k_ss + grp * 8;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kreg[kb][ks] = ok ? ld_global_16(p + ks * 32) : u32x4{0, 0, 0, 0};
-    }
+      for (int ks = 0; ks < KS; ++ks) kreg[kb][ks] = buffer_load_16(r, kvo[kb] + ks * 64);
   };
-
-  // V^T operand source: lane (m = qc, grp) loads keys f(st, e) = st*32 + 16*(e/4) + 4*grp + (e%4),
-  // channels 8m .. 8m+7 (zero for channels >= D)
   u32x4 vreg[2][8];
   auto load_v = [&](int t) {
-    const TileAddr ta = decode_tile_addr(a, b, g, t, k_pool_rows, v_pool_rows);
-    const bool ch_ok = qc * 8 < D && ta.v != nullptr;
+    const rsrc_t r = decode_tile_rsrc(a.v, a.v_pages, a.v_max_pages, v_pool_pages, a.v_sb, a.v_sh, a.v_ss, b, g, t,
+                                      len, D);
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int f = st * 32 + 16 * (e >> 2) + 4 * grp + (e & 3);
-        const bool ok = ch_ok && t * kDecTK + f < len;
-        vreg[st][e] = ok ? ld_global_16(ta.v + (int64_t)f * a.v_ss + qc * 8) : u32x4{0, 0, 0, 0};
-      }
+      for (int e = 0; e < 8; ++e) vreg[st][e] = buffer_load_16(r, vvo[st][e >> 2] + (e & 3) * vrow);
   };
 
   f32x4 acc[8];  // acc[j][i] = O[query qc][channel 32*grp + 8*i + j]
@@ -153,6 +154,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a, int kv_
     const int t0 = s_begin + w;
     if (t0 < s_end) load_k(t0);
   }
+  // the Q operand and the first K tile have landed before the loop (keeps the wait-count pass from
+  // treating the Q registers as pending inside it)
+  wait_vmem_all();
 
   for (int c = 0; c < nchunks; ++c) {
     const int t = s_begin + c * kDecWaves + w;
@@ -169,12 +173,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a, int kv_
         s[kb] = x;
       }
       // s[kb][i] = S^T[key t*64 + kb*16 + 4*grp + i][query qc]
+      const int lim = qc < G ? len - 1 - t * kDecTK : -1;  // key offset o in the tile is valid iff o <= lim
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = t * kDecTK + kb * 16 + 4 * grp + i;
-          if (qc >= G || j >= len) s[kb][i] = neg_inf();
+          const int o = kb * 16 + 4 * grp + i;
+          if (o > lim) s[kb][i] = neg_inf();
           mx = fmaxf(mx, s[kb][i]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -223,14 +228,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a, int kv_
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         // P^T operand: keys st*32 + 16*(e/4) + 4*grp + (e%4) = s[2st + e/4][e%4]
-        float p[8];
+        uint32_t pk[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = exp2_fast(s[2 * st + (e >> 2)][e & 3] * a.scale_log2 - moff);
-          l_part += p[e];
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = exp2_fast(fmaf(s[2 * st + (e >> 2)][e & 3], a.scale_log2, -moff));
+          const float p1 = exp2_fast(fmaf(s[2 * st + (e >> 2)][(e & 3) + 1], a.scale_log2, -moff));
+          pk[e >> 1] = pack_bf16x2(p0, p1);
+          l_part = dot2_bf16_sum(pk[e >> 1], l_part);
         }
-        const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+        const bf16x8 pb = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           // A_j: channel 8m + j of the 8 loaded key rows, packed two keys per dword
@@ -310,16 +316,16 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   a.o[(int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ch] = __builtin_bit_cast(uint16_t, x);
 }
 
-hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
+hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_pages, int64_t v_pool_pages,
                               hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv * a.num_splits);
   const unsigned cgrid = (unsigned)((int64_t)a.B * a.Hq);
   if (grid == 0) return hipSuccess;
   if (d == 128) {
-    hipLaunchKernelGGL((decode_split_kernel<128>), dim3(grid), dim3(256), 0, stream, a, kv_cap, k_pool_rows, v_pool_rows);
+    hipLaunchKernelGGL((decode_split_kernel<128>), dim3(grid), dim3(256), 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);
     hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(cgrid), dim3(128), 0, stream, a);
   } else if (d == 64) {
-    hipLaunchKernelGGL((decode_split_kernel<64>), dim3(grid), dim3(256), 0, stream, a, kv_cap, k_pool_rows, v_pool_rows);
+    hipLaunchKernelGGL((decode_split_kernel<64>), dim3(grid), dim3(256), 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);
     hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(cgrid), dim3(64), 0, stream, a);
   } else {
     return hipErrorInvalidValue;
