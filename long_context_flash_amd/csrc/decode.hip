@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const uint32_t x0 = vreg[st][2 * u][dw], x1 = vreg[st][2 * u + 1][dw];
-            av[u] = (j & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+            av[u] = (j & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
           }
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pb, acc[j], 0, 0, 0);
         }

@@ -162,8 +162,8 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int p = 0; p < VW; ++p) {
       const int c0 = vcg * CPT + 2 * p;
-      const u32x2 even = {(vst[0][p] & 0xffffu) | (vst[1][p] << 16), (vst[2][p] & 0xffffu) | (vst[3][p] << 16)};
-      const u32x2 odd = {(vst[0][p] >> 16) | (vst[1][p] & 0xffff0000u), (vst[2][p] >> 16) | (vst[3][p] & 0xffff0000u)};
+      const u32x2 even = {pack_lo16(vst[0][p], vst[1][p]), pack_lo16(vst[2][p], vst[3][p])};
+      const u32x2 odd = {pack_hi16(vst[0][p], vst[1][p]), pack_hi16(vst[2][p], vst[3][p])};
       *reinterpret_cast<u32x2*>(&v_lds[buf][c0 * VROW + vpos]) = even;
       *reinterpret_cast<u32x2*>(&v_lds[buf][(c0 + 1) * VROW + vpos]) = odd;
     }
