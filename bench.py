@@ -31,6 +31,84 @@ if ROOT not in sys.path:
 METRIC = "dense-equiv attn TFLOP/s (prefill 128K) + decode KV GB/s, at ~50% tile sparsity"
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "long_context_flash_amd", "csrc")
+KERNEL_SOURCES = {"prefill": ["prefill.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"],
+                  "decode": ["decode.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"]}
+COPY_PROBE_BYTES = 1 << 30
+
+
+def sources_sha(path_kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[path_kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(path_kind):
+    """HBM bytes per launch recorded from FETCH_SIZE/WRITE_SIZE counter runs, if taken on the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[path_kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == sources_sha(path_kind) else None
+
+
+def summarize_traffic(fetch_dir, write_dir, command):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) into HBM bytes per launch,
+    each scaled by what the same counter reads for a device copy of COPY_PROBE_BYTES."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_names = [n for n in fetch if "copy" in n.lower()]
+    copy = max(copy_names, key=lambda n: max(fetch[n]))
+    kib = COPY_PROBE_BYTES / 1024.0
+    f_fac = kib / max(fetch[copy])
+    w_fac = kib / max(write[copy])
+
+    def launch_bytes(pred):
+        tot = 0.0
+        for n in fetch:
+            if pred(n):
+                tot += (sum(fetch[n]) / len(fetch[n]) * f_fac + sum(write[n]) / len(write[n]) * w_fac) * 1024
+        return tot
+
+    rec = {"copy_kernel": copy, "fetch_factor": f_fac, "write_factor": w_fac, "command": command,
+           "prefill": {"kernels": "prefill_kernel", "bytes_per_launch": launch_bytes(lambda n: "prefill_kernel" in n),
+                       "source_sha256": sources_sha("prefill")},
+           "decode": {"kernels": "decode_split_kernel + decode_combine_kernel",
+                      "bytes_per_launch": launch_bytes(lambda n: "decode_split" in n or "decode_combine" in n),
+                      "source_sha256": sources_sha("decode")}}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = ["# HBM traffic from FETCH_SIZE / WRITE_SIZE (rocprofv3 --pmc), prefill_s128k and decode_b32_kv128k_paged",
+             "", "Commands (MI355X, one GPU; $REPO is the repository root):", "", "```", command, "```", "",
+             f"Normalisation: a device copy of {COPY_PROBE_BYTES} bytes (`{copy}`) reads FETCH_SIZE = "
+             f"{max(fetch[copy]):.0f} KiB and WRITE_SIZE = {max(write[copy]):.0f} KiB; factors "
+             f"{f_fac:.4f} (fetch) and {w_fac:.4f} (write) scale each kernel's counters to bytes.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/dispatch (scaled) |",
+             "|---|---|---|---|---|"]
+    for n in sorted(fetch):
+        fk = sum(fetch[n]) / len(fetch[n])
+        wk = sum(write.get(n, [0])) / max(len(write.get(n, [0])), 1)
+        lines.append(f"| `{n[:90]}` | {len(fetch[n])} | {fk:.0f} | {wk:.0f} | {(fk * f_fac + wk * w_fac) * 1024:.4g} |")
+    lines += ["", f"Per launch: prefill {rec['prefill']['bytes_per_launch']:.4g} B; decode (split + combine) "
+              f"{rec['decode']['bytes_per_launch']:.4g} B."]
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic__prefill_s128k__decode_b32_kv128k_paged.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(rec, indent=1))
 
 
 def log(msg):
@@ -113,7 +191,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy a 1 GiB device buffer (normalises FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc output directories and exit")
+    ap.add_argument("--traffic-command", default="", help="command line recorded with --summarize-traffic")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.traffic_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
@@ -211,7 +297,7 @@ def main():
                           "relevant_tile_frac": pw.rel_frac, "seed": pw.seed}
         res["roofline"] = {"bound": "mfma", "achieved": round(executed / t / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(executed / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                           "traffic": None, "kernel": "prefill_kernel<128,128>",
+                           "traffic": recorded_traffic("prefill"), "kernel": "prefill_kernel<128,128>",
                            "per_launch_flop": executed, "note": "executed = 2*128*64*128 FLOP per visited "
                            "tile (QK^T) + the same per kept tile (PV)"}
     if run_decode:
@@ -231,13 +317,21 @@ def main():
                          "seed": dw.seed}
         res["roofline_decode"] = {"bound": "hbm", "achieved": round((kb + vk + small) / t / 1e9, 1),
                                   "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                  "frac": round((kb + vk + small) / t / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                                  "frac": round((kb + vk + small) / t / 1e9 / HBM_PEAK_GBPS, 4),
+                                  "traffic": recorded_traffic("decode"),
                                   "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
                                   "per_launch_bytes": kb + vk + small}
         if "value" not in res:
             res["value"] = res["decode_kv_gbps"]
             res["unit"] = "GB/s"
     res["config"] = cfg
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         if run_prefill:
             log("cpu baseline: oracle on sampled prefill units")
