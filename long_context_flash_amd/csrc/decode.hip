@@ -36,6 +36,7 @@ namespace ssm {
 constexpr int kDecTK = 64;
 constexpr int kDecWaves = 4;
 constexpr int kDecMaxG = 16;
+constexpr int kDecSortMax = 1024;  // batches up to this size are dispatched longest sequence first
 
 // Buffer resource over the valid rows of key tile t of (b, g): rows past kv_len, and every row of a
 // tile whose page id is outside the pool, read as zero.
@@ -45,7 +46,8 @@ __device__ __forceinline__ rsrc_t decode_tile_rsrc(const uint16_t* pool, const i
   const int rows = min(kDecTK, len - t * kDecTK);
   const uint16_t* base;
   if (pages) {
-    const int pg = pages[(int64_t)b * max_pages + t];
+    // the page id is wave-uniform: keep it (and the resource) in scalar registers
+    const int pg = __builtin_amdgcn_readfirstlane(pages[(int64_t)b * max_pages + t]);
     if (pg < 0 || pg >= pool_pages) return make_rsrc(pool, 0u);
     base = pool + (int64_t)pg * sb + (int64_t)g * sh;
   } else {
@@ -65,26 +67,52 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   __shared__ float cl[kDecWaves][kDecMaxG];
   __shared__ __attribute__((aligned(16))) float cacc[kDecWaves][kDecMaxG][D];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ int lens_lds[kDecSortMax];
+  __shared__ unsigned cnt_lds[kDecWaves][2];
+  __shared__ int b_lds;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform: the tile index, its page id and its buffer resource then live in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qc = lane & 15, grp = lane >> 4;  // query column, lane group (key group for operands)
   const int P = a.num_splits;
   const int split = blockIdx.x % P;
-  const int bg = blockIdx.x / P;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int rg = blockIdx.x / P;
+  const int rank = rg / a.Hkv, g = rg - rank * a.Hkv;
   const int G = a.G;
+  auto clamp_len = [&](int l) { return l < 0 ? 0 : (l > kv_cap ? kv_cap : l); };
 
-  int len = a.kv_lens[b];
-  len = len < 0 ? 0 : (len > kv_cap ? kv_cap : len);
+  // Longest sequences first: workgroups are dispatched in index order, so the rank-th longest
+  // sequence (ties by index) takes the rank-th group of Hkv * P workgroups and the short ones
+  // fill the tail.  Batches larger than kDecSortMax keep the plain order.
+  int b = rank;
+  if (a.B <= kDecSortMax) {
+    for (int i = tid; i < a.B; i += 256) lens_lds[i] = clamp_len(a.kv_lens[i]);
+    __syncthreads();
+    for (int c = tid; c < a.B; c += 256) {
+      const int lc = lens_lds[c];
+      int r = 0;
+      for (int j = 0; j < a.B; ++j) {
+        const int lj = lens_lds[j];
+        r += lj > lc || (lj == lc && j < c);
+      }
+      if (r == rank) b_lds = c;
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(b_lds);
+  }
+  const int bg = b * a.Hkv + g;
+  const int len = clamp_len(__builtin_amdgcn_readfirstlane(a.kv_lens[b]));
   const int nt = (len + kDecTK - 1) / kDecTK;
   const int tps = (nt + P - 1) / P;
   const int s_begin = min(nt, split * tps), s_end = min(nt, s_begin + tps);
   const int64_t srow = (int64_t)bg * a.max_tiles;
 
   // statistics rows: this split owns tiles [split*tps, split*tps + tps); the last split also owns the tail
-  if (tid == 0) {
+  {
     const int own_lo = min(a.max_tiles, split * tps);
     const int own_hi = split == P - 1 ? a.max_tiles : min(a.max_tiles, split * tps + tps);
-    for (int t = max(own_lo, s_end); t < own_hi; ++t) {
+    for (int t = max(own_lo, s_end) + tid; t < own_hi; t += 256) {
       if (a.tile_state) a.tile_state[srow + t] = 0;
       if (a.unit_gap) a.unit_gap[srow + t] = __builtin_nanf("");
     }
@@ -286,11 +314,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     a.part_o[(part_row + (int64_t)q * P) * D + ch] = ok ? o / lsum : 0.f;
     if (ch == 0) a.part_lse[part_row + (int64_t)q * P] = ok ? mstar * a.scale_log2 + __builtin_log2f(lsum) : neg_inf();
   }
-  if (a.counters && lane == 0) {
-    atomicAdd(&a.counters[0], (unsigned long long)n_vis);
-    atomicAdd(&a.counters[1], (unsigned long long)(n_vis - n_exec));
-    atomicAdd(&a.counters[2], (unsigned long long)n_vis);
-    atomicAdd(&a.counters[3], (unsigned long long)n_exec);
+  // skip counters: one set of atomics per workgroup
+  if (a.counters) {
+    if (lane == 0) {
+      cnt_lds[w][0] = n_vis;
+      cnt_lds[w][1] = n_exec;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long vis = 0, ex = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) vis += cnt_lds[w2][0], ex += cnt_lds[w2][1];
+      atomicAdd(&a.counters[0], vis);
+      atomicAdd(&a.counters[1], vis - ex);
+      atomicAdd(&a.counters[2], vis);
+      atomicAdd(&a.counters[3], ex);
+    }
   }
 }
 
