@@ -42,7 +42,7 @@ class _PrefillShape(ctypes.Structure):
 class _DecodeShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("smax", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("num_splits", ctypes.c_int32),
-                ("scale", ctypes.c_double), ("tau", ctypes.c_double)]
+                ("scale", ctypes.c_double), ("tau", ctypes.c_double), ("sink_seed", ctypes.c_int32)]
 
 
 def load(path=None):
@@ -118,8 +118,9 @@ def prefill(q, k, v, *, causal=True, tau=-math.log(1000.0), tile_q=128, tile_k=6
 
 
 def decode(q, k, v, kv_lens, *, tau=-math.log(1000.0), tile_k=64, num_splits=16, scale=0.0, units=None,
-           override=None, form="closed", threads=None, lib=None) -> dict:
+           override=None, form="closed", sink_seed=False, threads=None, lib=None) -> dict:
     """Skip Softmax split-K decode on q [B,Hq,d], contiguous caches k/v [B,Hkv,smax,d], kv_lens [B].
+    sink_seed: splits after the first start their running maximum at the first tile's row maxima.
 
     Returns dict: out [n,G,d], lse [n,G], state/gamma [n,ceil(smax/tile_k)], dropped [n,G]
     for the listed units (unit = b*Hkv + g) or all units in that order."""
@@ -138,7 +139,7 @@ def decode(q, k, v, kv_lens, *, tau=-math.log(1000.0), tile_k=64, num_splits=16,
         ov = np.ascontiguousarray(override, dtype=np.int8).reshape(n, maxt)
     res = {"out": np.empty((n, G, d)), "lse": np.empty((n, G)), "state": np.empty((n, maxt), np.uint8),
            "gamma": np.empty((n, maxt)), "dropped": np.empty((n, G))}
-    shape = _DecodeShape(B, Hq, Hkv, d, smax, tile_k, num_splits, float(scale), float(tau))
+    shape = _DecodeShape(B, Hq, Hkv, d, smax, tile_k, num_splits, float(scale), float(tau), 1 if sink_seed else 0)
     rc = (lib or load()).oracle_decode(ctypes.byref(shape), _p(q), _p(k), _p(v), _dtype_code(q, k, v),
                                        _p(kv_lens), _p(units_arr), n, _p(ov), 1 if form == "scan" else 0,
                                        _p(res["out"]), _p(res["lse"]), _p(res["state"]), _p(res["gamma"]),

@@ -31,6 +31,12 @@
  *   5. The running maximum before tile t ("m_{i-1}", written "MI-1" in the
  *      recap's Key Points and Skip Softmax Mechanism): the max of M_r over the
  *      earlier tiles of the same scan, -inf for the scan's first tile.
+ *      Sink-seeded split-K (decode option, READING): a split after the first
+ *      starts from the unit's first-tile maxima M_r(0) instead of -inf, so its
+ *      running maximum is max(M_r(0), earlier tiles of the split).  Tile 0 is
+ *      the first tile of split 0 and is always kept, so the seed is a score the
+ *      combined softmax contains, as the running maximum of one sequential scan
+ *      would be.
  *   6. Gap g_r(t) = M_r(t) - running max (+inf when the running max is -inf);
  *      unit gap Gamma(t) = max over non-abstaining rows (every row of the
  *      tile must agree before the block is skipped, READING of "block").
@@ -78,6 +84,7 @@ typedef struct {
   const int64_t* limit;     /* key j valid for row r iff j < limit[r] */
   int nscans;
   const int* scan_first;    /* [nscans + 1] */
+  int seed_scans;           /* scans after the first start from the first tile's row maxima */
   double scale, tau;
   const int8_t* override;   /* [ntiles] or NULL */
 } unit_t;
@@ -143,7 +150,7 @@ static int unit_closed(const unit_t* u, unit_out* o) {
     }
   /* 5-7: per scan, prefix maxima, gaps, unit gap, decision */
   for (int s = 0; s < u->nscans; ++s) {
-    for (int r = 0; r < nr; ++r) R[r] = -INFINITY;
+    for (int r = 0; r < nr; ++r) R[r] = u->seed_scans && s > 0 && nt > 0 ? M[(int64_t)r * nt] : -INFINITY;
     for (int t = u->scan_first[s]; t < u->scan_first[s + 1]; ++t) {
       double G = -INFINITY;
       int voters = 0;
@@ -211,8 +218,20 @@ static int unit_scan(const unit_t* u, unit_out* o) {
   double* lt = (double*)malloc(sizeof(double) * (size_t)nr * T);
   double* Mt = (double*)malloc(sizeof(double) * (size_t)nr);
   double* row = (double*)malloc(sizeof(double) * (size_t)d);
+  double* seed = (double*)malloc(sizeof(double) * (size_t)nr);
   int rc = 0;
-  if (!m || !l || !a || !os || !ls || !lt || !Mt || !row) { rc = 2; goto done; }
+  if (!m || !l || !a || !os || !ls || !lt || !Mt || !row || !seed) { rc = 2; goto done; }
+  /* sink seeding: the row maxima of the unit's first tile, from its own logits */
+  for (int r = 0; r < nr; ++r) seed[r] = -INFINITY;
+  if (u->seed_scans)
+    for (int j = 0; j < T && j < nk; ++j) {
+      load_row(u, u->k, j, row);
+      for (int r = 0; r < nr; ++r) {
+        if (j >= u->limit[r]) continue;
+        double x = u->scale * dot(u->q + (int64_t)r * d, row, d);
+        if (x > seed[r]) seed[r] = x;
+      }
+    }
   for (int s = 0; s < ns; ++s) {
     for (int r = 0; r < nr; ++r) { m[r] = -INFINITY; l[r] = 0; }
     memset(a, 0, sizeof(double) * (size_t)nr * d);
@@ -232,7 +251,9 @@ static int unit_scan(const unit_t* u, unit_out* o) {
       double G = -INFINITY;
       int voters = 0;
       for (int r = 0; r < nr; ++r) {
-        double g = row_gap(Mt[r], m[r]);
+        /* the scan's running maximum; a seeded split also counts the first tile's maximum */
+        double run = s > 0 && seed[r] > m[r] ? seed[r] : m[r];
+        double g = row_gap(Mt[r], run);
         if (isnan(g)) continue;
         ++voters;
         if (g > G) G = g;
@@ -293,7 +314,7 @@ static int unit_scan(const unit_t* u, unit_out* o) {
     if (o->dropped) o->dropped[r] = NAN;
   }
 done:
-  free(m); free(l); free(a); free(os); free(ls); free(lt); free(Mt); free(row);
+  free(m); free(l); free(a); free(os); free(ls); free(lt); free(Mt); free(row); free(seed);
   return rc;
 }
 
@@ -467,6 +488,7 @@ static int decode_one(void* vctx, int64_t n) {
   u.kv_stride = d;
   u.limit = limit;
   u.nscans = P; u.scan_first = first;
+  u.seed_scans = s->sink_seed != 0;
   u.scale = D->scale; u.tau = s->tau;
   u.override = D->override ? D->override + n * D->maxt : NULL;
   unit_out o;

@@ -50,6 +50,8 @@ typedef struct {
   int32_t smax;
   int32_t tile_k, num_splits;
   double scale, tau;
+  int32_t sink_seed;          /* 1: every split after the first starts its running maximum at the
+                                 unit's first-tile maxima instead of -inf (sink-seeded split-K) */
 } oracle_decode_shape;
 
 /* Decode units are u = b*Hkv + g (rows: the G = Hq/Hkv query heads of group g).

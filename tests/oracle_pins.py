@@ -170,10 +170,13 @@ def pin_forms_agree(lib=None):
         assert np.abs(a["lse"][np.isfinite(a["lse"])] - b["lse"][np.isfinite(b["lse"])]).max() < 1e-12
     q, k, v, lens = decode_planted(5)
     for P in (1, 4, 16):
-        a = oracle.decode(q, k, v, lens, tau=-LN1000, num_splits=P, lib=lib)
-        b = oracle.decode(q, k, v, lens, tau=-LN1000, num_splits=P, form="scan", lib=lib)
-        assert np.array_equal(a["state"], b["state"]), f"decode closed vs scan mask P={P}"
-        assert np.abs(a["out"] - b["out"]).max() < 1e-12
+        for seeded in (False, True):
+            a = oracle.decode(q, k, v, lens, tau=-LN1000, num_splits=P, sink_seed=seeded, lib=lib)
+            b = oracle.decode(q, k, v, lens, tau=-LN1000, num_splits=P, form="scan", sink_seed=seeded, lib=lib)
+            assert np.array_equal(a["state"], b["state"]), f"decode closed vs scan mask P={P} seeded={seeded}"
+            vis = a["state"] > 0
+            assert np.array_equal(a["gamma"][vis], b["gamma"][vis]), f"decode gammas P={P} seeded={seeded}"
+            assert np.abs(a["out"] - b["out"]).max() < 1e-12
 
 
 def decode_planted(seed, B=3, Hq=16, Hkv=2, d=64, smax=4096):
@@ -309,6 +312,38 @@ def pin_output_given_mask(lib=None):
     assert np.abs(got2 - ref2).max() < 1e-12
 
 
+def pin_sink_seed(lib=None):
+    """Sink-seeded split-K decode.  Each split's running maximum is max(first-tile maxima, earlier tiles of
+    the split), which lies between the split-local one (earlier tiles of the split only) and the sequential
+    one (every earlier tile), so the skip sets nest: split-local <= seeded <= sequential (P = 1).  With one
+    split, seeding changes nothing; at tau = -inf nothing is skipped and the output is dense attention; the
+    dropped-mass bound holds, since tile 0 (the seed) is always kept by the first split."""
+    q, k, v, lens = decode_planted(71)
+    dense = sdpa_decode(q, k, v, lens)
+    for tau in (-LN1000, -4.0, -2.0):
+        seq = oracle.decode(q, k, v, lens, tau=tau, num_splits=1, lib=lib)
+        one = oracle.decode(q, k, v, lens, tau=tau, num_splits=1, sink_seed=True, lib=lib)
+        assert np.array_equal(seq["state"], one["state"]) and np.abs(seq["out"] - one["out"]).max() == 0.0
+        for P in (4, 16):
+            loc = oracle.decode(q, k, v, lens, tau=tau, num_splits=P, lib=lib)
+            sd = oracle.decode(q, k, v, lens, tau=tau, num_splits=P, sink_seed=True, lib=lib)
+            s_loc, s_sd, s_seq = (x["state"] == oracle.SKIPPED for x in (loc, sd, seq))
+            assert not (s_loc & ~s_sd).any(), f"split-local skip not kept skipped by seeding (tau={tau}, P={P})"
+            assert not (s_sd & ~s_seq).any(), f"seeded skip not skipped sequentially (tau={tau}, P={P})"
+            assert np.array_equal(loc["state"] > 0, sd["state"] > 0), "visited tiles differ"
+            assert (sd["state"][:, 0] == oracle.EXECUTED).all(), "tile 0 skipped"
+            if tau == -LN1000 and P == 16:
+                assert s_sd.sum() > s_loc.sum(), "seeding must recover sparsity on the planted input"
+            nskip = s_sd.sum(1)
+            assert (sd["dropped"] <= nskip[:, None] * 64 * math.exp(tau) * (1 + 1e-12) + 1e-300).all()
+            delta = sd["dropped"]
+            dev = np.abs(sd["out"] - dense.reshape(sd["out"].shape)).max(-1)
+            assert (dev <= 2 * delta / (1 + delta) * np.abs(v).max() + 1e-12).all()
+    r = oracle.decode(q, k, v, lens, tau=-math.inf, num_splits=16, sink_seed=True, lib=lib)
+    assert not (r["state"] == oracle.SKIPPED).any()
+    assert np.abs(r["out"] - dense.reshape(r["out"].shape)).max() < 1e-12
+
+
 # ----------------------------------------------------------------- worked examples
 def _w1_inputs():
     """d=2, S=128, q_i=(1,0); tile-0 keys (0,0) -> logit 0; tile-1 keys (-10,0) -> logit -10 (scale 1).
@@ -391,8 +426,42 @@ def pin_worked_examples(lib=None):
     assert np.abs(r["out"][0, :, 0] - 2.0).max() < 1e-12
 
 
+def pin_worked_example_sink_seed(lib=None):
+    """W6 (decode, d = 2, scale 1, two query heads q = (1, 0), kv_len = 256, four tiles): the keys of tile t
+    give the logit L_t = (0, 5, -2, -10)[t] and v_j = (t, 1).  At tau = -ln 1000 (about -6.91):
+      split-local, P = 4: every tile is the first of its split            -> kept {0, 1, 2, 3}
+      seeded,      P = 4: tile t > 0 is compared with L_0 = 0: gaps 5, -2, -10       -> kept {0, 1, 2}
+      sequential,  P = 1: running maxima 0, 5, 5: gaps 5, -7, -15                   -> kept {0, 1}
+    and the output is (sum_K t e^L_t / sum_K e^L_t, 1) over the kept set K."""
+    L = [0.0, 5.0, -2.0, -10.0]
+    k = np.zeros((1, 1, 256, 2)); v = np.zeros((1, 1, 256, 2))
+    for t in range(4):
+        k[0, 0, 64 * t:64 * (t + 1), 0] = L[t]
+        v[0, 0, 64 * t:64 * (t + 1)] = (t, 1.0)
+    q = np.zeros((1, 2, 2)); q[..., 0] = 1.0
+    lens = np.array([256], np.int32)
+
+    def want(kept):
+        w = np.array([math.exp(L[t]) for t in kept])
+        return np.array([(w * np.array(kept)).sum() / w.sum(), 1.0])
+
+    for P, seeded, kept in ((4, False, [0, 1, 2, 3]), (4, True, [0, 1, 2]), (1, False, [0, 1]), (1, True, [0, 1]),
+                            (2, True, [0, 1, 2])):
+        # P = 2: splits {0, 1} and {2, 3}; the second starts from L_0 = 0, keeps tile 2 (gap -2), then
+        # compares tile 3 with max(0, -2) = 0 (gap -10): skipped
+        for form in ("closed", "scan"):
+            r = oracle.decode(q, k, v, lens, tau=-LN1000, num_splits=P, scale=1.0, sink_seed=seeded, form=form,
+                              lib=lib)
+            st = [1 if t in kept else 2 for t in range(4)]
+            assert list(r["state"][0]) == st, f"W6 mask P={P} seeded={seeded} {form}: {list(r['state'][0])}"
+            assert np.abs(r["out"][0] - want(kept)).max() < 1e-12, f"W6 output P={P} seeded={seeded} {form}"
+    r = oracle.decode(q, k, v, lens, tau=-LN1000, num_splits=4, scale=1.0, sink_seed=True, lib=lib)
+    assert list(r["gamma"][0]) == [math.inf, 5.0, -2.0, -10.0], "W6 gaps against the seed"
+
+
 ALL_PINS = [pin_dense_prefill, pin_dense_decode, pin_longdouble_bruteforce, pin_forms_agree, pin_mask_invariants,
-            pin_uniform_scores, pin_dropped_mass, pin_split_invariance, pin_output_given_mask, pin_worked_examples]
+            pin_uniform_scores, pin_dropped_mass, pin_split_invariance, pin_output_given_mask, pin_worked_examples,
+            pin_sink_seed, pin_worked_example_sink_seed]
 
 
 def run_all(lib=None):

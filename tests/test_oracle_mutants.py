@@ -29,7 +29,13 @@ MUTANTS = [
     ("values_read_from_keys", "load_row(u, u->v, j, row);", "load_row(u, u->k, j, row);", 2),
     ("normaliser_drops_first_key", "if (m > -INFINITY)\n      for (int j = 0;", "if (m > -INFINITY)\n      for (int j = 1;", 1),
     ("no_rescale_in_scan", "l[r] *= c;", "l[r] *= 1.0;", 1),
-    ("running_max_not_reset_per_split", "for (int r = 0; r < nr; ++r) R[r] = -INFINITY;", "if (s == 0) for (int r = 0; r < nr; ++r) R[r] = -INFINITY;", 1),
+    ("running_max_not_reset_per_split",
+     "for (int r = 0; r < nr; ++r) R[r] = u->seed_scans && s > 0 && nt > 0 ? M[(int64_t)r * nt] : -INFINITY;",
+     "if (s == 0) for (int r = 0; r < nr; ++r) R[r] = -INFINITY;", 1),
+    ("sink_seed_from_split_first_tile", "? M[(int64_t)r * nt] :", "? M[(int64_t)r * nt + u->scan_first[s]] :", 1),
+    ("sink_seed_from_tile_one", "? M[(int64_t)r * nt] :", "? M[(int64_t)r * nt + (nt > 1)] :", 1),
+    ("sink_seed_ignored_in_scan_form", "double run = s > 0 && seed[r] > m[r] ? seed[r] : m[r];", "double run = m[r];", 1),
+    ("sink_seed_flag_dropped", "u.seed_scans = s->sink_seed != 0;", "u.seed_scans = 0;", 1),
     ("combine_equal_weights", "double w = exp(ls[(int64_t)s * nr + r] - big);", "double w = ls[(int64_t)s * nr + r] > -INFINITY ? 1.0 : 0.0;", 1),
     ("tile_max_includes_next_key", "j < (t + 1) * T && j < nk", "j <= (t + 1) * T && j < nk", 1),
     ("split_size_floor", "const int tps = (nt + P - 1) / P;", "const int tps = nt / P > 0 ? nt / P : 1;", 1),
