@@ -139,6 +139,44 @@ def decode_bytes(w, lens, state, P):
     return k_bytes, v_kept, v_all, small
 
 
+def time_sink_seeded_decode(ssm, torch, np, w, data, dq, kp, vp, pt, lens, dout, ws, dstate, tau, steps, dev):
+    """The sink-seeded split-K variant on the same decode workload and tau, timed on its own (after the step
+    timing): HIP events around each call, counters in the timed calls, tile states from one more call."""
+    cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+    stats = ssm.SkipStats(counters=cnt)
+    run = lambda st: ssm.ssm_decode(dq, kp, vp, lens, tau=tau, out=dout, page_table=pt, num_splits=w.num_splits,
+                                    workspace=ws, skip_stats=st, sink_seed=True)
+    run(stats)
+    torch.cuda.synchronize()
+    cnt.zero_()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        run(stats)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    dstate.zero_()
+    run(ssm.SkipStats(tile_state=dstate))
+    state = dstate.cpu().numpy()
+    c = cnt.cpu().numpy() / steps
+    if not (int((state != 0).sum()) == c[0] and int((state == 2).sum()) == c[1]):
+        raise RuntimeError("sink-seeded decode: tile states disagree with the timed counters")
+    kb, vk, va, small = decode_bytes(w, data["kv_lens"], state, w.num_splits)
+    nt = -(-data["kv_lens"] // 64)
+    seeded_splits = 0  # non-empty splits after the first: ceil(n / ceil(n / P)) - 1 per sequence of n tiles
+    for n in (int(x) for x in nt if x > 0):
+        tps = -(-n // w.num_splits)
+        seeded_splits += -(-n // tps) - 1
+    seed_bytes = float(seeded_splits) * w.Hkv * 64 * w.d * 2  # key tile 0 once more per seeded split
+    t = ms / 1e3
+    tot = kb + vk + small + seed_bytes
+    return {"ms": round(ms, 4), "tau": tau, "sparsity": round(float(c[1]) / float(c[0]), 4),
+            "kv_gbps": round((kb + vk) / t / 1e9, 1), "total_gbps": round(tot / t / 1e9, 1),
+            "hbm_frac": round(tot / t / 1e9 / HBM_PEAK_GBPS, 4), "per_launch_bytes": tot,
+            "speedup_vs_split_local": None}
+
+
 def cpu_baseline_prefill(w, data, threads, n_units=256):
     """Time the fp64 oracle on a bounded sample of prefill units; dense-equivalent TFLOP/s."""
     import numpy as np
@@ -337,6 +375,9 @@ def main():
         if "value" not in res:
             res["value"] = res["decode_kv_gbps"]
             res["unit"] = "GB/s"
+        res["decode_sink_seeded"] = time_sink_seeded_decode(ssm, torch, np, dw, ddata, dq, kp, vp, pt, lens, dout, ws,
+                                                            dstate, tau_d, args.steps, dev)
+        res["decode_sink_seeded"]["speedup_vs_split_local"] = round(res["decode_ms"] / res["decode_sink_seeded"]["ms"], 3)
     res["config"] = cfg
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 enum {
   SSM_OK = 0,
@@ -98,7 +98,19 @@ typedef struct {
   int32_t num_splits;      /* decode split-K chunks: 0 -> 16; 1..64 */
   void* workspace;         /* decode: device buffer of >= ssm_decode_workspace_bytes() bytes */
   size_t workspace_bytes;
+  int32_t decode_flags;    /* decode: 0 or SSM_DECODE_SINK_SEED; other bits are SSM_EINVAL */
 } ssm_opts;
+
+/* Sink-seeded split-K decode.  By default every split-K chunk is an independent
+ * scan whose running maximum starts at -inf, so the first tile of every chunk
+ * is kept.  With this flag a chunk after the first starts its running maximum
+ * at the unit's first-tile (tile 0) row maxima: the comparison the recap's Key
+ * Points and Skip Softmax Mechanism make against the running maximum then
+ * includes the score a single sequential scan would already have seen (tile 0
+ * is always kept by the first chunk).  Costs one extra read of key tile 0 per
+ * chunk; skips at least the tiles the default skips.  The output remains the
+ * exact softmax over the kept keys. */
+#define SSM_DECODE_SINK_SEED 1
 
 /* Causal or full prefill (self-attention, S_q = S_k = seqlen).
  *   q   [B, S, Hq, d]  bf16    k, v [B, S, Hkv, d] bf16    out [B, S, Hq, d] bf16
@@ -115,7 +127,8 @@ int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, i
  * The unit of the skip decision is one KV group (its Hq/Hkv query heads vote
  * together).  The unit's n = ceil(kv_len/64) key tiles are cut into num_splits
  * chunks of ceil(n/num_splits) tiles; each chunk is an independent scan whose
- * running maximum starts at -inf, so the first tile of every chunk is kept.
+ * running maximum starts at -inf, so the first tile of every chunk is kept
+ * (see SSM_DECODE_SINK_SEED for the seeded variant).
  * Needs opts->workspace (see ssm_decode_workspace_bytes). */
 int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
                const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,

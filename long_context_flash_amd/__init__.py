@@ -53,7 +53,12 @@ class SkipStatsC(ctypes.Structure):
 
 class Opts(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_float), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
-                ("num_splits", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("num_splits", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("decode_flags", ctypes.c_int32)]
+
+
+ABI_VERSION = 2               # the layout above matches SSM_ABI_VERSION of include/ssm.h
+DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
 
 
 _lib = None
@@ -176,11 +181,13 @@ def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
                tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
                page_table: Optional[torch.Tensor] = None, v_page_table: Optional[torch.Tensor] = None,
                num_splits: int = 16, workspace: Optional[torch.Tensor] = None,
-               skip_stats: Optional[SkipStats] = None, stream=None, scale: float = 0.0) -> torch.Tensor:
+               skip_stats: Optional[SkipStats] = None, stream=None, scale: float = 0.0,
+               sink_seed: bool = False) -> torch.Tensor:
     """Skip Softmax split-K decode.
 
     q [B,Hq,d] bf16; k_cache/v_cache contiguous [B,Hkv,Smax,d] (page_table None) or paged pools
-    [pages,Hkv,64,d] with page_table int32 [B,max_pages]; kv_lens int32 [B] on the GPU."""
+    [pages,Hkv,64,d] with page_table int32 [B,max_pages]; kv_lens int32 [B] on the GPU.
+    sink_seed: splits after the first start their running maximum at the first key tile's row maxima."""
     if out is None:
         out = torch.empty_like(q)
     B, Hq, d = q.shape
@@ -203,7 +210,8 @@ def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
         raise ValueError("kv_lens must be a contiguous int32 tensor")
     kc, vc = cache(k_cache, page_table), cache(v_cache, vpt)
     qd, od = describe(q), describe(out)
-    opts = Opts(float(scale), 0, 64, int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    opts = Opts(float(scale), 0, 64, int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                DECODE_SINK_SEED if sink_seed else 0)
     st = skip_stats.c() if skip_stats is not None else None
     rc = lib().ssm_decode(ctypes.byref(qd), ctypes.byref(kc), ctypes.byref(vc), kv_lens.data_ptr(), float(tau),
                           ctypes.byref(od), ctypes.byref(st) if st else None, _stream_handle(stream),

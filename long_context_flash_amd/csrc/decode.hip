@@ -28,6 +28,11 @@
 //   (eight 16-byte rows) and transposes them in registers; MFMA j uses channel
 //   j of each loaded chunk, so its 16 output rows are channels 8m + j.
 //   V is loaded only after the vote keeps the tile.
+//
+// Sink-seeded split-K (optional): a split after the first starts its prefix
+// maximum at key tile 0's per-query maxima instead of -inf; each wave scores
+// tile 0 once before its scan.  The combined output stays the exact softmax
+// over the kept keys; the seed only changes which tiles are skipped.
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -175,9 +180,41 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f32x4{};
   float m_run = neg_inf(), l_part = 0.f;
-  float r_prev = neg_inf();  // prefix max of tile maxima over earlier chunks (this lane's query)
   unsigned n_exec = 0, n_vis = 0;
 
+  // S^T of key tile t (its K operand in kreg): s[kb][i] = S^T[key t*64 + kb*16 + 4*grp + i][query qc],
+  // -inf for invalid keys and padding columns; returns the tile maximum of this lane's query
+  auto score = [&](int t, f32x4 (&s)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 x = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[kb][ks]), qreg[ks], x, 0, 0, 0);
+      s[kb] = x;
+    }
+    const int lim = qc < G ? len - 1 - t * kDecTK : -1;  // key offset o in the tile is valid iff o <= lim
+    float mx = neg_inf();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = kb * 16 + 4 * grp + i;
+        if (o > lim) s[kb][i] = neg_inf();
+        mx = fmaxf(mx, s[kb][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+  };
+
+  // prefix max of tile maxima over earlier chunks (this lane's query).  A split scan starts at -inf;
+  // with sink seeding, a split after the first starts at key tile 0's maxima (every wave scores it)
+  float r_prev = neg_inf();
+  if (a.sink_seed && s_begin > 0) {
+    load_k(0);
+    f32x4 s0[4];
+    r_prev = score(0, s0);
+  }
   {
     const int t0 = s_begin + w;
     if (t0 < s_end) load_k(t0);
@@ -191,28 +228,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     const bool has = t < s_end;
     f32x4 s[4];
     float mx = neg_inf();
-    if (has) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        f32x4 x = f32x4{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[kb][ks]), qreg[ks], x, 0, 0, 0);
-        s[kb] = x;
-      }
-      // s[kb][i] = S^T[key t*64 + kb*16 + 4*grp + i][query qc]
-      const int lim = qc < G ? len - 1 - t * kDecTK : -1;  // key offset o in the tile is valid iff o <= lim
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int o = kb * 16 + 4 * grp + i;
-          if (o > lim) s[kb][i] = neg_inf();
-          mx = fmaxf(mx, s[kb][i]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    }
+    if (has) mx = score(t, s);
     if (lane < kDecMaxG) mt[c & 1][w][lane] = mx;
     __syncthreads();
     float r = r_prev, r_all = r_prev;

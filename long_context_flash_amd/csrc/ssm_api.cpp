@@ -205,6 +205,8 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
   if (tile_k != 64) return fail(SSM_EUNSUPPORTED, "tile_k %d not supported (64)", tile_k);
   const int P = (opts && opts->num_splits) ? opts->num_splits : 16;
   if (P < 1 || P > 64) return fail(SSM_EUNSUPPORTED, "num_splits %d not supported (1..64)", P);
+  const int32_t flags = opts ? opts->decode_flags : 0;
+  if (flags & ~SSM_DECODE_SINK_SEED) return fail(SSM_EINVAL, "unknown decode_flags bits 0x%x", (unsigned)flags);
   float scale;
   if ((rc = resolve_scale(opts, (int)d, &scale))) return rc;
   if (B > 65535 || Hq > 65536 || B * Hkv * P > INT32_MAX) return fail(SSM_EUNSUPPORTED, "problem too large");
@@ -238,6 +240,7 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
   a.B = (int)B; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv);
   a.max_tiles = (int)max_tiles;
   a.num_splits = P;
+  a.sink_seed = (flags & SSM_DECODE_SINK_SEED) ? 1 : 0;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.tau_raw = std::isinf(tau) ? tau : tau / scale;

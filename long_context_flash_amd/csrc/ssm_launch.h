@@ -42,6 +42,7 @@ struct DecodeArgs {
   int32_t B, Hq, Hkv, G;
   int32_t max_tiles;         // row length of tile_state / unit_gap
   int32_t num_splits;
+  int32_t sink_seed;         // 1: splits after the first start their running max at tile 0's row maxima
   float scale, scale_log2, tau_raw;
   float* part_o;             // workspace [B, Hq, P, d] fp32
   float* part_lse;           // workspace [B, Hq, P] fp32 (base-2 log-sum-exp of raw-scaled logits)

@@ -119,7 +119,7 @@ def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, wh
     return {"max_abs": max_abs, "rel_l2": rel, "sparsity": sparsity, "state": st, "out": out}
 
 
-def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda"):
+def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda", sink_seed=False):
     q = ssm.bf16_from_bits(data["q"], device)
     lens = torch.from_numpy(data["kv_lens"]).to(device)
     B, Hq, d = data["q"].shape
@@ -134,7 +134,8 @@ def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda"):
         pt = None
         Hkv, max_tiles = kc.shape[1], -(-kc.shape[2] // 64)
     stats = ssm.SkipStats.alloc(B * Hkv, max_tiles, device, gaps=True)
-    out = ssm.ssm_decode(q, kc, vc, lens, tau=tau, page_table=pt, num_splits=num_splits, skip_stats=stats)
+    out = ssm.ssm_decode(q, kc, vc, lens, tau=tau, page_table=pt, num_splits=num_splits, skip_stats=stats,
+                         sink_seed=sink_seed)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
             stats.counters.cpu().numpy())
@@ -152,11 +153,11 @@ def contiguous_from_pages(pool, page_table, kv_lens, batches):
     return out
 
 
-def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", threads=None):
+def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", threads=None, sink_seed=False):
     """GPU decode on the whole batch vs the oracle on the listed sequences (all when None)."""
     B, Hq, d = data["q"].shape
-    log(f"{where}: GPU decode B={B} Hq={Hq} d={d} tau={tau} P={num_splits} paged={paged}")
-    out, st, gap, cnt = run_decode_gpu(data, tau=tau, num_splits=num_splits, paged=paged)
+    log(f"{where}: GPU decode B={B} Hq={Hq} d={d} tau={tau} P={num_splits} paged={paged} sink_seed={sink_seed}")
+    out, st, gap, cnt = run_decode_gpu(data, tau=tau, num_splits=num_splits, paged=paged, sink_seed=sink_seed)
     vis = int((st > 0).sum())
     skipped = int((st == 2).sum())
     assert list(cnt) == [vis, skipped, vis, vis - skipped], f"{where}: counters {list(cnt)} vs tile_state"
@@ -173,7 +174,8 @@ def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", 
     else:
         kc, vc = data["k_cache"][batches], data["v_cache"][batches]
     log(f"{where}: oracle on {len(batches)} sequences")
-    ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits, threads=threads)
+    ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits,
+                        sink_seed=sink_seed, threads=threads)
     mt = ref["state"].shape[1]
     rows = (batches[:, None] * Hkv + np.arange(Hkv)[None]).ravel()
     st_g = st[rows][:, :mt]
@@ -183,7 +185,7 @@ def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", 
     if flips.any():
         ov = np.where(flips, np.where(st_g == 2, 1, 0), -1).astype(np.int8)
         ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits,
-                            override=ov, threads=threads)
+                            override=ov, sink_seed=sink_seed, threads=threads)
     got = out[batches].reshape(ref["out"].shape)
     max_abs, rel = errors(got, ref["out"])
     sparsity = skipped / max(vis, 1)

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert ssm.ssm_abi_version() == 1
+    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 2
     for code in range(5):
         assert ssm.ssm_strerror(code)
     assert "unknown" in ssm.ssm_strerror(99)
@@ -152,7 +152,7 @@ def call_decode(lib, q=None, kc=None, vc=None, lens=FAKE, tau=-6.9, o=None, opts
     ("no_workspace", ssm.SSM_EWORKSPACE), ("small_workspace", ssm.SSM_EWORKSPACE), ("null_lens", ssm.SSM_EINVAL),
     ("pos_tau", ssm.SSM_EINVAL), ("page_size", ssm.SSM_EUNSUPPORTED), ("mixed_paging", ssm.SSM_EINVAL),
     ("group_too_big", ssm.SSM_EUNSUPPORTED), ("splits", ssm.SSM_EUNSUPPORTED), ("batch", ssm.SSM_EINVAL),
-    ("head_dim", ssm.SSM_EUNSUPPORTED),
+    ("head_dim", ssm.SSM_EUNSUPPORTED), ("unknown_flag", ssm.SSM_EINVAL),
 ])
 def test_decode_rejects(lib, case, code):
     kw = {}
@@ -179,6 +179,8 @@ def test_decode_rejects(lib, case, code):
     elif case == "head_dim":
         kw["q"], kw["o"] = desc([2, 16, 80]), desc([2, 16, 80])
         kw["kc"], kw["vc"] = cache([2, 2, 1024, 80]), cache([2, 2, 1024, 80])
+    elif case == "unknown_flag":
+        kw["opts"] = ssm.Opts(0.0, 0, 0, 16, 256 * 1024, 1 << 30, 2)
     rc = call_decode(lib, **kw)
     assert rc == code, (rc, ssm.ssm_last_error())
 
@@ -191,3 +193,27 @@ def test_product_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", text), f"{f} mentions the oracle"
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors of the descriptor structs have the C compiler's sizes and field offsets."""
+    structs = {"ssm_tensor": ssm.Tensor, "ssm_kv_cache": ssm.KvCache, "ssm_skip_stats": ssm.SkipStatsC,
+               "ssm_opts": ssm.Opts}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssm.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        cname, field, val = line.split()
+        got[(cname, field)] = int(val)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
