@@ -42,7 +42,8 @@ class _PrefillShape(ctypes.Structure):
 class _DecodeShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("smax", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("num_splits", ctypes.c_int32),
-                ("scale", ctypes.c_double), ("tau", ctypes.c_double), ("sink_seed", ctypes.c_int32)]
+                ("scale", ctypes.c_double), ("tau", ctypes.c_double), ("sink_seed", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_double), ("v_scale", ctypes.c_double)]
 
 
 def load(path=None):
@@ -118,9 +119,12 @@ def prefill(q, k, v, *, causal=True, tau=-math.log(1000.0), tile_q=128, tile_k=6
 
 
 def decode(q, k, v, kv_lens, *, tau=-math.log(1000.0), tile_k=64, num_splits=16, scale=0.0, units=None,
-           override=None, form="closed", sink_seed=False, threads=None, lib=None) -> dict:
+           override=None, form="closed", sink_seed=False, k_scale=1.0, v_scale=1.0, threads=None,
+           lib=None) -> dict:
     """Skip Softmax split-K decode on q [B,Hq,d], contiguous caches k/v [B,Hkv,smax,d], kv_lens [B].
     sink_seed: splits after the first start their running maximum at the first tile's row maxima.
+    k and v may be uint8 arrays of OCP fp8 e4m3 codes; keys and values are then k_scale * code and
+    v_scale * code (the scales also apply to other k/v dtypes).
 
     Returns dict: out [n,G,d], lse [n,G], state/gamma [n,ceil(smax/tile_k)], dropped [n,G]
     for the listed units (unit = b*Hkv + g) or all units in that order."""
@@ -128,6 +132,13 @@ def decode(q, k, v, kv_lens, *, tau=-math.log(1000.0), tile_k=64, num_splits=16,
     kv_lens = np.ascontiguousarray(kv_lens, dtype=np.int32)
     B, Hq, d = q.shape
     _, Hkv, smax, _ = k.shape
+    if k.dtype == np.uint8 or v.dtype == np.uint8:
+        if k.dtype != v.dtype:
+            raise TypeError("k and v must share one dtype")
+        kv_dtype = 3
+    else:
+        kv_dtype = _dtype_code(k, v)
+    q_dtype = _dtype_code(q)
     if k.shape != (B, Hkv, smax, d) or v.shape != k.shape or kv_lens.shape != (B,):
         raise ValueError("k/v must be [B,Hkv,smax,d], kv_lens [B]")
     G = Hq // Hkv
@@ -139,8 +150,9 @@ def decode(q, k, v, kv_lens, *, tau=-math.log(1000.0), tile_k=64, num_splits=16,
         ov = np.ascontiguousarray(override, dtype=np.int8).reshape(n, maxt)
     res = {"out": np.empty((n, G, d)), "lse": np.empty((n, G)), "state": np.empty((n, maxt), np.uint8),
            "gamma": np.empty((n, maxt)), "dropped": np.empty((n, G))}
-    shape = _DecodeShape(B, Hq, Hkv, d, smax, tile_k, num_splits, float(scale), float(tau), 1 if sink_seed else 0)
-    rc = (lib or load()).oracle_decode(ctypes.byref(shape), _p(q), _p(k), _p(v), _dtype_code(q, k, v),
+    shape = _DecodeShape(B, Hq, Hkv, d, smax, tile_k, num_splits, float(scale), float(tau), 1 if sink_seed else 0,
+                         kv_dtype, float(k_scale), float(v_scale))
+    rc = (lib or load()).oracle_decode(ctypes.byref(shape), _p(q), _p(k), _p(v), q_dtype,
                                        _p(kv_lens), _p(units_arr), n, _p(ov), 1 if form == "scan" else 0,
                                        _p(res["out"]), _p(res["lse"]), _p(res["state"]), _p(res["gamma"]),
                                        _p(res["dropped"]), threads or default_threads())

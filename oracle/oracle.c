@@ -49,6 +49,9 @@
  *   8. Output: softmax over the kept keys, o_r = sum_j e^{l-mu} v_j / Z,
  *      lse_r = mu + ln Z.
  *   9. Diagnostics: tile state, Gamma per tile, dropped mass per row.
+ *   Decode K/V may be stored as OCP fp8 e4m3 codes with per-tensor scales
+ *   (key = k_scale * code, value = v_scale * code); steps 1-10 then apply to
+ *   those dequantised values.
  *  10. A second, independent form: the online (running-max) softmax scan the
  *      pages describe, with the split-K log-sum-exp combine.  Because
  *      tau <= 0, a skipped tile never holds a new maximum, so the scan's
@@ -63,9 +66,19 @@
 #include <string.h>
 
 /* ------------------------------------------------------------ input access */
+/* OCP 8-bit float E4M3 ("e4m3fn"): sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+ * is subnormal (m * 2^-9); no infinities; S.1111.111 is NaN; largest finite value 448. */
+static double fp8_e4m3_value(uint8_t b) {
+  const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);  /* (1 + m/8) 2^(e-7) */
+  return sign ? -mag : mag;
+}
+
 static double widen(const void* base, int dt, int64_t i) {
   if (dt == ORACLE_F64) return ((const double*)base)[i];
   if (dt == ORACLE_F32) return (double)((const float*)base)[i];
+  if (dt == ORACLE_FP8E4M3) return fp8_e4m3_value(((const uint8_t*)base)[i]);
   /* bf16: the 16 stored bits are the top half of an IEEE binary32 */
   uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
   float f;
@@ -79,7 +92,8 @@ typedef struct {
   const double* q;          /* [nr][d] */
   const void* k;
   const void* v;
-  int dt;
+  int dt;                   /* dtype of k and v */
+  double k_mul, v_mul;      /* per-tensor dequantisation factors of k and v */
   int64_t kv_base, kv_stride; /* key j, channel c at element kv_base + j*kv_stride + c */
   const int64_t* limit;     /* key j valid for row r iff j < limit[r] */
   int nscans;
@@ -98,7 +112,8 @@ typedef struct {
 } unit_out;
 
 static void load_row(const unit_t* u, const void* src, int j, double* dst) {
-  for (int c = 0; c < u->d; ++c) dst[c] = widen(src, u->dt, u->kv_base + (int64_t)j * u->kv_stride + c);
+  const double mul = src == u->k ? u->k_mul : u->v_mul;
+  for (int c = 0; c < u->d; ++c) dst[c] = mul * widen(src, u->dt, u->kv_base + (int64_t)j * u->kv_stride + c);
 }
 
 static double dot(const double* a, const double* b, int d) {
@@ -398,6 +413,7 @@ static int prefill_one(void* vctx, int64_t n) {
   u.ntiles = s->causal ? (i1 - 1) / s->tile_k + 1 : P->nkt;
   u.nkeys = u.ntiles * s->tile_k < s->S ? u.ntiles * s->tile_k : s->S;
   u.q = q; u.k = P->k; u.v = P->v; u.dt = P->dt;
+  u.k_mul = 1.0; u.v_mul = 1.0;
   u.kv_base = ((int64_t)b * s->S * s->Hkv + g) * d;
   u.kv_stride = (int64_t)s->Hkv * d;
   u.limit = limit;
@@ -452,7 +468,7 @@ int oracle_prefill(const oracle_prefill_shape* s, const void* q, const void* k, 
 typedef struct {
   const oracle_decode_shape* s;
   const void *q, *k, *v;
-  int dt, form, maxt;
+  int dt, kvdt, form, maxt;
   double scale;
   const int32_t* kv_lens;
   const int64_t* units;
@@ -483,7 +499,9 @@ static int decode_one(void* vctx, int64_t n) {
   unit_t u;
   memset(&u, 0, sizeof u);
   u.nr = G; u.d = d; u.tile_k = T; u.ntiles = nt; u.nkeys = len;
-  u.q = q; u.k = D->k; u.v = D->v; u.dt = D->dt;
+  u.q = q; u.k = D->k; u.v = D->v; u.dt = D->kvdt;
+  u.k_mul = s->k_scale > 0 ? s->k_scale : 1.0;
+  u.v_mul = s->v_scale > 0 ? s->v_scale : 1.0;
   u.kv_base = ((int64_t)b * s->Hkv + g) * (int64_t)s->smax * d;
   u.kv_stride = d;
   u.limit = limit;
@@ -508,15 +526,16 @@ int oracle_decode(const oracle_decode_shape* s, const void* q, const void* k, co
                   const int32_t* kv_lens, const int64_t* units, int64_t n_units, const int8_t* override,
                   int form, double* out, double* lse, uint8_t* state, double* gamma, double* dropped,
                   int threads) {
+  const int kvdt = s && s->kv_dtype >= 0 ? s->kv_dtype : in_dtype;
   if (!s || !q || !k || !v || !kv_lens || s->B < 1 || s->Hq < 1 || s->Hkv < 1 || s->d < 1 ||
       s->Hq % s->Hkv || s->smax < 0 || s->tile_k < 1 || s->num_splits < 1 || !valid_tau(s->tau) ||
-      in_dtype < 0 || in_dtype > 2)
+      in_dtype < 0 || in_dtype > 2 || kvdt < 0 || kvdt > 3 || isnan(s->k_scale) || isnan(s->v_scale))
     return 1;
   for (int b = 0; b < s->B; ++b)
     if (kv_lens[b] < 0 || kv_lens[b] > s->smax) return 1;
   decode_job D;
   memset(&D, 0, sizeof D);
-  D.s = s; D.q = q; D.k = k; D.v = v; D.dt = in_dtype; D.form = form;
+  D.s = s; D.q = q; D.k = k; D.v = v; D.dt = in_dtype; D.kvdt = kvdt; D.form = form;
   D.maxt = (s->smax + s->tile_k - 1) / s->tile_k;
   D.scale = s->scale > 0 ? s->scale : 1.0 / sqrt((double)s->d);
   D.kv_lens = kv_lens;

@@ -6,8 +6,9 @@
  * with the HIP library.
  *
  * All buffers are host memory owned by the caller.  Inputs are read as fp32,
- * bf16 bit patterns or fp64 (ORACLE_F32 / ORACLE_BF16 / ORACLE_F64) and
- * widened to double; all arithmetic is in double.
+ * bf16 bit patterns, fp64 or (decode K/V only) OCP fp8 e4m3 codes
+ * (ORACLE_F32 / ORACLE_BF16 / ORACLE_F64 / ORACLE_FP8E4M3) and widened to
+ * double; all arithmetic is in double.
  *
  * Return codes: 0 ok, 1 invalid argument, 2 allocation failure,
  *               3 internal assertion failed (a visited tile with no valid key).
@@ -20,7 +21,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2, ORACLE_FP8E4M3 = 3 };
 enum { ORACLE_CLOSED_FORM = 0, ORACLE_SCAN_FORM = 1 };
 enum { ORACLE_TILE_UNVISITED = 0, ORACLE_TILE_EXECUTED = 1, ORACLE_TILE_SKIPPED = 2 };
 
@@ -52,6 +53,9 @@ typedef struct {
   double scale, tau;
   int32_t sink_seed;          /* 1: every split after the first starts its running maximum at the
                                  unit's first-tile maxima instead of -inf (sink-seeded split-K) */
+  int32_t kv_dtype;           /* dtype of k and v; < 0: the same as q's (in_dtype) */
+  double k_scale, v_scale;    /* per-tensor dequantisation factors: key = k_scale * stored value,
+                                 value = v_scale * stored value; <= 0 means 1 */
 } oracle_decode_shape;
 
 /* Decode units are u = b*Hkv + g (rows: the G = Hq/Hkv query heads of group g).

@@ -344,6 +344,53 @@ def pin_sink_seed(lib=None):
     assert np.abs(r["out"] - dense.reshape(r["out"].shape)).max() < 1e-12
 
 
+def fp8_e4m3_codes_to_f64(codes):
+    """torch's OCP float8_e4m3fn conversion of uint8 codes to float64 (the library routine of the fp8 pin)."""
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_fp8_kv(lib=None):
+    """K/V given as OCP fp8 e4m3 codes with per-tensor scales: the oracle must equal the same decode on the
+    values torch decodes from the codes (times the scales), in both forms, split-local and seeded, and
+    dense SDPA at tau = -inf.  Every finite code (subnormals, both zeros, +-448) appears in K and V."""
+    r0 = rng(81)
+    B, Hq, Hkv, d, smax = 3, 8, 2, 64, 1100
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    kc = r0.choice(finite, size=(B, Hkv, smax, d))
+    vc = r0.choice(finite, size=(B, Hkv, smax, d))
+    kc[0, 0, :len(finite), 0] = finite
+    vc[0, 0, :len(finite), 0] = finite
+    q = r0.standard_normal((B, Hq, d)) * 2e-3          # keeps logits of order 1 for |k| up to 448 * k_scale
+    q[:, :, 1] = 1.0                                     # channel 1 carries a sink: code 0x7E = 448 on tile 0,
+    kc[:, :, :, 1] = 0                                   # zero elsewhere (+20.7 logits on the sink tile)
+    kc[:, :, :64, 1] = 0x7E
+    ks, vs = 0.37, 1.9
+    kf, vf = fp8_e4m3_codes_to_f64(kc) * ks, fp8_e4m3_codes_to_f64(vc) * vs
+    assert np.isfinite(kf).all() and np.isfinite(vf).all()
+    lens = np.array([smax, 777, 64], np.int32)
+    for P, seeded in ((1, False), (16, False), (16, True)):
+        for tau in (-LN1000, -2.0, -math.inf):
+            for form in ("closed", "scan"):
+                a = oracle.decode(q, kc, vc, lens, tau=tau, num_splits=P, sink_seed=seeded, k_scale=ks, v_scale=vs,
+                                  form=form, lib=lib)
+                b = oracle.decode(q, kf, vf, lens, tau=tau, num_splits=P, sink_seed=seeded, form=form, lib=lib)
+                assert np.array_equal(a["state"], b["state"]), f"fp8 mask P={P} seeded={seeded} tau={tau} {form}"
+                assert np.abs(a["out"] - b["out"]).max() < 1e-12, f"fp8 output P={P} seeded={seeded} tau={tau}"
+            if tau == -LN1000 and P == 16:
+                assert (a["state"] == oracle.SKIPPED).any(), "the fp8 input must skip something"
+    dense = sdpa_decode(q, kf, vf, lens)
+    r = oracle.decode(q, kc, vc, lens, tau=-math.inf, num_splits=16, k_scale=ks, v_scale=vs, lib=lib)
+    assert np.abs(r["out"] - dense.reshape(r["out"].shape)).max() < 1e-12
+    # one key per sequence: the output is that key's value, so every code's value is observed directly
+    lens1 = np.ones(len(finite), np.int32)
+    v1 = np.zeros((len(finite), 1, 1, 1), np.uint8); v1[:, 0, 0, 0] = finite
+    k1 = np.zeros_like(v1)
+    r = oracle.decode(np.zeros((len(finite), 1, 1)), k1, v1, lens1, tau=-math.inf, num_splits=1, k_scale=1.0,
+                      v_scale=1.0, lib=lib)
+    assert np.array_equal(r["out"][:, 0, 0], fp8_e4m3_codes_to_f64(finite)), "fp8 code values"
+
+
 # ----------------------------------------------------------------- worked examples
 def _w1_inputs():
     """d=2, S=128, q_i=(1,0); tile-0 keys (0,0) -> logit 0; tile-1 keys (-10,0) -> logit -10 (scale 1).
@@ -461,7 +508,7 @@ def pin_worked_example_sink_seed(lib=None):
 
 ALL_PINS = [pin_dense_prefill, pin_dense_decode, pin_longdouble_bruteforce, pin_forms_agree, pin_mask_invariants,
             pin_uniform_scores, pin_dropped_mass, pin_split_invariance, pin_output_given_mask, pin_worked_examples,
-            pin_sink_seed, pin_worked_example_sink_seed]
+            pin_sink_seed, pin_worked_example_sink_seed, pin_fp8_kv]
 
 
 def run_all(lib=None):

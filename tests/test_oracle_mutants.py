@@ -36,6 +36,11 @@ MUTANTS = [
     ("sink_seed_from_tile_one", "? M[(int64_t)r * nt] :", "? M[(int64_t)r * nt + (nt > 1)] :", 1),
     ("sink_seed_ignored_in_scan_form", "double run = s > 0 && seed[r] > m[r] ? seed[r] : m[r];", "double run = m[r];", 1),
     ("sink_seed_flag_dropped", "u.seed_scans = s->sink_seed != 0;", "u.seed_scans = 0;", 1),
+    ("fp8_exponent_bias_8", "ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)", 1),
+    ("fp8_subnormals_as_normals", "e == 0 ? ldexp((double)m, -9) :", "e < 0 ? ldexp((double)m, -9) :", 1),
+    ("fp8_k_scale_dropped", "u.k_mul = s->k_scale > 0 ? s->k_scale : 1.0;", "u.k_mul = 1.0;", 1),
+    ("fp8_v_scale_on_keys", "const double mul = src == u->k ? u->k_mul : u->v_mul;",
+     "const double mul = src == u->k ? u->v_mul : u->v_mul;", 1),
     ("combine_equal_weights", "double w = exp(ls[(int64_t)s * nr + r] - big);", "double w = ls[(int64_t)s * nr + r] > -INFINITY ? 1.0 : 0.0;", 1),
     ("tile_max_includes_next_key", "j < (t + 1) * T && j < nk", "j <= (t + 1) * T && j < nk", 1),
     ("split_size_floor", "const int tps = (nt + P - 1) / P;", "const int tps = nt / P > 0 ? nt / P : 1;", 1),
