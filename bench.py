@@ -121,11 +121,12 @@ def prefill_flops(w, visited, kept):
     return dense, per_tile * (visited + kept)
 
 
-def decode_bytes(w, lens, state, P):
-    """Algorithmic HBM bytes of one decode call (see the design notes for the accounting)."""
+def decode_bytes(w, lens, state, P, kv_elem=2):
+    """Algorithmic HBM bytes of one decode call (see the design notes for the accounting); kv_elem: bytes per
+    cached K/V element (2 bf16, 1 fp8)."""
     import numpy as np
     d, Hkv, Hq, B = w.d, w.Hkv, w.Hq, w.B
-    k_bytes = float(lens.astype(np.int64).sum()) * Hkv * d * 2
+    k_bytes = float(lens.astype(np.int64).sum()) * Hkv * d * kv_elem
     nt = -(-lens // 64)
     kept_rows = 0
     for b in range(B):
@@ -133,8 +134,8 @@ def decode_bytes(w, lens, state, P):
         st = state[b * Hkv:(b + 1) * Hkv, :nt[b]]
         kept = st == 1
         kept_rows += int(kept[:, :-1].sum()) * 64 + int(kept[:, -1].sum()) * last_rows
-    v_kept = float(kept_rows) * d * 2
-    v_all = float(lens.astype(np.int64).sum()) * Hkv * d * 2
+    v_kept = float(kept_rows) * d * kv_elem
+    v_all = float(lens.astype(np.int64).sum()) * Hkv * d * kv_elem
     small = 2 * B * Hq * d * 2 + 2 * float(nt.sum()) * 4 + 2 * B * Hq * P * (d + 1) * 4
     return k_bytes, v_kept, v_all, small
 
@@ -175,6 +176,47 @@ def time_sink_seeded_decode(ssm, torch, np, w, data, dq, kp, vp, pt, lens, dout,
             "kv_gbps": round((kb + vk) / t / 1e9, 1), "total_gbps": round(tot / t / 1e9, 1),
             "hbm_frac": round(tot / t / 1e9 / HBM_PEAK_GBPS, 4), "per_launch_bytes": tot,
             "speedup_vs_split_local": None}
+
+
+def time_fp8_decode(ssm, torch, np, w, data, dq, kp, vp, pt, lens, dout, ws, dstate, tau, steps, dev):
+    """The decode over an fp8 e4m3 copy of the same paged cache (per-tensor scales amax/448, quantised on the
+    GPU before timing), same tau and splits, timed on its own after the step timing."""
+    def quant(pool):
+        amax = float(pool.abs().max().float())
+        scale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+        codes = torch.empty(pool.shape, dtype=torch.float8_e4m3fn, device=dev)
+        for i in range(0, pool.shape[0], 4096):
+            codes[i:i + 4096] = (pool[i:i + 4096].float() / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return codes, scale
+    k8, ks = quant(kp)
+    v8, vs = quant(vp)
+    cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+    run = lambda st: ssm.ssm_decode(dq, k8, v8, lens, tau=tau, out=dout, page_table=pt, num_splits=w.num_splits,
+                                    workspace=ws, skip_stats=st, k_scale=ks, v_scale=vs)
+    run(ssm.SkipStats(counters=cnt))
+    torch.cuda.synchronize()
+    cnt.zero_()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        run(ssm.SkipStats(counters=cnt))
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    dstate.zero_()
+    run(ssm.SkipStats(tile_state=dstate))
+    state = dstate.cpu().numpy()
+    c = cnt.cpu().numpy() / steps
+    if not (int((state != 0).sum()) == c[0] and int((state == 2).sum()) == c[1]):
+        raise RuntimeError("fp8 decode: tile states disagree with the timed counters")
+    kb, vk, va, small = decode_bytes(w, data["kv_lens"], state, w.num_splits, kv_elem=1)
+    t = ms / 1e3
+    del k8, v8
+    return {"ms": round(ms, 4), "tau": tau, "k_scale": ks, "v_scale": vs,
+            "sparsity": round(float(c[1]) / float(c[0]), 4), "kv_gbps": round((kb + vk) / t / 1e9, 1),
+            "total_gbps": round((kb + vk + small) / t / 1e9, 1),
+            "hbm_frac": round((kb + vk + small) / t / 1e9 / HBM_PEAK_GBPS, 4), "per_launch_bytes": kb + vk + small,
+            "speedup_vs_bf16": None}
 
 
 def cpu_baseline_prefill(w, data, threads, n_units=256):
@@ -378,6 +420,9 @@ def main():
         res["decode_sink_seeded"] = time_sink_seeded_decode(ssm, torch, np, dw, ddata, dq, kp, vp, pt, lens, dout, ws,
                                                             dstate, tau_d, args.steps, dev)
         res["decode_sink_seeded"]["speedup_vs_split_local"] = round(res["decode_ms"] / res["decode_sink_seeded"]["ms"], 3)
+        res["decode_fp8_kv"] = time_fp8_decode(ssm, torch, np, dw, ddata, dq, kp, vp, pt, lens, dout, ws, dstate, tau_d,
+                                               args.steps, dev)
+        res["decode_fp8_kv"]["speedup_vs_bf16"] = round(res["decode_ms"] / res["decode_fp8_kv"]["ms"], 3)
     res["config"] = cfg
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 enum {
   SSM_OK = 0,
@@ -46,11 +46,12 @@ enum {
   SSM_EHIP = 4           /* a HIP runtime call or kernel launch failed */
 };
 
-enum { SSM_BF16 = 0, SSM_FP32 = 1 };
+enum { SSM_BF16 = 0, SSM_FP32 = 1, SSM_FP8_E4M3 = 2 /* OCP 8-bit float, 4 exponent / 3 mantissa bits */ };
 
 /* Strided tensor view.  stride[] is in elements; the last dimension must be
  * contiguous (stride 1).  data must be 16-byte aligned and every other stride
- * a multiple of 8 elements, so rows can be moved in 16-byte pieces. */
+ * a multiple of 16 bytes (8 bf16 or 16 fp8 elements), so rows can be moved in
+ * 16-byte pieces. */
 typedef struct {
   void* data;
   int32_t dtype;    /* SSM_BF16 or SSM_FP32 */
@@ -65,12 +66,16 @@ typedef struct {
  *               int32 [B, max_pages] row-major array; logical key tile t of
  *               sequence b lives in page page_table[b*max_pages + t].  Only
  *               entries t < ceil(kv_len[b]/page_size) are read and they must be
- *               in [0, num_pages).  page_size must equal the key tile (64). */
+ *               in [0, num_pages).  page_size must equal the key tile (64).
+ *   pool.dtype: SSM_BF16, or SSM_FP8_E4M3 with `scale` the per-tensor
+ *               dequantisation factor (element value = scale * code; finite, > 0;
+ *               ignored for bf16).  K and V caches must share one dtype. */
 typedef struct {
   ssm_tensor pool;
   const int32_t* page_table;
   int32_t page_size;
   int32_t max_pages;
+  float scale;
 } ssm_kv_cache;
 
 /* Optional skip statistics (every member may be NULL / 0).
@@ -122,7 +127,8 @@ int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, i
                 float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream, const ssm_opts* opts);
 
 /* Single-token GQA decode with split-K and a log-sum-exp combine.
- *   q [B, Hq, d] bf16; out [B, Hq, d] bf16; kv_lens device int32 [B], each in [0, Smax or
+ *   q [B, Hq, d] bf16; out [B, Hq, d] bf16; K/V caches bf16 or fp8 e4m3 (see ssm_kv_cache: an fp8
+ *   cache is read at half the bytes and each code is converted exactly to bf16 for the MFMAs); kv_lens device int32 [B], each in [0, Smax or
  *   max_pages*page_size]; query b attends to keys j < kv_lens[b].  kv_len 0 gives 0.
  * The unit of the skip decision is one KV group (its Hq/Hkv query heads vote
  * together).  The unit's n = ceil(kv_len/64) key tiles are cut into num_splits

@@ -25,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
-SSM_BF16, SSM_FP32 = 0, 1
+SSM_BF16, SSM_FP32, SSM_FP8_E4M3 = 0, 1, 2
 EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_decode", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
                     "ssm_abi_version")
 
@@ -43,7 +43,7 @@ class Tensor(ctypes.Structure):
 
 class KvCache(ctypes.Structure):
     _fields_ = [("pool", Tensor), ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
-                ("max_pages", ctypes.c_int32)]
+                ("max_pages", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 class SkipStatsC(ctypes.Structure):
@@ -57,7 +57,7 @@ class Opts(ctypes.Structure):
                 ("decode_flags", ctypes.c_int32)]
 
 
-ABI_VERSION = 2               # the layout above matches SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 3               # the layout above matches SSM_ABI_VERSION of include/ssm.h
 DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
 
 
@@ -99,7 +99,7 @@ def describe(t: Optional[torch.Tensor]) -> Tensor:
     if t.dim() > 4:
         raise ValueError("at most 4 dimensions")
     d.data = t.data_ptr()
-    d.dtype = SSM_BF16 if t.dtype == torch.bfloat16 else (SSM_FP32 if t.dtype == torch.float32 else -1)
+    d.dtype = {torch.bfloat16: SSM_BF16, torch.float32: SSM_FP32, torch.float8_e4m3fn: SSM_FP8_E4M3}.get(t.dtype, -1)
     d.ndim = t.dim()
     for i in range(t.dim()):
         d.shape[i] = t.shape[i]
@@ -182,12 +182,14 @@ def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
                page_table: Optional[torch.Tensor] = None, v_page_table: Optional[torch.Tensor] = None,
                num_splits: int = 16, workspace: Optional[torch.Tensor] = None,
                skip_stats: Optional[SkipStats] = None, stream=None, scale: float = 0.0,
-               sink_seed: bool = False) -> torch.Tensor:
+               sink_seed: bool = False, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
     """Skip Softmax split-K decode.
 
     q [B,Hq,d] bf16; k_cache/v_cache contiguous [B,Hkv,Smax,d] (page_table None) or paged pools
     [pages,Hkv,64,d] with page_table int32 [B,max_pages]; kv_lens int32 [B] on the GPU.
-    sink_seed: splits after the first start their running maximum at the first key tile's row maxima."""
+    sink_seed: splits after the first start their running maximum at the first key tile's row maxima.
+    k_cache/v_cache may be torch.float8_e4m3fn tensors of codes; keys and values are then k_scale * code and
+    v_scale * code."""
     if out is None:
         out = torch.empty_like(q)
     B, Hq, d = q.shape
@@ -195,9 +197,10 @@ def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
         workspace = decode_workspace(B, Hq, d, num_splits, q.device)
     vpt = page_table if v_page_table is None else v_page_table
 
-    def cache(t, pt):
+    def cache(t, pt, sc):
         c = KvCache()
         c.pool = describe(t)
+        c.scale = float(sc)
         if pt is not None:
             if pt.dtype != torch.int32 or pt.dim() != 2 or not pt.is_contiguous():
                 raise ValueError("page_table must be a contiguous int32 [B, max_pages] tensor")
@@ -208,7 +211,7 @@ def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
 
     if kv_lens.dtype != torch.int32 or not kv_lens.is_contiguous():
         raise ValueError("kv_lens must be a contiguous int32 tensor")
-    kc, vc = cache(k_cache, page_table), cache(v_cache, vpt)
+    kc, vc = cache(k_cache, page_table, k_scale), cache(v_cache, vpt, v_scale)
     qd, od = describe(q), describe(out)
     opts = Opts(float(scale), 0, 64, int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                 DECODE_SINK_SEED if sink_seed else 0)

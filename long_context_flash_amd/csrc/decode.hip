@@ -29,6 +29,11 @@
 //   j of each loaded chunk, so its 16 output rows are channels 8m + j.
 //   V is loaded only after the vote keeps the tile.
 //
+// FP8 cache (optional): K and V stored as OCP e4m3 codes with one dequantisation
+// scale per tensor.  Half the bytes of a bf16 cache are read; each code is
+// converted exactly to bf16 in registers and the same bf16 MFMAs run.  The key
+// scale is folded into the logit scale, the value scale into the split output.
+//
 // Sink-seeded split-K (optional): a split after the first starts its prefix
 // maximum at key tile 0's per-query maxima instead of -inf; each wave scores
 // tile 0 once before its scan.  The combined output stays the exact softmax
@@ -43,30 +48,42 @@ constexpr int kDecWaves = 4;
 constexpr int kDecMaxG = 16;
 constexpr int kDecSortMax = 1024;  // batches up to this size are dispatched longest sequence first
 
-// Buffer resource over the valid rows of key tile t of (b, g): rows past kv_len, and every row of a
-// tile whose page id is outside the pool, read as zero.
-__device__ __forceinline__ rsrc_t decode_tile_rsrc(const uint16_t* pool, const int32_t* pages, int max_pages,
+// Buffer resource over the valid rows of key tile t of (b, g) in a pool of ES-byte elements: rows past
+// kv_len, and every row of a tile whose page id is outside the pool, read as zero.
+template <int ES>
+__device__ __forceinline__ rsrc_t decode_tile_rsrc(const void* pool, const int32_t* pages, int max_pages,
                                                    int64_t pool_pages, int64_t sb, int64_t sh, int64_t ss, int b,
                                                    int g, int t, int len, int d) {
   const int rows = min(kDecTK, len - t * kDecTK);
-  const uint16_t* base;
+  const uint8_t* p8 = static_cast<const uint8_t*>(pool);
+  int64_t elem;
   if (pages) {
     // the page id is wave-uniform: keep it (and the resource) in scalar registers
     const int pg = __builtin_amdgcn_readfirstlane(pages[(int64_t)b * max_pages + t]);
     if (pg < 0 || pg >= pool_pages) return make_rsrc(pool, 0u);
-    base = pool + (int64_t)pg * sb + (int64_t)g * sh;
+    elem = (int64_t)pg * sb + (int64_t)g * sh;
   } else {
-    base = pool + (int64_t)b * sb + (int64_t)g * sh + (int64_t)t * kDecTK * ss;
+    elem = (int64_t)b * sb + (int64_t)g * sh + (int64_t)t * kDecTK * ss;
   }
-  return make_rsrc(base, rows_bytes(rows, ss, d));
+  return make_rsrc(p8 + elem * ES, rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ss + d) * ES));
+}
+
+// Eight OCP fp8 e4m3 codes (bytes 0..7 of x) as eight bf16: exact, since every e4m3 value has at most
+// four significant bits and an exponent inside bf16's range (v_cvt_pk_f32_fp8, then a bf16 pack).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 x) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[0], false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[0], true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[1], false), e = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[1], true);
+  return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]), pack_bf16x2(e[0], e[1])};
 }
 
 // kv_cap: keys the cache can hold (contiguous Smax, paged max_pages*64);
 // pool_pages: number of pages in the pools (paged only).
-template <int D>
+// ES: bytes per K/V element (2: bf16 cache; 1: fp8 e4m3 cache, converted to bf16 in registers).
+template <int D, int ES>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int kv_cap, int64_t k_pool_pages,
                                                               int64_t v_pool_pages) {
   constexpr int KS = D / 32;            // k-steps of the QK^T MFMA
+  static_assert(ES == 1 || ES == 2, "bf16 or fp8 cache");
   __shared__ float mt[2][kDecWaves][kDecMaxG];  // per-chunk tile maxima (double-buffered by chunk parity)
   __shared__ float cm[kDecWaves][kDecMaxG];
   __shared__ float cl[kDecWaves][kDecMaxG];
@@ -143,9 +160,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   }
 
   // lane offsets inside a tile (bytes), fixed for the whole scan
-  uint32_t kvo[4];  // K: row kb*16 + qc, channels grp*8 + ks*32 (+ ks*64 bytes as an immediate)
+  uint32_t kvo[4];  // K: row kb*16 + qc, channels grp*8 + ks*32 (+ ks*32*ES bytes as an immediate)
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) kvo[kb] = (uint32_t)((kb * 16 + qc) * a.k_ss * 2 + grp * 16);
+  for (int kb = 0; kb < 4; ++kb) kvo[kb] = (uint32_t)(((kb * 16 + qc) * a.k_ss + grp * 8) * ES);
   // V: lane (m = qc, grp) loads keys st*32 + 16*(e/4) + 4*grp + (e%4), channels 8m .. 8m+7 (zero for 8m >= D)
   const bool v_ch_ok = qc * 8 < D;
   uint32_t vvo[2][2];
@@ -153,27 +170,40 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int eh = 0; eh < 2; ++eh)
-      vvo[st][eh] = v_ch_ok ? (uint32_t)((st * 32 + 16 * eh + 4 * grp) * a.v_ss * 2 + qc * 16) : 0xffffffffu;
-  const uint32_t vrow = (uint32_t)(a.v_ss * 2);
+      vvo[st][eh] = v_ch_ok ? (uint32_t)(((st * 32 + 16 * eh + 4 * grp) * a.v_ss + qc * 8) * ES) : 0xffffffffu;
+  const uint32_t vrow = (uint32_t)(a.v_ss * ES);
 
   const int nchunks = (s_end - s_begin + kDecWaves - 1) / kDecWaves;
-  u32x4 kreg[4][KS];  // A operand of the QK^T MFMAs: key block kb, k-step ks
+  // A operand of the QK^T MFMAs, key block kb, k-step ks: bf16 as loaded, or fp8 codes converted at use
+  u32x4 kreg[4][KS];
+  u32x2 kraw[4][KS];
   auto load_k = [&](int t) {
-    const rsrc_t r = decode_tile_rsrc(a.k, a.k_pages, a.k_max_pages, k_pool_pages, a.k_sb, a.k_sh, a.k_ss, b, g, t,
-                                      len, D);
+    const rsrc_t r = decode_tile_rsrc<ES>(a.k, a.k_pages, a.k_max_pages, k_pool_pages, a.k_sb, a.k_sh, a.k_ss, b, g,
+                                          t, len, D);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kreg[kb][ks] = buffer_load_16(r, kvo[kb] + ks * 64);
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (ES == 2) kreg[kb][ks] = buffer_load_16(r, kvo[kb] + ks * 64);
+        else kraw[kb][ks] = buffer_load_8(r, kvo[kb] + ks * 32);
+      }
   };
-  u32x4 vreg[2][8];
+  auto k_operand = [&](int kb, int ks) {
+    if constexpr (ES == 2) return as_bf16x8(kreg[kb][ks]);
+    else return as_bf16x8(fp8x8_to_bf16x8(kraw[kb][ks]));
+  };
+  u32x4 vreg[2][8];  // 8 key rows x 8 channels per st (bf16), converted from vraw for an fp8 cache
+  u32x2 vraw[2][8];
   auto load_v = [&](int t) {
-    const rsrc_t r = decode_tile_rsrc(a.v, a.v_pages, a.v_max_pages, v_pool_pages, a.v_sb, a.v_sh, a.v_ss, b, g, t,
-                                      len, D);
+    const rsrc_t r = decode_tile_rsrc<ES>(a.v, a.v_pages, a.v_max_pages, v_pool_pages, a.v_sb, a.v_sh, a.v_ss, b, g,
+                                          t, len, D);
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vreg[st][e] = buffer_load_16(r, vvo[st][e >> 2] + (e & 3) * vrow);
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (ES == 2) vreg[st][e] = buffer_load_16(r, vvo[st][e >> 2] + (e & 3) * vrow);
+        else vraw[st][e] = buffer_load_8(r, vvo[st][e >> 2] + (e & 3) * vrow);
+      }
   };
 
   f32x4 acc[8];  // acc[j][i] = O[query qc][channel 32*grp + 8*i + j]
@@ -190,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
       f32x4 x = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[kb][ks]), qreg[ks], x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kb, ks), qreg[ks], x, 0, 0, 0);
       s[kb] = x;
     }
     const int lim = qc < G ? len - 1 - t * kDecTK : -1;  // key offset o in the tile is valid iff o <= lim
@@ -223,6 +253,34 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   // treating the Q registers as pending inside it)
   wait_vmem_all();
 
+  // P.V of a kept tile runs one chunk later, when its V rows (loaded after the vote) have arrived
+  bf16x8 pend[2];        // that tile's P^T operands (keys st*32 .. st*32+31)
+  bool pending = false;  // wave-uniform
+  auto pv = [&]() {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // this st's 8 key rows as bf16 (an fp8 cache is converted here, one st at a time)
+      u32x4 vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (ES == 2) vr[e] = vreg[st][e];
+        else vr[e] = fp8x8_to_bf16x8(vraw[st][e]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // A_j: channel 8m + j of the 8 loaded key rows, packed two keys per dword
+        const int dw = j >> 1;
+        u32x4 av;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t x0 = vr[2 * u][dw], x1 = vr[2 * u + 1][dw];
+          av[u] = (j & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
+        }
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pend[st], acc[j], 0, 0, 0);
+      }
+    }
+  };
+
   for (int c = 0; c < nchunks; ++c) {
     const int t = s_begin + c * kDecWaves + w;
     const bool has = t < s_end;
@@ -253,11 +311,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
       }
       if (lane == 0 && a.tile_state) a.tile_state[srow + t] = keep ? 1 : 2;
     }
+    // the previous kept tile's V rows were loaded one chunk ago and arrived while this tile was scored
+    // and voted on; its P.V goes in before this tile can rescale the accumulators
+    if (pending) pv();
     if (keep) load_v(t);
     {
       const int tn = t + kDecWaves;
       if (c + 1 < nchunks && tn < s_end) load_k(tn);
     }
+    pending = keep;
     if (keep) {
       ++n_exec;
       const float m_new = fmaxf(m_run, mx);
@@ -280,22 +342,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
           pk[e >> 1] = pack_bf16x2(p0, p1);
           l_part = dot2_bf16_sum(pk[e >> 1], l_part);
         }
-        const bf16x8 pb = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          // A_j: channel 8m + j of the 8 loaded key rows, packed two keys per dword
-          const int dw = j >> 1;
-          u32x4 av;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t x0 = vreg[st][2 * u][dw], x1 = vreg[st][2 * u + 1][dw];
-            av[u] = (j & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
-          }
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pb, acc[j], 0, 0, 0);
-        }
+        pend[st] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
       }
     }
   }
+  if (pending) pv();
 
   // ---- combine the four waves' partial softmax states
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
@@ -327,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
       }
     }
     const bool ok = lsum > 0.f;
-    a.part_o[(part_row + (int64_t)q * P) * D + ch] = ok ? o / lsum : 0.f;
+    a.part_o[(part_row + (int64_t)q * P) * D + ch] = ok ? o / lsum * a.v_scale : 0.f;
     if (ch == 0) a.part_lse[part_row + (int64_t)q * P] = ok ? mstar * a.scale_log2 + __builtin_log2f(lsum) : neg_inf();
   }
   // skip counters: one set of atomics per workgroup
@@ -376,15 +427,19 @@ hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv * a.num_splits);
   const unsigned cgrid = (unsigned)((int64_t)a.B * a.Hq);
   if (grid == 0) return hipSuccess;
-  if (d == 128) {
-    hipLaunchKernelGGL((decode_split_kernel<128>), dim3(grid), dim3(256), 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);
-    hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(cgrid), dim3(128), 0, stream, a);
-  } else if (d == 64) {
-    hipLaunchKernelGGL((decode_split_kernel<64>), dim3(grid), dim3(256), 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);
-    hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(cgrid), dim3(64), 0, stream, a);
-  } else {
+  const dim3 blk(256);
+  if (d == 128 && !a.kv_fp8)
+    hipLaunchKernelGGL((decode_split_kernel<128, 2>), dim3(grid), blk, 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);
+  else if (d == 128)
+    hipLaunchKernelGGL((decode_split_kernel<128, 1>), dim3(grid), blk, 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);
+  else if (d == 64 && !a.kv_fp8)
+    hipLaunchKernelGGL((decode_split_kernel<64, 2>), dim3(grid), blk, 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);
+  else if (d == 64)
+    hipLaunchKernelGGL((decode_split_kernel<64, 1>), dim3(grid), blk, 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);
+  else
     return hipErrorInvalidValue;
-  }
+  if (d == 128) hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(cgrid), dim3(128), 0, stream, a);
+  else hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(cgrid), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -29,14 +29,17 @@ int check_tensor(const ssm_tensor* t, const char* name, int ndim, int dtype) {
   if (!t) return fail(SSM_EINVAL, "%s: NULL descriptor", name);
   if (!t->data) return fail(SSM_EINVAL, "%s: NULL data pointer", name);
   if (t->ndim != ndim) return fail(SSM_EINVAL, "%s: expected %d dims, got %d", name, ndim, (int)t->ndim);
-  if (t->dtype != dtype) return fail(SSM_EUNSUPPORTED, "%s: dtype %d not supported (bf16 required)", name, (int)t->dtype);
+  if (t->dtype != dtype)
+    return fail(SSM_EUNSUPPORTED, "%s: dtype %d not supported here (%s required)", name, (int)t->dtype,
+                dtype == SSM_BF16 ? "bf16" : "fp8 e4m3");
   for (int i = 0; i < ndim; ++i)
     if (t->shape[i] < 0) return fail(SSM_EINVAL, "%s: negative extent in dim %d", name, i);
   if (t->stride[ndim - 1] != 1) return fail(SSM_EINVAL, "%s: last dimension must be contiguous", name);
+  const int gran = dtype == SSM_FP8_E4M3 ? 16 : 8;  // elements per 16 bytes
   for (int i = 0; i < ndim - 1; ++i)
-    if (t->stride[i] < 0 || t->stride[i] % 8 != 0)
-      return fail(SSM_EUNSUPPORTED, "%s: stride[%d]=%lld must be a non-negative multiple of 8 elements", name, i,
-                  (long long)t->stride[i]);
+    if (t->stride[i] < 0 || t->stride[i] % gran != 0)
+      return fail(SSM_EUNSUPPORTED, "%s: stride[%d]=%lld must be a non-negative multiple of %d elements", name, i,
+                  (long long)t->stride[i], gran);
   if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0) return fail(SSM_EUNSUPPORTED, "%s: data must be 16-byte aligned", name);
   return SSM_OK;
 }
@@ -158,8 +161,11 @@ int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, i
 static int check_cache(const ssm_kv_cache* c, const char* name, int64_t B, int64_t d, int* kv_cap, int64_t* pool_rows,
                        int64_t* heads) {
   if (!c) return fail(SSM_EINVAL, "%s: NULL descriptor", name);
-  int rc = check_tensor(&c->pool, name, 4, SSM_BF16);
+  const int dt = c->pool.dtype == SSM_FP8_E4M3 ? SSM_FP8_E4M3 : SSM_BF16;
+  int rc = check_tensor(&c->pool, name, 4, dt);
   if (rc) return rc;
+  if (dt == SSM_FP8_E4M3 && !(c->scale > 0.f && std::isfinite(c->scale)))
+    return fail(SSM_EINVAL, "%s: an fp8 cache needs a finite scale > 0", name);
   if (c->pool.shape[3] != d) return fail(SSM_EINVAL, "%s: head_dim mismatch", name);
   *heads = c->pool.shape[1];
   if (c->page_table) {
@@ -195,6 +201,8 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
     return rc;
   if ((k_cache->page_table == nullptr) != (v_cache->page_table == nullptr))
     return fail(SSM_EINVAL, "k_cache and v_cache must both be paged or both contiguous");
+  if (k_cache->pool.dtype != v_cache->pool.dtype) return fail(SSM_EINVAL, "k_cache and v_cache dtypes differ");
+  const bool fp8 = k_cache->pool.dtype == SSM_FP8_E4M3;
   if (hk != hv) return fail(SSM_EINVAL, "k/v head counts differ");
   const int64_t Hkv = hk;
   if (Hkv <= 0 || Hq % Hkv != 0) return fail(SSM_EINVAL, "Hq (%lld) must be a positive multiple of Hkv (%lld)",
@@ -228,8 +236,8 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
   ssm::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
   a.q = static_cast<const uint16_t*>(q->data);
-  a.k = static_cast<const uint16_t*>(k_cache->pool.data);
-  a.v = static_cast<const uint16_t*>(v_cache->pool.data);
+  a.k = k_cache->pool.data;
+  a.v = v_cache->pool.data;
   a.kv_lens = kv_lens;
   a.k_pages = k_cache->page_table;
   a.v_pages = v_cache->page_table;
@@ -241,9 +249,13 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
   a.max_tiles = (int)max_tiles;
   a.num_splits = P;
   a.sink_seed = (flags & SSM_DECODE_SINK_SEED) ? 1 : 0;
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.tau_raw = std::isinf(tau) ? tau : tau / scale;
+  a.kv_fp8 = fp8 ? 1 : 0;
+  a.v_scale = fp8 ? v_cache->scale : 1.f;
+  // logits = scale * k_scale * (q . code): the key scale joins the softmax scale
+  const float lscale = fp8 ? scale * k_cache->scale : scale;
+  a.scale = lscale;
+  a.scale_log2 = lscale * 1.4426950408889634f;
+  a.tau_raw = std::isinf(tau) ? tau : tau / lscale;
   char* ws_base = static_cast<char*>(opts->workspace);
   const size_t rows = (size_t)B * Hq * P;
   a.part_o = reinterpret_cast<float*>(ws_base);

@@ -28,8 +28,8 @@ struct PrefillArgs {
 
 struct DecodeArgs {
   const uint16_t* q;         // [B, Hq, d]
-  const uint16_t* k;         // pool
-  const uint16_t* v;
+  const void* k;             // pool of bf16 or fp8 e4m3 elements (kv_fp8)
+  const void* v;
   const int32_t* kv_lens;    // [B]
   const int32_t* k_pages;    // nullable: paged
   const int32_t* v_pages;
@@ -43,7 +43,9 @@ struct DecodeArgs {
   int32_t max_tiles;         // row length of tile_state / unit_gap
   int32_t num_splits;
   int32_t sink_seed;         // 1: splits after the first start their running max at tile 0's row maxima
-  float scale, scale_log2, tau_raw;
+  int32_t kv_fp8;            // 1: K/V pools hold fp8 e4m3 codes; scale includes the key scale
+  float v_scale;             // value dequantisation scale (1 for bf16)
+  float scale, scale_log2, tau_raw;  // scale: logit scale per raw q.k product (softmax scale x key scale)
   float* part_o;             // workspace [B, Hq, P, d] fp32
   float* part_lse;           // workspace [B, Hq, P] fp32 (base-2 log-sum-exp of raw-scaled logits)
   uint16_t* o;               // [B, Hq, d]

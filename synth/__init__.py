@@ -230,6 +230,46 @@ def gen_decode(w: DecodeWorkload, *, kv_lens=None, contiguous=None, paged=None, 
     return out
 
 
+FP8_E4M3_MAX = 448.0  # largest finite OCP e4m3 value
+
+
+def _amax_bf16(bits: np.ndarray, chunk: int = 1 << 26) -> float:
+    flat = bits.reshape(-1)
+    m = 0.0
+    for i in range(0, flat.size, chunk):
+        m = max(m, float(np.abs(bf16_bits_to_f32(flat[i:i + chunk])).max(initial=0.0)))
+    return m
+
+
+def quantize_fp8_e4m3(bits: np.ndarray, scale: float, chunk: int = 1 << 26) -> np.ndarray:
+    """OCP fp8 e4m3 storage codes (uint8) of a bf16 tensor with one per-tensor scale: code = the e4m3 value
+    nearest to x / scale (ties to even, torch's float8_e4m3fn conversion), |x / scale| clamped to 448.
+    Storage preparation of an input (like the bf16 rounding above); no attention arithmetic."""
+    import torch
+    flat = bits.reshape(-1)
+    out = np.empty(flat.size, np.uint8)
+    for i in range(0, flat.size, chunk):
+        x = torch.from_numpy(bf16_bits_to_f32(flat[i:i + chunk]) / np.float32(scale))
+        out[i:i + chunk] = x.clamp_(-FP8_E4M3_MAX, FP8_E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return out.reshape(bits.shape)
+
+
+def fp8_kv(data: dict) -> dict:
+    """fp8 e4m3 copies of the K/V of a gen_decode() result with one scale per tensor (amax / 448, as float32):
+    k_scale / v_scale, and the codes of whichever of k_pool/v_pool and k_cache/v_cache exist (a pool and a
+    contiguous cache hold the same keys and share the scale)."""
+    out = {}
+    for name in ("k", "v"):
+        src = data.get(f"{name}_pool", data.get(f"{name}_cache"))
+        amax = _amax_bf16(src)
+        scale = float(np.float32(amax / FP8_E4M3_MAX)) if amax > 0 else 1.0
+        out[f"{name}_scale"] = scale
+        for kind in ("pool", "cache"):
+            if f"{name}_{kind}" in data:
+                out[f"{name}_{kind}"] = quantize_fp8_e4m3(data[f"{name}_{kind}"], scale)
+    return out
+
+
 def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     return (a.astype(np.uint32) << 16).view(np.float32)
@@ -242,6 +282,6 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return (x >> 16).astype(np.uint16)
 
 
-__all__ = ["PrefillWorkload", "DecodeWorkload", "WORKLOADS", "TINY_PREFILL", "DECODE_32K", "PREFILL_16K",
+__all__ = ["quantize_fp8_e4m3", "fp8_kv", "FP8_E4M3_MAX", "PrefillWorkload", "DecodeWorkload", "WORKLOADS", "TINY_PREFILL", "DECODE_32K", "PREFILL_16K",
            "PREFILL_128K", "DECODE_128K", "gen_prefill", "gen_decode", "kv_lens_for", "bf16_bits_to_f32",
            "f32_to_bf16_bits", "build", "default_threads", "replace"]

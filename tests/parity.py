@@ -119,23 +119,32 @@ def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, wh
     return {"max_abs": max_abs, "rel_l2": rel, "sparsity": sparsity, "state": st, "out": out}
 
 
-def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda", sink_seed=False):
+def fp8_device(codes, device):
+    """uint8 e4m3 codes -> torch.float8_e4m3fn tensor on ``device``."""
+    return torch.from_numpy(codes).to(device).view(torch.float8_e4m3fn)
+
+
+def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda", sink_seed=False, fp8=None):
+    """fp8: the synth.fp8_kv() copies of the K/V (the GPU then reads the codes with their scales)."""
     q = ssm.bf16_from_bits(data["q"], device)
     lens = torch.from_numpy(data["kv_lens"]).to(device)
     B, Hq, d = data["q"].shape
+    kind = "pool" if paged else "cache"
+    if fp8 is not None:
+        kc, vc = fp8_device(fp8[f"k_{kind}"], device), fp8_device(fp8[f"v_{kind}"], device)
+        scales = dict(k_scale=fp8["k_scale"], v_scale=fp8["v_scale"])
+    else:
+        kc, vc = ssm.bf16_from_bits(data[f"k_{kind}"], device), ssm.bf16_from_bits(data[f"v_{kind}"], device)
+        scales = {}
     if paged:
-        kc = ssm.bf16_from_bits(data["k_pool"], device)
-        vc = ssm.bf16_from_bits(data["v_pool"], device)
         pt = torch.from_numpy(data["page_table"]).to(device)
         Hkv, max_tiles = kc.shape[1], pt.shape[1]
     else:
-        kc = ssm.bf16_from_bits(data["k_cache"], device)
-        vc = ssm.bf16_from_bits(data["v_cache"], device)
         pt = None
         Hkv, max_tiles = kc.shape[1], -(-kc.shape[2] // 64)
     stats = ssm.SkipStats.alloc(B * Hkv, max_tiles, device, gaps=True)
     out = ssm.ssm_decode(q, kc, vc, lens, tau=tau, page_table=pt, num_splits=num_splits, skip_stats=stats,
-                         sink_seed=sink_seed)
+                         sink_seed=sink_seed, **scales)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
             stats.counters.cpu().numpy())
@@ -153,11 +162,15 @@ def contiguous_from_pages(pool, page_table, kv_lens, batches):
     return out
 
 
-def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", threads=None, sink_seed=False):
-    """GPU decode on the whole batch vs the oracle on the listed sequences (all when None)."""
+def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", threads=None, sink_seed=False,
+                 fp8=None):
+    """GPU decode on the whole batch vs the oracle on the listed sequences (all when None).  fp8: the
+    synth.fp8_kv() copies of the K/V; both sides then read the same codes and scales."""
     B, Hq, d = data["q"].shape
-    log(f"{where}: GPU decode B={B} Hq={Hq} d={d} tau={tau} P={num_splits} paged={paged} sink_seed={sink_seed}")
-    out, st, gap, cnt = run_decode_gpu(data, tau=tau, num_splits=num_splits, paged=paged, sink_seed=sink_seed)
+    log(f"{where}: GPU decode B={B} Hq={Hq} d={d} tau={tau} P={num_splits} paged={paged} sink_seed={sink_seed} "
+        f"fp8={fp8 is not None}")
+    out, st, gap, cnt = run_decode_gpu(data, tau=tau, num_splits=num_splits, paged=paged, sink_seed=sink_seed,
+                                       fp8=fp8)
     vis = int((st > 0).sum())
     skipped = int((st == 2).sum())
     assert list(cnt) == [vis, skipped, vis, vis - skipped], f"{where}: counters {list(cnt)} vs tile_state"
@@ -168,14 +181,16 @@ def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", 
     if batches is None:
         batches = np.arange(B)
     batches = np.asarray(batches)
+    src = fp8 if fp8 is not None else data
     if paged:
-        kc = contiguous_from_pages(data["k_pool"], data["page_table"], lens, batches)
-        vc = contiguous_from_pages(data["v_pool"], data["page_table"], lens, batches)
+        kc = contiguous_from_pages(src["k_pool"], data["page_table"], lens, batches)
+        vc = contiguous_from_pages(src["v_pool"], data["page_table"], lens, batches)
     else:
-        kc, vc = data["k_cache"][batches], data["v_cache"][batches]
+        kc, vc = src["k_cache"][batches], src["v_cache"][batches]
+    scales = dict(k_scale=fp8["k_scale"], v_scale=fp8["v_scale"]) if fp8 is not None else {}
     log(f"{where}: oracle on {len(batches)} sequences")
     ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits,
-                        sink_seed=sink_seed, threads=threads)
+                        sink_seed=sink_seed, threads=threads, **scales)
     mt = ref["state"].shape[1]
     rows = (batches[:, None] * Hkv + np.arange(Hkv)[None]).ravel()
     st_g = st[rows][:, :mt]
@@ -185,7 +200,7 @@ def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", 
     if flips.any():
         ov = np.where(flips, np.where(st_g == 2, 1, 0), -1).astype(np.int8)
         ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits,
-                            override=ov, sink_seed=sink_seed, threads=threads)
+                            override=ov, sink_seed=sink_seed, threads=threads, **scales)
     got = out[batches].reshape(ref["out"].shape)
     max_abs, rel = errors(got, ref["out"])
     sparsity = skipped / max(vis, 1)

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 2
+    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 3
     for code in range(5):
         assert ssm.ssm_strerror(code)
     assert "unknown" in ssm.ssm_strerror(99)
@@ -127,9 +127,10 @@ def test_prefill_stats_too_small(lib):
     assert rc == ssm.SSM_EINVAL and "tile_state" in ssm.ssm_last_error()
 
 
-def cache(shape, paged=False, max_pages=0):
+def cache(shape, paged=False, max_pages=0, dtype=ssm.SSM_BF16, scale=0.0, stride=None):
     c = ssm.KvCache()
-    c.pool = desc(shape)
+    c.pool = desc(shape, dtype=dtype, stride=stride)
+    c.scale = scale
     if paged:
         c.page_table = FAKE
         c.page_size = shape[2]
@@ -152,7 +153,9 @@ def call_decode(lib, q=None, kc=None, vc=None, lens=FAKE, tau=-6.9, o=None, opts
     ("no_workspace", ssm.SSM_EWORKSPACE), ("small_workspace", ssm.SSM_EWORKSPACE), ("null_lens", ssm.SSM_EINVAL),
     ("pos_tau", ssm.SSM_EINVAL), ("page_size", ssm.SSM_EUNSUPPORTED), ("mixed_paging", ssm.SSM_EINVAL),
     ("group_too_big", ssm.SSM_EUNSUPPORTED), ("splits", ssm.SSM_EUNSUPPORTED), ("batch", ssm.SSM_EINVAL),
-    ("head_dim", ssm.SSM_EUNSUPPORTED), ("unknown_flag", ssm.SSM_EINVAL),
+    ("head_dim", ssm.SSM_EUNSUPPORTED), ("unknown_flag", ssm.SSM_EINVAL), ("fp8_no_scale", ssm.SSM_EINVAL),
+    ("fp8_nan_scale", ssm.SSM_EINVAL), ("mixed_kv_dtypes", ssm.SSM_EINVAL), ("fp8_stride", ssm.SSM_EUNSUPPORTED),
+    ("fp32_cache", ssm.SSM_EUNSUPPORTED),
 ])
 def test_decode_rejects(lib, case, code):
     kw = {}
@@ -181,6 +184,19 @@ def test_decode_rejects(lib, case, code):
         kw["kc"], kw["vc"] = cache([2, 2, 1024, 80]), cache([2, 2, 1024, 80])
     elif case == "unknown_flag":
         kw["opts"] = ssm.Opts(0.0, 0, 0, 16, 256 * 1024, 1 << 30, 2)
+    elif case in ("fp8_no_scale", "fp8_nan_scale"):
+        sc = 0.0 if case == "fp8_no_scale" else math.nan
+        kw["kc"] = cache([2, 2, 1024, 128], dtype=ssm.SSM_FP8_E4M3, scale=sc)
+        kw["vc"] = cache([2, 2, 1024, 128], dtype=ssm.SSM_FP8_E4M3, scale=1.0)
+    elif case == "mixed_kv_dtypes":
+        kw["kc"] = cache([2, 2, 1024, 128], dtype=ssm.SSM_FP8_E4M3, scale=1.0)
+    elif case == "fp8_stride":
+        st = [2 * 1024 * 136, 1024 * 136, 136, 1]  # 136 fp8 elements: not a multiple of 16 bytes
+        kw["kc"] = cache([2, 2, 1024, 128], dtype=ssm.SSM_FP8_E4M3, scale=1.0, stride=st)
+        kw["vc"] = cache([2, 2, 1024, 128], dtype=ssm.SSM_FP8_E4M3, scale=1.0, stride=st)
+    elif case == "fp32_cache":
+        kw["kc"] = cache([2, 2, 1024, 128], dtype=ssm.SSM_FP32)
+        kw["vc"] = cache([2, 2, 1024, 128], dtype=ssm.SSM_FP32)
     rc = call_decode(lib, **kw)
     assert rc == code, (rc, ssm.ssm_last_error())
 
