@@ -36,7 +36,8 @@ def build(extra_flags=(), out_path=None) -> str:
 class _PrefillShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
-                ("causal", ctypes.c_int32), ("scale", ctypes.c_double), ("tau", ctypes.c_double)]
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_double), ("tau", ctypes.c_double),
+                ("S_k", ctypes.c_int32)]
 
 
 class _DecodeShape(ctypes.Structure):
@@ -91,16 +92,17 @@ def default_threads() -> int:
 
 def prefill(q, k, v, *, causal=True, tau=-math.log(1000.0), tile_q=128, tile_k=64, scale=0.0,
             units=None, override=None, form="closed", threads=None, lib=None) -> dict:
-    """Skip Softmax prefill on q [B,S,Hq,d], k/v [B,S,Hkv,d].
+    """Skip Softmax prefill on q [B,S,Hq,d], k/v [B,S_k,Hkv,d] with S_k >= S (S_k > S: chunked prefill, the
+    queries being the last S of the S_k positions; causal masking is then bottom-right aligned).
 
-    Returns dict: out [n,tile_q,d], lse [n,tile_q], state/gamma [n,ceil(S/tile_k)], dropped [n,tile_q],
+    Returns dict: out [n,tile_q,d], lse [n,tile_q], state/gamma [n,ceil(S_k/tile_k)], dropped [n,tile_q],
     for the listed units (unit = (b*Hq + h)*ceil(S/tile_q) + qt) or all units in that order."""
     q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
     B, S, Hq, d = q.shape
-    Hkv = k.shape[2]
-    if k.shape != (B, S, Hkv, d) or v.shape != k.shape:
-        raise ValueError("k/v must be [B,S,Hkv,d] matching q")
-    nqt, nkt = -(-S // tile_q), -(-S // tile_k)
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Sk, Hkv, d) or v.shape != k.shape or Sk < S:
+        raise ValueError("k/v must be [B,S_k,Hkv,d] with S_k >= S")
+    nqt, nkt = -(-S // tile_q), -(-Sk // tile_k)
     units_arr = None if units is None else np.ascontiguousarray(units, dtype=np.int64)
     n = B * Hq * nqt if units_arr is None else len(units_arr)
     ov = None
@@ -108,7 +110,7 @@ def prefill(q, k, v, *, causal=True, tau=-math.log(1000.0), tile_q=128, tile_k=6
         ov = np.ascontiguousarray(override, dtype=np.int8).reshape(n, nkt)
     res = {"out": np.empty((n, tile_q, d)), "lse": np.empty((n, tile_q)), "state": np.empty((n, nkt), np.uint8),
            "gamma": np.empty((n, nkt)), "dropped": np.empty((n, tile_q))}
-    shape = _PrefillShape(B, S, Hq, Hkv, d, tile_q, tile_k, int(bool(causal)), float(scale), float(tau))
+    shape = _PrefillShape(B, S, Hq, Hkv, d, tile_q, tile_k, int(bool(causal)), float(scale), float(tau), Sk)
     rc = (lib or load()).oracle_prefill(ctypes.byref(shape), _p(q), _p(k), _p(v), _dtype_code(q, k, v),
                                         _p(units_arr), n, _p(ov), 1 if form == "scan" else 0,
                                         _p(res["out"]), _p(res["lse"]), _p(res["state"]), _p(res["gamma"]),

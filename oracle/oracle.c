@@ -20,7 +20,9 @@
  *   1. Logits l_rj = scale * <q_r, k_j> for every visited (row, key) pair.
  *   2. Validity: causal prefill j <= i (top-left aligned, READING);
  *      non-causal j < S; decode j < kv_len (the new token is already in the
- *      cache, READING).
+ *      cache, READING).  Chunked prefill (S new queries against S_k >= S keys
+ *      whose last S positions are the queries' own): query i sees keys
+ *      j <= S_k - S + i (bottom-right aligned, READING), non-causal j < S_k.
  *   3. Units and scans: a prefill unit is (b, h, q-tile) with one ascending
  *      scan over its visited key tiles; a decode unit is (b, KV group) whose
  *      rows are the group's query heads, scanned as num_splits consecutive
@@ -383,7 +385,7 @@ static int valid_tau(double tau) { return !isnan(tau) && (tau == -INFINITY || ta
 typedef struct {
   const oracle_prefill_shape* s;
   const void *q, *k, *v;
-  int dt, form, nqt, nkt;
+  int dt, form, nqt, nkt, Sk;
   double scale;
   const int64_t* units;
   const int8_t* override;
@@ -398,23 +400,24 @@ static int prefill_one(void* vctx, int64_t n) {
   const int qt = (int)(uid % P->nqt), h = (int)((uid / P->nqt) % s->Hq), b = (int)(uid / P->nqt / s->Hq);
   const int G = s->Hq / s->Hkv, g = h / G, Tq = s->tile_q, d = s->d;
   const int i0 = qt * Tq, i1 = (qt + 1) * Tq < s->S ? (qt + 1) * Tq : s->S;
+  const int Sk = P->Sk, off = Sk - s->S;  /* keys per sequence; position of query 0 among them */
   double* q = (double*)malloc(sizeof(double) * (size_t)Tq * d);
   int64_t* limit = (int64_t*)malloc(sizeof(int64_t) * (size_t)Tq);
   if (!q || !limit) { free(q); free(limit); return 2; }
   for (int r = 0; r < Tq; ++r) {
     const int i = i0 + r;
-    limit[r] = i < s->S ? (s->causal ? i + 1 : s->S) : 0;
+    limit[r] = i < s->S ? (s->causal ? off + i + 1 : Sk) : 0;
     for (int c = 0; c < d; ++c)
       q[(int64_t)r * d + c] = i < s->S ? widen(P->q, P->dt, (((int64_t)b * s->S + i) * s->Hq + h) * d + c) : 0.0;
   }
   unit_t u;
   memset(&u, 0, sizeof u);
   u.nr = Tq; u.d = d; u.tile_k = s->tile_k;
-  u.ntiles = s->causal ? (i1 - 1) / s->tile_k + 1 : P->nkt;
-  u.nkeys = u.ntiles * s->tile_k < s->S ? u.ntiles * s->tile_k : s->S;
+  u.ntiles = s->causal ? (off + i1 - 1) / s->tile_k + 1 : P->nkt;
+  u.nkeys = u.ntiles * s->tile_k < Sk ? u.ntiles * s->tile_k : Sk;
   u.q = q; u.k = P->k; u.v = P->v; u.dt = P->dt;
   u.k_mul = 1.0; u.v_mul = 1.0;
-  u.kv_base = ((int64_t)b * s->S * s->Hkv + g) * d;
+  u.kv_base = ((int64_t)b * Sk * s->Hkv + g) * d;
   u.kv_stride = (int64_t)s->Hkv * d;
   u.limit = limit;
   int scan_first[2] = {0, u.ntiles};
@@ -444,13 +447,15 @@ int oracle_prefill(const oracle_prefill_shape* s, const void* q, const void* k, 
                    const int64_t* units, int64_t n_units, const int8_t* override, int form,
                    double* out, double* lse, uint8_t* state, double* gamma, double* dropped, int threads) {
   if (!s || !q || !k || !v || s->B < 1 || s->S < 1 || s->Hq < 1 || s->Hkv < 1 || s->d < 1 ||
-      s->Hq % s->Hkv || s->tile_q < 1 || s->tile_k < 1 || !valid_tau(s->tau) || in_dtype < 0 || in_dtype > 2)
+      s->Hq % s->Hkv || s->tile_q < 1 || s->tile_k < 1 || !valid_tau(s->tau) || in_dtype < 0 || in_dtype > 2 ||
+      (s->S_k != 0 && s->S_k < s->S))
     return 1;
   prefill_job P;
   memset(&P, 0, sizeof P);
   P.s = s; P.q = q; P.k = k; P.v = v; P.dt = in_dtype; P.form = form;
   P.nqt = (s->S + s->tile_q - 1) / s->tile_q;
-  P.nkt = (s->S + s->tile_k - 1) / s->tile_k;
+  P.Sk = s->S_k ? s->S_k : s->S;
+  P.nkt = (P.Sk + s->tile_k - 1) / s->tile_k;
   P.scale = s->scale > 0 ? s->scale : 1.0 / sqrt((double)s->d);
   const int64_t total = (int64_t)s->B * s->Hq * P.nqt;
   if (units) {

@@ -31,16 +31,19 @@ typedef struct {
   int32_t causal;             /* 1: query i sees keys j <= i; 0: all j < S */
   double scale;               /* <= 0 selects 1/sqrt(d) */
   double tau;                 /* -inf: never skip; otherwise must be <= 0 */
+  int32_t S_k;                /* chunked prefill: keys per sequence (k, v are [B,S_k,Hkv,d]); the S
+                                 queries are the last S of S_k positions, so query i sees keys
+                                 j <= S_k - S + i (bottom-right causal).  0 means S_k = S. */
 } oracle_prefill_shape;
 
 /* Prefill units are u = (b*Hq + h)*ceil(S/tile_q) + qt.  units == NULL means all
- * units in that order.  Per listed unit (index n):
+ * units in that order.  Per listed unit (index n), with nkt = ceil(S_k/tile_k):
  *   out      [n][tile_q][d]   rows past S are 0
  *   lse      [n][tile_q]      natural log; rows past S are -inf
- *   state    [n][ceil(S/tile_k)]   0 unvisited, 1 executed, 2 skipped
- *   gamma    [n][ceil(S/tile_k)]   unit gap; NaN when unvisited
+ *   state    [n][nkt]   0 unvisited, 1 executed, 2 skipped
+ *   gamma    [n][nkt]   unit gap; NaN when unvisited
  *   dropped  [n][tile_q]      mass of valid keys outside the kept set (closed form only; NaN in scan form)
- *   override [n][ceil(S/tile_k)]   -1 decide by the rule, 0 force keep, 1 force skip (may be NULL)
+ *   override [n][nkt]   -1 decide by the rule, 0 force keep, 1 force skip (may be NULL)
  * Any output may be NULL. */
 int oracle_prefill(const oracle_prefill_shape* s, const void* q, const void* k, const void* v, int in_dtype,
                    const int64_t* units, int64_t n_units, const int8_t* override, int form,

@@ -391,6 +391,73 @@ def pin_fp8_kv(lib=None):
     assert np.array_equal(r["out"][:, 0, 0], fp8_e4m3_codes_to_f64(finite)), "fp8 code values"
 
 
+def chunk_inputs(seed, B, S, Sk, Hq, Hkv, d, planted=2):
+    """Chunked-prefill inputs: q [B,S,Hq,d] are the queries of the last S of Sk positions; k/v [B,Sk,Hkv,d]."""
+    q, k, v = prefill_inputs(seed, B, Sk, Hq, Hkv, d, planted=planted)
+    return np.ascontiguousarray(q[:, Sk - S:]), k, v
+
+
+def bottom_right_mask(B, Hq, S, Sk, causal):
+    m = np.ones((B, Hq, S, Sk), bool)
+    if causal:
+        off = Sk - S
+        m &= np.arange(Sk)[None, :] <= (off + np.arange(S))[:, None]
+    return m
+
+
+def pin_chunked_prefill(lib=None):
+    """Chunked prefill (S queries = the last S of Sk positions, bottom-right causal).  At tau = -inf it is SDPA
+    with the bottom-right mask; when the chunk starts on a query-tile boundary its units are exactly units of the
+    full prefill over all Sk positions (same rows, same key tiles), so masks and outputs must be identical."""
+    for seed, (S, Sk, Hq, Hkv, d, causal, Tq) in enumerate([(64, 200, 4, 2, 32, True, 64), (77, 301, 4, 1, 64, True, 64),
+                                                           (130, 130, 2, 1, 16, True, 128), (5, 9, 2, 1, 2, True, 64),
+                                                           (100, 250, 4, 2, 32, False, 128), (1, 190, 4, 4, 64, True, 128)]):
+        q, k, v = chunk_inputs(90 + seed, 1, S, Sk, Hq, Hkv, d)
+        r = oracle.prefill(q, k, v, causal=causal, tau=-math.inf, tile_q=Tq, tile_k=64, lib=lib)
+        ref = sdpa_prefill(q, k, v, False, key_mask=bottom_right_mask(1, Hq, S, Sk, causal))
+        got = unit_rows(r["out"], 1, S, Hq, Tq)
+        assert np.abs(got - ref).max() < 1e-12, f"chunk S={S} Sk={Sk} causal={causal} vs SDPA"
+        nkt = -(-Sk // 64)
+        nqt = -(-S // Tq)
+        last = (Sk - S + np.minimum(S, (np.arange(nqt) + 1) * Tq) - 1) // 64 if causal else np.full(nqt, nkt - 1)
+        for h in range(Hq):
+            for qt in range(nqt):
+                st = r["state"][h * nqt + qt]
+                assert (st[:last[qt] + 1] == oracle.EXECUTED).all() and (st[last[qt] + 1:] == 0).all(), "visited tiles"
+    for Tq in (64, 128):
+        S, Sk = 3 * Tq, 3 * Tq + 2 * Tq
+        q, k, v = chunk_inputs(97, 1, S, Sk, 4, 2, 64, planted=3)
+        qfull, _, _ = chunk_inputs(97, 1, Sk, Sk, 4, 2, 64, planted=3)
+        for tau in (-LN1000, -2.0):
+            a = oracle.prefill(q, k, v, causal=True, tau=tau, tile_q=Tq, tile_k=64, lib=lib)
+            f = oracle.prefill(qfull, k, v, causal=True, tau=tau, tile_q=Tq, tile_k=64, lib=lib)
+            nq, nf = S // Tq, Sk // Tq
+            units_f = np.array([h * nf + (Sk - S) // Tq + qt for h in range(4) for qt in range(nq)])
+            assert np.array_equal(a["state"], f["state"][units_f]), f"aligned chunk mask Tq={Tq} tau={tau}"
+            assert np.abs(a["out"] - f["out"][units_f]).max() < 1e-12
+            assert (a["state"] == oracle.SKIPPED).any(), "the planted input must skip something"
+
+
+def pin_worked_example_chunk(lib=None):
+    """W7: W1's keys (tile 0 logit 0, tile 1 logit -10; v = (j, 1) then (1000, -1)) with the queries at positions
+    64..127 only (S = 64, Sk = 128, causal, bottom-right).  Query i sees keys 0..64+i, so tile 1 is visited
+    (partially) by every row and trails by 10: skipped at tau = -ln 1000 (every row gets (31.5, 1)); at tau = -inf
+    row i gets (2016 + 1000 (i+1) e^-10, 64 - (i+1) e^-10) / (64 + (i+1) e^-10)."""
+    q1, k1, v1 = _w1_inputs()
+    q = np.ascontiguousarray(q1[:, 64:])
+    e = math.exp(-10.0)
+    for tau, skipped in ((-LN1000, True), (-math.inf, False)):
+        r = oracle.prefill(q, k1, v1, causal=True, tau=tau, tile_q=64, tile_k=64, scale=1.0, lib=lib)
+        assert list(r["state"][0]) == [1, 2 if skipped else 1], f"W7 mask tau={tau}"
+        i = np.arange(64)
+        if skipped:
+            want = np.stack([np.full(64, 31.5), np.ones(64)], 1)
+        else:
+            n = i + 1
+            want = np.stack([(2016 + 1000 * n * e) / (64 + n * e), (64 - n * e) / (64 + n * e)], 1)
+        assert np.abs(r["out"][0] - want).max() < 1e-12, f"W7 output tau={tau}"
+
+
 # ----------------------------------------------------------------- worked examples
 def _w1_inputs():
     """d=2, S=128, q_i=(1,0); tile-0 keys (0,0) -> logit 0; tile-1 keys (-10,0) -> logit -10 (scale 1).
@@ -508,7 +575,7 @@ def pin_worked_example_sink_seed(lib=None):
 
 ALL_PINS = [pin_dense_prefill, pin_dense_decode, pin_longdouble_bruteforce, pin_forms_agree, pin_mask_invariants,
             pin_uniform_scores, pin_dropped_mass, pin_split_invariance, pin_output_given_mask, pin_worked_examples,
-            pin_sink_seed, pin_worked_example_sink_seed, pin_fp8_kv]
+            pin_sink_seed, pin_worked_example_sink_seed, pin_fp8_kv, pin_chunked_prefill, pin_worked_example_chunk]
 
 
 def run_all(lib=None):

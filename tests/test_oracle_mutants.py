@@ -23,7 +23,7 @@ MUTANTS = [
     ("skip_comparison_not_strict", "unit_gap < u->tau", "unit_gap <= u->tau", 1),
     ("unit_gap_min_over_rows", "if (g > G) G = g;", "if (voters == 1 || g < G) G = g;", 2),
     ("first_tile_gap_not_infinite", "return INFINITY;  /* first tile", "return tile_max;  /* first tile", 1),
-    ("causal_off_by_one", "(s->causal ? i + 1 : s->S)", "(s->causal ? i : s->S)", 1),
+    ("causal_off_by_one", "(s->causal ? off + i + 1 : Sk)", "(s->causal ? off + i : Sk)", 1),
     ("gqa_head_map_modulo", "g = h / G,", "g = h % s->Hkv,", 1),
     ("scale_1_over_d", "1.0 / sqrt((double)s->d)", "1.0 / (double)s->d", 2),
     ("values_read_from_keys", "load_row(u, u->v, j, row);", "load_row(u, u->k, j, row);", 2),
@@ -39,6 +39,12 @@ MUTANTS = [
     ("fp8_exponent_bias_8", "ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)", 1),
     ("fp8_subnormals_as_normals", "e == 0 ? ldexp((double)m, -9) :", "e < 0 ? ldexp((double)m, -9) :", 1),
     ("fp8_k_scale_dropped", "u.k_mul = s->k_scale > 0 ? s->k_scale : 1.0;", "u.k_mul = 1.0;", 1),
+    ("chunk_top_left_causal", "limit[r] = i < s->S ? (s->causal ? off + i + 1 : Sk) : 0;",
+     "limit[r] = i < s->S ? (s->causal ? i + 1 : Sk) : 0;", 1),
+    ("chunk_offset_off_by_one", "limit[r] = i < s->S ? (s->causal ? off + i + 1 : Sk) : 0;",
+     "limit[r] = i < s->S ? (s->causal ? off + i + 2 : Sk) : 0;", 1),
+    ("chunk_tiles_without_offset", "u.ntiles = s->causal ? (off + i1 - 1) / s->tile_k + 1 : P->nkt;",
+     "u.ntiles = s->causal ? (i1 - 1) / s->tile_k + 1 : P->nkt;", 1),
     ("fp8_v_scale_on_keys", "const double mul = src == u->k ? u->k_mul : u->v_mul;",
      "const double mul = src == u->k ? u->v_mul : u->v_mul;", 1),
     ("combine_equal_weights", "double w = exp(ls[(int64_t)s * nr + r] - big);", "double w = ls[(int64_t)s * nr + r] > -INFINITY ? 1.0 : 0.0;", 1),
