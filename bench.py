@@ -36,6 +36,10 @@ CSRC = os.path.join(ROOT, "long_context_flash_amd", "csrc")
 KERNEL_SOURCES = {"prefill": ["prefill.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"],
                   "decode": ["decode.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"]}
 COPY_PROBE_BYTES = 1 << 30
+# the step's kernels as the profiler names them (d = 128, tile_q = 128, plain prefill, bf16 cache)
+PREFILL_KERNEL = "prefill_kernel<128, 128, false>"
+DECODE_SPLIT_KERNEL = "decode_split_kernel<128, 2>"
+DECODE_COMBINE_KERNEL = "decode_combine_kernel<128>"
 
 
 def sources_sha(path_kind):
@@ -86,10 +90,11 @@ def summarize_traffic(fetch_dir, write_dir, command):
         return tot
 
     rec = {"copy_kernel": copy, "fetch_factor": f_fac, "write_factor": w_fac, "command": command,
-           "prefill": {"kernels": "prefill_kernel", "bytes_per_launch": launch_bytes(lambda n: "prefill_kernel" in n),
+           "prefill": {"kernels": PREFILL_KERNEL,
+                       "bytes_per_launch": launch_bytes(lambda n: PREFILL_KERNEL in n),
                        "source_sha256": sources_sha("prefill")},
            "decode": {"kernels": "decode_split_kernel + decode_combine_kernel",
-                      "bytes_per_launch": launch_bytes(lambda n: "decode_split" in n or "decode_combine" in n),
+                      "bytes_per_launch": launch_bytes(lambda n: DECODE_SPLIT_KERNEL in n or DECODE_COMBINE_KERNEL in n),
                       "source_sha256": sources_sha("decode")}}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
@@ -219,6 +224,57 @@ def time_fp8_decode(ssm, torch, np, w, data, dq, kp, vp, pt, lens, dout, ws, dst
             "speedup_vs_bf16": None}
 
 
+CHUNK_Q = 8192  # the chunked-prefill leg: the last 8192 queries of the 128K input against all of its keys
+
+
+def time_chunked_prefill(ssm, torch, np, w, data, tau, steps, dev):
+    """Chunked prefill against a paged cache (NEXT row): the last CHUNK_Q queries of the 128K prefill input
+    attend to all S keys held in a 64-token-page pool at a seeded random page order; timed on its own after
+    the steps with HIP events, skip counters in the timed calls."""
+    S, nq = w.S, CHUNK_Q
+    npages = -(-S // 64)
+    perm = np.random.default_rng(w.seed).permutation(npages).astype(np.int32)
+    k = torch.from_numpy(data["k"][0].view(np.int16)).view(torch.bfloat16)      # [S, Hkv, d] host
+    v = torch.from_numpy(data["v"][0].view(np.int16)).view(torch.bfloat16)
+    pool_k = torch.empty(npages, w.Hkv, 64, w.d, dtype=torch.bfloat16, device=dev)
+    pool_v = torch.empty_like(pool_k)
+    kd = k.to(dev).view(npages, 64, w.Hkv, w.d).transpose(1, 2)
+    vd = v.to(dev).view(npages, 64, w.Hkv, w.d).transpose(1, 2)
+    idx = torch.from_numpy(perm.astype(np.int64)).to(dev)
+    pool_k[idx] = kd
+    pool_v[idx] = vd
+    del kd, vd
+    pt = torch.from_numpy(perm[None, :]).to(dev)
+    q = torch.from_numpy(data["q"][0, S - nq:].view(np.int16)).view(torch.bfloat16).to(dev)   # [nq, Hq, d]
+    qs = torch.tensor([0, nq], dtype=torch.int32, device=dev)
+    kl = torch.tensor([S], dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+    run = lambda: ssm.ssm_prefill_paged(q, pool_k, pool_v, pt, qs, kl, nq, causal=True, tau=tau, out=out,
+                                        skip_stats=ssm.SkipStats(counters=cnt), tile_q=w.tile_q)
+    run()
+    torch.cuda.synchronize()
+    cnt.zero_()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    c = cnt.cpu().numpy() / steps
+    visited, skipped = float(c[0]), float(c[1])
+    off = S - nq
+    dense = 4.0 * w.Hq * w.d * (nq * off + nq * (nq + 1) / 2)  # query i sees off + i + 1 keys
+    executed = 2.0 * w.tile_q * w.tile_k * w.d * (2 * visited - skipped)
+    t = ms / 1e3
+    del pool_k, pool_v, q, out
+    return {"workload": f"chunk q{nq} of kv{S} (paged, 64-token pages)", "ms": round(ms, 3),
+            "dense_tflops": round(dense / t / 1e12, 2), "executed_tflops": round(executed / t / 1e12, 2),
+            "mfma_frac": round(executed / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "sparsity": round(skipped / visited, 4),
+            "tau": tau}
+
+
 def cpu_baseline_prefill(w, data, threads, n_units=256):
     """Time the fp64 oracle on a bounded sample of prefill units; dense-equivalent TFLOP/s."""
     import numpy as np
@@ -277,6 +333,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the step (prefill + decode); skip the chunked-prefill, sink-seeded and fp8 legs "
+                         "(used for the profiler runs, so each kernel name is one configuration)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 1 GiB device buffer (normalises FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -385,9 +444,11 @@ def main():
                           "relevant_tile_frac": pw.rel_frac, "seed": pw.seed}
         res["roofline"] = {"bound": "mfma", "achieved": round(executed / t / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(executed / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                           "traffic": recorded_traffic("prefill"), "kernel": "prefill_kernel<128,128>",
+                           "traffic": recorded_traffic("prefill"), "kernel": PREFILL_KERNEL,
                            "per_launch_flop": executed, "note": "executed = 2*128*64*128 FLOP per visited "
                            "tile (QK^T) + the same per kept tile (PV)"}
+    if run_prefill and not args.main_only:
+        res["prefill_chunked_paged"] = time_chunked_prefill(ssm, torch, np, pw, pdata, tau_p, args.steps, dev)
     if run_decode:
         c = dcnt.cpu().numpy() / args.steps
         ssm.ssm_decode(dq, kp, vp, lens, tau=tau_d, out=dout, page_table=pt, num_splits=dw.num_splits,
@@ -412,11 +473,12 @@ def main():
                                   "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                   "frac": round((kb + vk + small) / t / 1e9 / HBM_PEAK_GBPS, 4),
                                   "traffic": recorded_traffic("decode"),
-                                  "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                                  "kernel": f"{DECODE_SPLIT_KERNEL} + {DECODE_COMBINE_KERNEL}",
                                   "per_launch_bytes": kb + vk + small}
         if "value" not in res:
             res["value"] = res["decode_kv_gbps"]
             res["unit"] = "GB/s"
+    if run_decode and not args.main_only:
         res["decode_sink_seeded"] = time_sink_seeded_decode(ssm, torch, np, dw, ddata, dq, kp, vp, pt, lens, dout, ws,
                                                             dstate, tau_d, args.steps, dev)
         res["decode_sink_seeded"]["speedup_vs_split_local"] = round(res["decode_ms"] / res["decode_sink_seeded"]["ms"], 3)

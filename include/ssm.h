@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 enum {
   SSM_OK = 0,
@@ -139,6 +139,25 @@ int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, i
 int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
                const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
                const ssm_opts* opts);
+
+/* Chunked prefill against a paged KV cache (a serving context phase: new tokens attend to the cached
+ * context and to each other).  A ragged batch of `batch` sequences:
+ *   q, out [total_q, Hq, d] bf16: sequence b's n_b = q_start[b+1] - q_start[b] query rows are rows
+ *     q_start[b] .. q_start[b+1]-1 (q_start: device int32 [batch+1], 0 <= n_b <= max_q_len);
+ *   k_cache, v_cache: paged bf16 pools [pages, Hkv, 64, d] with page tables of equal length (see
+ *     ssm_kv_cache); sequence b has kv_lens[b] (device int32 [batch]) keys, the last n_b of which are its
+ *     new tokens (already written to the cache): query i of sequence b sits at key position
+ *     kv_lens[b] - n_b + i and, with causal != 0, attends to keys j <= that position (bottom-right
+ *     aligned); otherwise to all kv_lens[b] keys.
+ * The unit of the skip decision is one query tile (tile_q rows) of one head of one sequence; its
+ * statistics row is unit (b*Hq + h)*ceil(max_q_len/tile_q) + q_tile with max_pages key tiles.  A
+ * sequence whose offsets are malformed (n_b < 0, n_b > max_q_len, rows past total_q) is not touched;
+ * one with kv_lens[b] < n_b or more keys than its page table holds gets zero outputs.  With
+ * kv_lens[b] = n_b this is ssm_prefill on one sequence. */
+int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+                      const int32_t* q_start, const int32_t* kv_lens, int32_t batch, int32_t max_q_len,
+                      int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+                      const ssm_opts* opts);
 
 /* Bytes of device workspace ssm_decode needs (fp32 partial outputs and
  * log-sum-exps per (b, query head, split)).  0 for invalid arguments. */

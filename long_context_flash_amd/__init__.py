@@ -26,8 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 SSM_BF16, SSM_FP32, SSM_FP8_E4M3 = 0, 1, 2
-EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_decode", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
-                    "ssm_abi_version")
+EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror",
+                    "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -57,7 +57,7 @@ class Opts(ctypes.Structure):
                 ("decode_flags", ctypes.c_int32)]
 
 
-ABI_VERSION = 3               # the layout above matches SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 4               # the layout above matches SSM_ABI_VERSION of include/ssm.h
 DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
 
 
@@ -79,6 +79,10 @@ def lib():
     L.ssm_decode.restype = ctypes.c_int
     L.ssm_decode.argtypes = [P(Tensor), P(KvCache), P(KvCache), ctypes.c_void_p, ctypes.c_float, P(Tensor),
                              P(SkipStatsC), ctypes.c_void_p, P(Opts)]
+    L.ssm_prefill_paged.restype = ctypes.c_int
+    L.ssm_prefill_paged.argtypes = [P(Tensor), P(KvCache), P(KvCache), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P(Tensor), P(SkipStatsC),
+                                    ctypes.c_void_p, P(Opts)]
     L.ssm_decode_workspace_bytes.restype = ctypes.c_size_t
     L.ssm_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 4
     L.ssm_strerror.restype = ctypes.c_char_p
@@ -168,6 +172,47 @@ def ssm_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     return out
 
 
+def _paged_cache(t: torch.Tensor, pt: torch.Tensor, scale: float = 1.0) -> KvCache:
+    c = KvCache()
+    c.pool = describe(t)
+    c.scale = float(scale)
+    if pt.dtype != torch.int32 or pt.dim() != 2 or not pt.is_contiguous():
+        raise ValueError("page_table must be a contiguous int32 [B, max_pages] tensor")
+    c.page_table = pt.data_ptr()
+    c.page_size = t.shape[2]
+    c.max_pages = pt.shape[1]
+    return c
+
+
+def ssm_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
+                      q_start: torch.Tensor, kv_lens: torch.Tensor, max_q_len: int, causal: bool = True,
+                      tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
+                      skip_stats: Optional[SkipStats] = None, stream=None, tile_q: int = 128, scale: float = 0.0,
+                      v_page_table: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunked prefill against a paged cache: q/out [total_q,Hq,d] bf16 (sequence b's rows q_start[b] ..
+    q_start[b+1]-1, the last of its kv_lens[b] cached keys); k_cache/v_cache [pages,Hkv,64,d] bf16 with
+    page_table int32 [B,max_pages]; q_start int32 [B+1] and kv_lens int32 [B] on the GPU."""
+    if out is None:
+        out = torch.empty_like(q)
+    for name, t in (("q_start", q_start), ("kv_lens", kv_lens)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    B = kv_lens.shape[0]
+    if q_start.shape[0] != B + 1:
+        raise ValueError("q_start must have batch + 1 entries")
+    kc = _paged_cache(k_cache, page_table)
+    vc = _paged_cache(v_cache, page_table if v_page_table is None else v_page_table)
+    qd, od = describe(q), describe(out)
+    opts = Opts(float(scale), int(tile_q), 64, 0, None, 0, 0)
+    st = skip_stats.c() if skip_stats is not None else None
+    rc = lib().ssm_prefill_paged(ctypes.byref(qd), ctypes.byref(kc), ctypes.byref(vc), q_start.data_ptr(),
+                                 kv_lens.data_ptr(), int(B), int(max_q_len), int(bool(causal)), float(tau),
+                                 ctypes.byref(od), ctypes.byref(st) if st else None, _stream_handle(stream),
+                                 ctypes.byref(opts))
+    _check(rc)
+    return out
+
+
 def ssm_decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:
     return int(lib().ssm_decode_workspace_bytes(B, Hq, d, num_splits))
 
@@ -241,6 +286,6 @@ def bf16_from_bits(a, device=None) -> torch.Tensor:
     return t.to(device) if device is not None else t
 
 
-__all__ = ["ssm_prefill", "ssm_decode", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
+__all__ = ["ssm_prefill", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
            "ssm_abi_version", "SkipStats", "SsmError", "prefill_stats_shape", "decode_workspace", "bf16_from_bits",
            "lib", "describe", "LIB_PATH", "EXPORTED_SYMBOLS"]

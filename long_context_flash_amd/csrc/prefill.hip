@@ -72,7 +72,9 @@ __device__ __forceinline__ void map_prefill_unit(int bid, const PrefillArgs& a, 
   qt = a.nqt - 1 - level;  // longest causal units first
 }
 
-template <int D, int TQ>
+// CHUNKED: queries of each sequence are the last ones of its cached keys (bottom-right causal), packed
+// ragged rows of q/o, K/V read through a page table (see PrefillArgs).
+template <int D, int TQ, bool CHUNKED>
 __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = TQ / 32;             // waves per workgroup
   constexpr int NT = NW * 64;             // threads
@@ -96,20 +98,47 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   int b, h, qt;
   map_prefill_unit(blockIdx.x, a, b, h, qt);
   const int g = h / a.G;
-  const int S = a.S;
-  const int q0 = qt * TQ;
-  const int q_end = min(S, q0 + TQ);
-  const int T = (a.causal ? (q_end - 1) / kTK : a.nkt - 1) + 1;  // visited key tiles
-  // tiles [0, T_in) have every (row, key) pair valid: no masking code runs for them
-  const int full_tiles = S / kTK;
-  const int T_in = q_end < q0 + TQ ? 0 : min(T, a.causal ? min(q0 / kTK, full_tiles) : full_tiles);
   const int64_t unit = ((int64_t)b * a.Hq + h) * a.nqt + qt;
+  const int q0 = qt * TQ;
+  // S queries against Sk keys; query i sits at key position off + i; q/o rows start at qrow0
+  int S = a.S, Sk = a.S, off = 0, qrow0 = 0;
+  bool keys_ok = true;
+  if constexpr (CHUNKED) {
+    qrow0 = __builtin_amdgcn_readfirstlane(a.q_start[b]);
+    S = __builtin_amdgcn_readfirstlane(a.q_start[b + 1]) - qrow0;
+    Sk = __builtin_amdgcn_readfirstlane(a.kv_lens[b]);
+    if (qrow0 < 0 || S < 0 || S > a.S || qrow0 + S > a.total_q) S = 0;  // malformed offsets: no rows touched
+    keys_ok = Sk >= S && Sk <= a.max_pages * kTK;                // otherwise its rows are written as zeros
+    off = Sk - S;
+    if (q0 >= S) {  // a query tile past this sequence's queries: only its statistics row is written
+      if (tid == 0)
+        for (int t = 0; t < a.nkt; ++t) {
+          if (a.tile_state) a.tile_state[unit * a.nkt + t] = 0;
+          if (a.unit_gap) a.unit_gap[unit * a.nkt + t] = __builtin_nanf("");
+        }
+      return;
+    }
+  }
+  const int q_end = min(S, q0 + TQ);
+  const int T = !keys_ok ? 0 : (a.causal ? (q_end - 1 + off) / kTK + 1 : (Sk + kTK - 1) / kTK);  // visited key tiles
+  // tiles [0, T_in) have every (row, key) pair valid: no masking code runs for them
+  const int full_tiles = Sk / kTK;
+  const int T_in = q_end < q0 + TQ ? 0 : min(T, a.causal ? min((q0 + off + 1) / kTK, full_tiles) : full_tiles);
   const float c2 = a.scale_log2;
 
-  // ---- buffer resources: one (b, head) slice each; bytes past the last row read as zero
-  const rsrc_t rq = make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D));
-  const rsrc_t rk = make_rsrc(a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh, rows_bytes(S, a.k_ss, D));
-  const rsrc_t rv = make_rsrc(a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh, rows_bytes(S, a.v_ss, D));
+  // ---- buffer resources: one (b, head) slice each (chunked: K/V per tile, below); bytes past the last row
+  // read as zero
+  const rsrc_t rq = CHUNKED ? make_rsrc(a.q + (int64_t)qrow0 * a.q_ss + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D))
+                            : make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D));
+  const rsrc_t rk = make_rsrc(a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh, CHUNKED ? 0u : rows_bytes(S, a.k_ss, D));
+  const rsrc_t rv = make_rsrc(a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh, CHUNKED ? 0u : rows_bytes(S, a.v_ss, D));
+  // chunked: the resource of key tile t of this KV head (rows past Sk and bad page ids read as zero)
+  auto page_rsrc = [&](const uint16_t* pool, const int32_t* pages, int64_t pool_pages, int64_t sb, int64_t sh,
+                       int64_t ss, int t) {
+    const int pg = __builtin_amdgcn_readfirstlane(pages[(int64_t)b * a.max_pages + t]);
+    if (pg < 0 || pg >= pool_pages) return make_rsrc(pool, 0u);
+    return make_rsrc(pool + (int64_t)pg * sb + (int64_t)g * sh, rows_bytes(min(kTK, Sk - t * kTK), ss, D));
+  };
 
   // ---- Q operand: lane (col, half) holds Q[row][ks*16 + half*8 .. +8] for every k-step
   const int iq = q0 + w * 32 + col;
@@ -137,21 +166,28 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   uint32_t vst[4][VW];
 
   auto load_tile = [&](int t) {
-    const uint32_t kb = koff0 + (uint32_t)t * k_tile_bytes;
+    rsrc_t rkt = rk, rvt = rv;
+    uint32_t tk = (uint32_t)t * k_tile_bytes, tv = (uint32_t)t * v_tile_bytes;
+    if constexpr (CHUNKED) {
+      rkt = page_rsrc(a.k, a.k_pages, a.k_pool_pages, a.k_sb, a.k_sh, a.k_ss, t);
+      rvt = page_rsrc(a.v, a.v_pages, a.v_pool_pages, a.v_sb, a.v_sh, a.v_ss, t);
+      tk = tv = 0;
+    }
+    const uint32_t kb = koff0 + tk;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) kst[i] = buffer_load_16(rk, kb + i * kstep);
-    const uint32_t vb = voff + (uint32_t)t * v_tile_bytes;
+    for (int i = 0; i < KPT; ++i) kst[i] = buffer_load_16(rkt, kb + i * kstep);
+    const uint32_t vb = voff + tv;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (VW % 4 == 0) {
 #pragma unroll
         for (int c4 = 0; c4 < VW; c4 += 4) {
-          const u32x4 x = buffer_load_16(rv, vb + r * vrow + c4 * 4);
+          const u32x4 x = buffer_load_16(rvt, vb + r * vrow + c4 * 4);
           vst[r][c4] = x[0]; vst[r][c4 + 1] = x[1]; vst[r][c4 + 2] = x[2]; vst[r][c4 + 3] = x[3];
         }
       } else {
         static_assert(VW == 2, "4 channels per thread use one 8-byte load");
-        const u32x2 x = buffer_load_8(rv, vb + r * vrow);
+        const u32x2 x = buffer_load_8(rvt, vb + r * vrow);
         vst[r][0] = x[0]; vst[r][1] = x[1];
       }
     }
@@ -198,7 +234,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     if constexpr (MASK) {
       // key offset o inside the tile is valid for this row iff o <= lim
       const int key_base = t * kTK;
-      const int lim = !row_ok ? -1 : (a.causal ? min(iq, S - 1) - key_base : S - 1 - key_base);
+      const int lim = !row_ok ? -1 : (a.causal ? iq + off - key_base : Sk - 1 - key_base);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -291,7 +327,8 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const float l_tot = pair_sum(l_part);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
-    uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)iq * a.o_ss + (int64_t)h * a.o_sh;
+    uint16_t* op = a.o + (CHUNKED ? (int64_t)(qrow0 + iq) * a.o_ss : (int64_t)b * a.o_sb + (int64_t)iq * a.o_ss) +
+                   (int64_t)h * a.o_sh;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -317,15 +354,22 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hq * a.nqt);
   if (grid == 0) return hipSuccess;
-  if (d == 128 && tile_q == 128) hipLaunchKernelGGL((prefill_kernel<128, 128>), dim3(grid), dim3(256), 0, stream, a);
-  else if (d == 128 && tile_q == 64) hipLaunchKernelGGL((prefill_kernel<128, 64>), dim3(grid), dim3(128), 0, stream, a);
-  else if (d == 64 && tile_q == 128) hipLaunchKernelGGL((prefill_kernel<64, 128>), dim3(grid), dim3(256), 0, stream, a);
-  else if (d == 64 && tile_q == 64) hipLaunchKernelGGL((prefill_kernel<64, 64>), dim3(grid), dim3(128), 0, stream, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  const dim3 blk(tile_q * 2);
+#define SSM_PREFILL_LAUNCH(D, TQ)                                                                        \
+  if (d == D && tile_q == TQ) {                                                                          \
+    if (chunked) hipLaunchKernelGGL((prefill_kernel<D, TQ, true>), dim3(grid), blk, 0, stream, a);       \
+    else hipLaunchKernelGGL((prefill_kernel<D, TQ, false>), dim3(grid), blk, 0, stream, a);              \
+    return hipGetLastError();                                                                            \
+  }
+  SSM_PREFILL_LAUNCH(128, 128)
+  SSM_PREFILL_LAUNCH(128, 64)
+  SSM_PREFILL_LAUNCH(64, 128)
+  SSM_PREFILL_LAUNCH(64, 64)
+#undef SSM_PREFILL_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ssm

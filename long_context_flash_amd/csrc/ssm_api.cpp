@@ -155,7 +155,7 @@ int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, i
     a.unit_gap = skip_stats->unit_gap;
     a.counters = skip_stats->counters;
   }
-  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, static_cast<hipStream_t>(stream)));
+  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, false, static_cast<hipStream_t>(stream)));
 }
 
 static int check_cache(const ssm_kv_cache* c, const char* name, int64_t B, int64_t d, int* kv_cap, int64_t* pool_rows,
@@ -268,6 +268,87 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
     a.counters = skip_stats->counters;
   }
   return launch_status(ssm::launch_decode_impl(a, (int)d, kv_cap, krows, vrows, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+                      const int32_t* q_start, const int32_t* kv_lens, int32_t batch, int32_t max_q_len,
+                      int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+                      const ssm_opts* opts) {
+  int rc;
+  if ((rc = check_tensor(q, "q", 3, SSM_BF16)) || (rc = check_tensor(out, "out", 3, SSM_BF16))) return rc;
+  if (!q_start || !kv_lens) return fail(SSM_EINVAL, "q_start and kv_lens must be device arrays");
+  if ((rc = check_tau(tau))) return rc;
+  if (batch < 0 || max_q_len < 0) return fail(SSM_EINVAL, "batch and max_q_len must be >= 0");
+  const int64_t total_q = q->shape[0], Hq = q->shape[1], d = q->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(SSM_EINVAL, "out shape mismatch in dim %d", i);
+  if (!k_cache || !v_cache || !k_cache->page_table || !v_cache->page_table)
+    return fail(SSM_EINVAL, "k_cache and v_cache must be paged");
+  int kcap, vcap;
+  int64_t krows, vrows, hk, hv;
+  if ((rc = check_cache(k_cache, "k_cache", batch, d, &kcap, &krows, &hk)) ||
+      (rc = check_cache(v_cache, "v_cache", batch, d, &vcap, &vrows, &hv)))
+    return rc;
+  if (k_cache->pool.dtype != SSM_BF16 || v_cache->pool.dtype != SSM_BF16)
+    return fail(SSM_EUNSUPPORTED, "chunked prefill reads bf16 caches");
+  if (k_cache->max_pages != v_cache->max_pages) return fail(SSM_EINVAL, "k and v page tables differ in length");
+  if (hk != hv) return fail(SSM_EINVAL, "k/v head counts differ");
+  const int64_t Hkv = hk;
+  if (Hkv <= 0 || Hq % Hkv != 0) return fail(SSM_EINVAL, "Hq (%lld) must be a positive multiple of Hkv (%lld)",
+                                             (long long)Hq, (long long)Hkv);
+  if (d != 64 && d != 128) return fail(SSM_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  const int tile_q = (opts && opts->tile_q) ? opts->tile_q : 128;
+  const int tile_k = (opts && opts->tile_k) ? opts->tile_k : 64;
+  if (tile_q != 64 && tile_q != 128) return fail(SSM_EUNSUPPORTED, "tile_q %d not supported (64 or 128)", tile_q);
+  if (tile_k != 64) return fail(SSM_EUNSUPPORTED, "tile_k %d not supported (64)", tile_k);
+  float scale;
+  if ((rc = resolve_scale(opts, (int)d, &scale))) return rc;
+  if (total_q > INT32_MAX || max_q_len > (1 << 30) || Hq > 65536) return fail(SSM_EUNSUPPORTED, "problem too large");
+  const int64_t nqt = ((int64_t)max_q_len + tile_q - 1) / tile_q, nkt = k_cache->max_pages;
+  const int64_t units = (int64_t)batch * Hq * nqt;
+  if (units > INT32_MAX) return fail(SSM_EUNSUPPORTED, "too many query tiles");
+  if (((int64_t)max_q_len + 128) * q->stride[0] * 2 + d * 2 > (int64_t)UINT32_MAX)
+    return fail(SSM_EUNSUPPORTED, "max_q_len too long for 32-bit slice offsets");
+  if (skip_stats) {
+    if (skip_stats->tile_state && skip_stats->tile_state_len < units * nkt)
+      return fail(SSM_EINVAL, "tile_state needs %lld elements", (long long)(units * nkt));
+    if (skip_stats->unit_gap && skip_stats->unit_gap_len < units * nkt)
+      return fail(SSM_EINVAL, "unit_gap needs %lld elements", (long long)(units * nkt));
+  }
+  if (batch == 0 || max_q_len == 0 || Hq == 0) return SSM_OK;
+
+  ssm::PrefillArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.k = static_cast<const uint16_t*>(k_cache->pool.data);
+  a.v = static_cast<const uint16_t*>(v_cache->pool.data);
+  a.o = static_cast<uint16_t*>(out->data);
+  a.q_ss = q->stride[0]; a.q_sh = q->stride[1];
+  a.o_ss = out->stride[0]; a.o_sh = out->stride[1];
+  a.k_sb = k_cache->pool.stride[0]; a.k_sh = k_cache->pool.stride[1]; a.k_ss = k_cache->pool.stride[2];
+  a.v_sb = v_cache->pool.stride[0]; a.v_sh = v_cache->pool.stride[1]; a.v_ss = v_cache->pool.stride[2];
+  a.B = batch; a.S = max_q_len; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv);
+  a.nqt = (int)nqt; a.nkt = (int)nkt;
+  a.causal = causal != 0;
+  const int64_t groups = (int64_t)batch * Hkv;
+  a.xcd_groups = groups % 8 == 0 ? (int)(groups / 8) : 0;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tau_raw = std::isinf(tau) ? tau : tau / scale;
+  if (skip_stats) {
+    a.tile_state = skip_stats->tile_state;
+    a.unit_gap = skip_stats->unit_gap;
+    a.counters = skip_stats->counters;
+  }
+  a.q_start = q_start;
+  a.kv_lens = kv_lens;
+  a.k_pages = k_cache->page_table;
+  a.v_pages = v_cache->page_table;
+  a.max_pages = k_cache->max_pages;
+  a.total_q = (int)total_q;
+  a.k_pool_pages = krows;
+  a.v_pool_pages = vrows;
+  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, true, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

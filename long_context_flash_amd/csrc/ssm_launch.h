@@ -24,6 +24,16 @@ struct PrefillArgs {
   uint8_t* tile_state;       // nullable [units, nkt]
   float* unit_gap;           // nullable [units, nkt]
   unsigned long long* counters;  // nullable [4]
+  // chunked prefill against a paged cache (prefill_kernel<..., true>): S is the longest query count;
+  // sequence b's queries are q rows q_start[b] .. q_start[b+1]-1 (o likewise; q_sb/o_sb unused), the last
+  // of its kv_lens[b] cached keys; key tile t of (b, KV head g) is page k_pages[b*max_pages + t]
+  const int32_t* q_start;
+  const int32_t* kv_lens;
+  const int32_t* k_pages;
+  const int32_t* v_pages;
+  int32_t max_pages;         // row length of the page tables (= nkt)
+  int32_t total_q;           // rows of q/o
+  int64_t k_pool_pages, v_pool_pages;
 };
 
 struct DecodeArgs {
@@ -55,7 +65,7 @@ struct DecodeArgs {
   unsigned long long* counters;
 };
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, hipStream_t stream);
 hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
                               hipStream_t stream);
 

@@ -208,3 +208,104 @@ def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", 
         f"gpu sparsity={sparsity:.3f}")
     assert max_abs <= MAX_ABS and rel <= REL_L2, f"{where}: max_abs {max_abs} rel_l2 {rel}"
     return {"max_abs": max_abs, "rel_l2": rel, "sparsity": sparsity, "state": st, "out": out}
+
+
+# ----------------------------------------------------------------- chunked prefill against a paged cache
+def chunk_batch(w, seqs, seed=0, extra_pages=3):
+    """A ragged chunked-prefill batch from GEN-A sequences: seqs = [(n_q, n_k), ...].  Sequence b is the GEN-A
+    input of w with S = n_k (seed w.seed + b); its queries are the last n_q positions; its keys fill
+    ceil(n_k/64) pages of a shared pool at randomly permuted page ids (plus a few unused pages)."""
+    import synth as _synth
+    Hq, Hkv, d = w.Hq, w.Hkv, w.d
+    per = [_synth.gen_prefill(_synth.replace(w, B=1, S=nk, seed=w.seed + b)) for b, (_, nk) in enumerate(seqs)]
+    npages = [-(-nk // 64) for _, nk in seqs]
+    total_pages = sum(npages) + extra_pages
+    perm = np.random.default_rng(seed).permutation(total_pages).astype(np.int32)
+    max_pages = max(max(npages), 1)
+    pool_k = np.zeros((total_pages, Hkv, 64, d), np.uint16)
+    pool_v = np.zeros_like(pool_k)
+    pt = np.full((len(seqs), max_pages), -1, np.int32)
+    q_rows, q_start = [], [0]
+    nxt = 0
+    for b, ((nq, nk), dat) in enumerate(zip(seqs, per)):
+        for t in range(npages[b]):
+            pg = perm[nxt]; nxt += 1
+            pt[b, t] = pg
+            rows = slice(t * 64, min(nk, (t + 1) * 64))
+            n = rows.stop - rows.start
+            pool_k[pg, :, :n] = dat["k"][0, rows].transpose(1, 0, 2)
+            pool_v[pg, :, :n] = dat["v"][0, rows].transpose(1, 0, 2)
+        q_rows.append(dat["q"][0, nk - nq:])
+        q_start.append(q_start[-1] + nq)
+    return {"seqs": seqs, "per": per, "q": np.ascontiguousarray(np.concatenate(q_rows, 0)),
+            "k_pool": pool_k, "v_pool": pool_v, "page_table": pt, "q_start": np.array(q_start, np.int32),
+            "kv_lens": np.array([nk for _, nk in seqs], np.int32), "max_q": max(nq for nq, _ in seqs)}
+
+
+def run_prefill_paged_gpu(cb, *, Hq, causal, tau, tile_q, device="cuda"):
+    q = ssm.bf16_from_bits(cb["q"], device)
+    kc = ssm.bf16_from_bits(cb["k_pool"], device)
+    vc = ssm.bf16_from_bits(cb["v_pool"], device)
+    pt = torch.from_numpy(cb["page_table"]).to(device)
+    qs = torch.from_numpy(cb["q_start"]).to(device)
+    kl = torch.from_numpy(cb["kv_lens"]).to(device)
+    B = len(cb["seqs"])
+    nqt = -(-cb["max_q"] // tile_q)
+    stats = ssm.SkipStats.alloc(B * Hq * nqt, pt.shape[1], device, gaps=True)
+    out = ssm.ssm_prefill_paged(q, kc, vc, pt, qs, kl, cb["max_q"], causal=causal, tau=tau, skip_stats=stats,
+                                tile_q=tile_q)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
+            stats.counters.cpu().numpy())
+
+
+def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads=None, sample=None):
+    """GPU chunked prefill on the whole ragged batch vs the oracle on each sequence (all its units, or the
+    (h, q_tile) pairs listed in sample[b])."""
+    seqs = cb["seqs"]
+    B = len(seqs)
+    log(f"{where}: GPU chunked prefill seqs={seqs} Hq={Hq} causal={causal} tau={tau} tile_q={tile_q}")
+    out, st, gap, cnt = run_prefill_paged_gpu(cb, Hq=Hq, causal=causal, tau=tau, tile_q=tile_q)
+    vis, skipped = int((st > 0).sum()), int((st == 2).sum())
+    assert list(cnt) == [vis, skipped, vis, vis - skipped], f"{where}: counters {list(cnt)} vs tile_state"
+    nqt_max = -(-cb["max_q"] // tile_q)
+    errs = []
+    for b, (nq, nk) in enumerate(seqs):
+        rows = np.arange(b * Hq * nqt_max, (b + 1) * Hq * nqt_max).reshape(Hq, nqt_max)
+        nqt = -(-nq // tile_q)
+        assert not st[rows[:, nqt:]].any(), f"{where}: query tiles past sequence {b} marked visited"
+        if nq == 0:
+            continue
+        dat = cb["per"][b]
+        qb = np.ascontiguousarray(dat["q"][:, nk - nq:])
+        if sample is not None:
+            hq = np.array(sample[b], np.int64).reshape(-1, 2)
+            ounits = hq[:, 0] * nqt + hq[:, 1]
+            u = rows[hq[:, 0], hq[:, 1]]
+        else:
+            ounits = None
+            u = rows[:, :nqt].ravel()
+        ref = oracle.prefill(qb, dat["k"], dat["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
+                             units=ounits, threads=threads)
+        nkt = ref["state"].shape[1]
+        st_g = st[u][:, :nkt]
+        assert not st[u][:, nkt:].any(), f"{where}: key tiles past sequence {b} marked visited"
+        flips, n_amb = compare_masks(st_g, ref["state"], ref["gamma"], tau, f"{where} seq {b}")
+        compare_gaps(gap[u][:, :nkt], ref["gamma"], ref["state"], f"{where} seq {b}")
+        if flips.any():
+            ov = np.where(flips, np.where(st_g == 2, 1, 0), -1).astype(np.int8)
+            ref = oracle.prefill(qb, dat["k"], dat["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
+                                 units=ounits, override=ov, threads=threads)
+        got = np.zeros_like(ref["out"])
+        q0 = cb["q_start"][b]
+        pairs = [(h, qt) for h in range(Hq) for qt in range(nqt)] if sample is None else [tuple(x) for x in hq]
+        for n, (h, qt) in enumerate(pairs):
+            r0, r1 = qt * tile_q, min(nq, (qt + 1) * tile_q)
+            got[n, :r1 - r0] = out[q0 + r0:q0 + r1, h]
+        errs.append(errors(got, ref["out"]))
+    max_abs = max((e[0] for e in errs), default=0.0)
+    rel = max((e[1] for e in errs), default=0.0)
+    sparsity = skipped / max(vis, 1)
+    log(f"{where}: max_abs={max_abs:.3e} rel_l2(worst seq)={rel:.3e} gpu sparsity={sparsity:.3f}")
+    assert max_abs <= MAX_ABS and rel <= REL_L2, f"{where}: max_abs {max_abs} rel_l2 {rel}"
+    return {"max_abs": max_abs, "rel_l2": rel, "sparsity": sparsity, "state": st, "out": out}

@@ -1,0 +1,62 @@
+"""HIP chunked prefill against a paged KV cache (ragged batch, bottom-right causal) vs the fp64 oracle (GPU)."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from parity import chunk_batch, check_prefill_paged, run_prefill_paged_gpu
+
+LN1000 = math.log(1000.0)
+pytestmark = pytest.mark.gpu
+
+SMALL = synth.replace(synth.PREFILL_16K, S=0, Hq=8, Hkv=2, rank=8, seed=300)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tile_q", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_batch(d, tile_q, causal):
+    """Chunks of 1, 63, 129 and 300 queries after prefixes that are and are not multiples of 64, a whole-sequence
+    chunk (no prefix) and an empty one."""
+    w = synth.replace(SMALL, d=d)
+    seqs = [(129, 700), (1, 65), (300, 300), (63, 1000), (0, 77), (200, 263)]
+    cb = chunk_batch(w, seqs, seed=1)
+    for tau in (-LN1000, -math.inf):
+        check_prefill_paged(cb, Hq=w.Hq, causal=causal, tau=tau, tile_q=tile_q,
+                            where=f"chunked d={d} tq={tile_q} causal={causal} tau={tau}")
+
+
+def test_whole_sequence_chunk_matches_prefill():
+    """A chunk holding every position of a sequence is the plain prefill: same decisions, same output."""
+    import long_context_flash_amd as ssm
+    import torch
+    w = synth.replace(SMALL, d=128)
+    cb = chunk_batch(w, [(512, 512)], seed=2)
+    out_p, st_p, _, _ = run_prefill_paged_gpu(cb, Hq=w.Hq, causal=True, tau=-LN1000, tile_q=128)
+    dat = cb["per"][0]
+    q, k, v = (ssm.bf16_from_bits(dat[x], "cuda") for x in ("q", "k", "v"))
+    stats = ssm.SkipStats.alloc(*ssm.prefill_stats_shape(1, 512, w.Hq, 128), "cuda")
+    out = ssm.ssm_prefill(q, k, v, causal=True, tau=-LN1000, skip_stats=stats, tile_q=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(out[0].float().cpu().numpy(), out_p)
+    assert np.array_equal(stats.tile_state.cpu().numpy(), st_p)
+
+
+def test_llama_shape_long_context_chunk():
+    """64 query / 8 KV heads, d = 128: a 2K chunk after a 14K prefix and a 1K chunk after a 3K prefix."""
+    w = synth.replace(synth.PREFILL_16K, S=0, seed=310)
+    cb = chunk_batch(w, [(2048, 16384), (1024, 4096)], seed=3)
+    r = check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=w.taus[2], tile_q=128, where="chunked llama 16k")
+    assert r["sparsity"] > 0.3
+
+
+def test_chunk_8k_of_128k_sampled():
+    """The benchmark's chunked workload: the last 8192 queries of the 128K prefill input against all 131072
+    keys in a paged pool; the oracle checks sampled units (the first and last query tiles among them)."""
+    w = synth.PREFILL_128K
+    cb = chunk_batch(w, [(8192, w.S)], seed=4)
+    sample = {0: [(0, 0), (9, 1), (17, 31), (40, 62), (63, 63)]}
+    r = check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=w.taus[0], tile_q=128, sample=sample,
+                            where="chunked 8k of 128k")
+    assert r["sparsity"] > 0.3
