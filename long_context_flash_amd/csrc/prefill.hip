@@ -219,17 +219,23 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     const int buf = t & 1;
     if (t + 1 < T) load_tile(t + 1);
 
-    // S^T for keys t*64 .. t*64+63 (two 32-key blocks) x this wave's 32 query columns
-    f32x16 s[2];
+    // S^T for keys t*64 .. t*64+63 (two 32-key blocks) x this wave's 32 query columns.  The two blocks'
+    // MFMA chains alternate k-step by k-step and each k-step's K operands are read from LDS two k-steps
+    // ahead, so neither an MFMA result nor an LDS read is waited for back to back.
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      const uint16_t* kl = &k_lds[buf][col * KROW + half * 8];
+      auto kop = [&](int kb, int ks) { return *reinterpret_cast<const u32x4*>(kl + kb * 32 * KROW + ks * 16); };
+      u32x4 x[KSTEPS][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 c = f32x16{};
+      for (int ks = 0; ks < 2; ++ks) x[ks][0] = kop(0, ks), x[ks][1] = kop(1, ks);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(&k_lds[buf][(kb * 32 + col) * KROW + ks * 16 + half * 8]);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x), qreg[ks], c, 0, 0, 0);
+        if (ks + 2 < KSTEPS) x[ks + 2][0] = kop(0, ks + 2), x[ks + 2][1] = kop(1, ks + 2);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[ks][0]), qreg[ks], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[ks][1]), qreg[ks], s[1], 0, 0, 0);
       }
-      s[kb] = c;
     }
     if constexpr (MASK) {
       // key offset o inside the tile is valid for this row iff o <= lim
@@ -288,6 +294,12 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
         m_ref = move ? m_true : m_ref;
       }
       const float moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+      // V^T operands of the first 16-key step, read now so that they land during the exponentials
+      const uint16_t* vl = &v_lds[buf][col * VROW + 8 * half];
+      auto vop = [&](int cb, int st) { return *reinterpret_cast<const u32x4*>(vl + cb * 32 * VROW + 16 * st); };
+      u32x4 vx[4][CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) vx[0][cb] = vop(cb, 0);
       bf16x8 pb[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -301,14 +313,18 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
         }
         pb[st] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
       }
-      // O^T += V^T . P^T
+      // O^T += V^T . P^T: the CB accumulator chains alternate step by step; the next step's operands are
+      // read while the current step's MFMAs issue
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int st = 0; st < 4; ++st) {
+        if (st + 1 < 4)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(&v_lds[buf][(cb * 32 + col) * VROW + 16 * st + 8 * half]);
-          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x), pb[st], acc[cb], 0, 0, 0);
-        }
+          for (int cb = 0; cb < CB; ++cb) vx[st + 1][cb] = vop(cb, st + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vx[st][cb]), pb[st], acc[cb], 0, 0, 0);
+      }
     }
     if (t + 1 < T) store_tile(buf ^ 1);
     __syncthreads();
