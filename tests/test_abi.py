@@ -233,3 +233,57 @@ def test_struct_layouts_match_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def call_prefill_paged(lib, q=None, kc=None, vc=None, q_start=FAKE, kv_lens=FAKE, batch=2, max_q=256, tau=-6.9,
+                       o=None, opts="default"):
+    q = q or desc([300, 16, 128])
+    o = o or desc([300, 16, 128])
+    kc = kc or cache([100, 2, 64, 128], paged=True, max_pages=64)
+    vc = vc or cache([100, 2, 64, 128], paged=True, max_pages=64)
+    if opts == "default":
+        opts = ssm.Opts(0.0, 0, 0, 0, None, 0, 0)
+    return lib.ssm_prefill_paged(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(vc), q_start, kv_lens, batch, max_q,
+                                 1, tau, ctypes.byref(o), None, None, ctypes.byref(opts) if opts else None)
+
+
+@pytest.mark.parametrize("case,code", [
+    ("contiguous_cache", ssm.SSM_EINVAL), ("null_q_start", ssm.SSM_EINVAL), ("null_kv_lens", ssm.SSM_EINVAL),
+    ("neg_batch", ssm.SSM_EINVAL), ("pos_tau", ssm.SSM_EINVAL), ("page_tables_differ", ssm.SSM_EINVAL),
+    ("fp8_cache", ssm.SSM_EUNSUPPORTED), ("head_dim", ssm.SSM_EUNSUPPORTED), ("tile_q", ssm.SSM_EUNSUPPORTED),
+    ("gqa", ssm.SSM_EINVAL), ("out_shape", ssm.SSM_EINVAL),
+])
+def test_prefill_paged_rejects(lib, case, code):
+    kw = {}
+    if case == "contiguous_cache":
+        kw["kc"], kw["vc"] = cache([2, 2, 1024, 128]), cache([2, 2, 1024, 128])
+    elif case == "null_q_start":
+        kw["q_start"] = None
+    elif case == "null_kv_lens":
+        kw["kv_lens"] = None
+    elif case == "neg_batch":
+        kw["batch"] = -1
+    elif case == "pos_tau":
+        kw["tau"] = 0.5
+    elif case == "page_tables_differ":
+        kw["vc"] = cache([100, 2, 64, 128], paged=True, max_pages=32)
+    elif case == "fp8_cache":
+        kw["kc"] = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=ssm.SSM_FP8_E4M3, scale=1.0)
+        kw["vc"] = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=ssm.SSM_FP8_E4M3, scale=1.0)
+    elif case == "head_dim":
+        kw["q"], kw["o"] = desc([300, 16, 96]), desc([300, 16, 96])
+        kw["kc"] = cache([100, 2, 64, 96], paged=True, max_pages=64)
+        kw["vc"] = cache([100, 2, 64, 96], paged=True, max_pages=64)
+    elif case == "tile_q":
+        kw["opts"] = ssm.Opts(0.0, 96, 0, 0, None, 0, 0)
+    elif case == "gqa":
+        kw["q"], kw["o"] = desc([300, 15, 128]), desc([300, 15, 128])
+    elif case == "out_shape":
+        kw["o"] = desc([299, 16, 128])
+    rc = call_prefill_paged(lib, **kw)
+    assert rc == code, (case, rc, ssm.ssm_last_error())
+
+
+def test_prefill_paged_empty_batch_is_a_no_op(lib):
+    assert call_prefill_paged(lib, batch=0) == ssm.SSM_OK
+    assert call_prefill_paged(lib, max_q=0) == ssm.SSM_OK
