@@ -17,9 +17,14 @@
 //   swap with lane^32 (v_permlane32_swap) that holds the other 32 keys.
 //   O^T (d x 32 queries) += V^T . P^T on the same MFMA.  The accumulator layout
 //   of S^T is consumed directly as the P^T operand (converted to bf16 in
-//   registers); V is staged in LDS transposed ([channel][key]) with the keys of
-//   each 16-key group stored in the order that matches that accumulator layout,
-//   so each operand is a single 16-byte LDS read.
+//   registers).
+//
+// Tiles go from HBM straight into LDS (buffer loads with an LDS destination,
+// no registers): key-row major, 16-byte chunks XOR-swizzled per row.  The K
+// operand is one 16-byte read per lane; the V^T operand is gathered by two
+// transposing reads (ds_read_b64_tr_b16) in the key order of the S^T
+// accumulator.  Rows past the sequence end fall outside the buffer resource and
+// land as zeros, so loads carry no predication.
 //
 // Skip vote: every lane votes "keep" unless its row abstains (no valid key in
 // the tile) or its gap (tile max - running max) is below tau; a wave ballot
@@ -28,11 +33,12 @@
 // never holds a new maximum, so this equals the prefix maximum over all
 // visited tiles.
 //
-// Pipeline: K and V tiles are double-buffered in LDS; the buffer loads of tile
-// t+1 are issued before tile t's MFMAs and written to LDS after them.  Rows
-// past the sequence end fall outside the buffer resource and read as zero, so
-// loads carry no predication.  Tiles wholly inside the causal triangle run a
-// step without any masking code; only the diagonal/ragged tiles mask.
+// Pipeline (one barrier per tile): S(t) and the vote on tile t; barrier; the
+// decision; the loads of K(t+2) and, only for a kept tile, V(t); then the
+// exponentials of tile t issued between the P*V MFMAs of the previous kept
+// tile t-1, so the transcendental work of one tile overlaps the matrix work of
+// the other inside each wave.  Tiles wholly inside the causal triangle run
+// without masking code; only the diagonal/ragged tiles mask.
 //
 // Exponentials use a lazily moved reference maximum: P = 2^(S*c - m_ref*c) with
 // m_ref only raised when the true running maximum exceeds it by more than 8
@@ -72,23 +78,34 @@ __device__ __forceinline__ void map_prefill_unit(int bid, const PrefillArgs& a, 
   qt = a.nqt - 1 - level;  // longest causal units first
 }
 
+// LDS tile layout: key row r of a K or V tile occupies 2*D bytes; its 16-byte chunk c (channels 8c..8c+7)
+// sits at chunk position c ^ swz(r).  K: 16 consecutive rows read at one logical chunk (one 16-lane
+// phase of an operand read) land on 16 distinct positions.  V: the 4 rows gathered by one transposing
+// read land on 4 distinct 4-chunk groups.
+template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
 // CHUNKED: queries of each sequence are the last ones of its cached keys (bottom-right causal), packed
 // ragged rows of q/o, K/V read through a page table (see PrefillArgs).
 template <int D, int TQ, bool CHUNKED>
 __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = TQ / 32;             // waves per workgroup
-  constexpr int NT = NW * 64;             // threads
-  constexpr int KROW = D + 8;             // K tile row stride in LDS (elements); +16 B avoids bank conflicts
-  constexpr int VROW = kTK + 8;           // V^T row stride in LDS (elements)
+  constexpr int ROWB = 2 * D;             // bytes per key row of a tile in LDS
   constexpr int KSTEPS = D / 16;          // k-steps of the QK^T MFMA
   constexpr int CB = D / 32;              // 32-channel blocks of the output
-  constexpr int KPT = kTK * D / 8 / NT;   // 16-byte K chunks per thread per tile
-  constexpr int CPT = kTK * D / (NT * 4); // V channels per thread (4 keys each)
-  constexpr int VW = CPT / 2;             // dwords per key row per thread
-  static_assert(KPT >= 1 && CPT >= 4 && CPT % 4 == 0, "tile split");
+  constexpr int IPW = kTK * ROWB / 1024 / NW;  // 1 KB direct-to-LDS loads per wave, tensor and tile
+  static_assert(IPW >= 1 && kTK * ROWB % (1024 * NW) == 0, "tile split");
+  constexpr int AHEAD = 2;                // MFMAs an LDS operand read runs ahead of its use
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VROW];
+  // separate arrays per buffer: the wait-count pass then sees that a load into one buffer does not
+  // alias reads of the other
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kTK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kTK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kTK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kTK * D];
   __shared__ uint32_t votes[2][NW];
   __shared__ float wave_gap[2][NW];
 
@@ -127,7 +144,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const float c2 = a.scale_log2;
 
   // ---- buffer resources: one (b, head) slice each (chunked: K/V per tile, below); bytes past the last row
-  // read as zero
+  // read as zero (also for the direct-to-LDS loads)
   const rsrc_t rq = CHUNKED ? make_rsrc(a.q + (int64_t)qrow0 * a.q_ss + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D))
                             : make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D));
   const rsrc_t rk = make_rsrc(a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh, CHUNKED ? 0u : rows_bytes(S, a.k_ss, D));
@@ -150,60 +167,72 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = as_bf16x8(buffer_load_16(rq, row_ok ? qoff + ks * 32 : qoff));
   }
 
-  // ---- tile staging: per-thread byte offsets inside a tile never change; tile t adds t*64 rows.
-  // K: thread tid moves 16-byte chunk (tid % (D/8)) of key rows tid/(D/8) + i*KSTRIDE, i < KPT.
-  constexpr int KSTRIDE = NT / (D / 8);
-  const int key0 = tid / (D / 8), ch0 = (tid % (D / 8)) * 8;
-  const uint32_t koff0 = (uint32_t)(key0 * a.k_ss * 2 + ch0 * 2), kstep = (uint32_t)(KSTRIDE * a.k_ss * 2);
-  const int klds0 = key0 * KROW + ch0;
-  const uint32_t k_tile_bytes = (uint32_t)(kTK * a.k_ss * 2), v_tile_bytes = (uint32_t)(kTK * a.v_ss * 2);
-  // V: thread moves keys 4*vkq .. 4*vkq+3 x channels vcg*CPT .. +CPT and writes them transposed;
-  // within each 16-key group the 4-key chunks are stored as 0, 2, 1, 3 (the P^T operand order)
-  const int vkq = tid & 15, vcg = tid >> 4;
-  const uint32_t voff = (uint32_t)(4 * vkq * a.v_ss * 2 + vcg * CPT * 2), vrow = (uint32_t)(a.v_ss * 2);
-  const int vpos = 16 * (vkq >> 2) + 4 * (((vkq & 1) << 1) | ((vkq >> 1) & 1));
-  u32x4 kst[KPT];
-  uint32_t vst[4][VW];
+  // ---- tile loads, straight into LDS: load i of wave w fills LDS bytes [(w*IPW + i) KB, +1 KB) of the
+  // tile, lane l the 16 bytes at l*16 of it, i.e. chunk position p of row r; it fetches the logical chunk
+  // p ^ swz(r) of that key row.
+  constexpr int RPL = 1024 / ROWB;  // key rows per load
+  const int lrow = lane / (ROWB / 16), lpos = lane % (ROWB / 16);
+  const uint32_t k_row_bytes = (uint32_t)(a.k_ss * 2), v_row_bytes = (uint32_t)(a.v_ss * 2);
+  const uint32_t k_tile_bytes = kTK * k_row_bytes, v_tile_bytes = kTK * v_row_bytes;
+  // Row (w*IPW + i)*RPL + lrow: both swizzles split into a per-lane part and a part of the load index
+  // (their bit fields do not overlap), so the chunk offset is (lane part) ^ (uniform part).
+  uint32_t k_dma = (uint32_t)(w * IPW * RPL + lrow) * k_row_bytes;   // row part of this lane's K loads
+  uint32_t k_dmx = (uint32_t)(lpos ^ swz_k<D>(lrow)) * 16;           // chunk part
+  uint32_t v_dma = (uint32_t)(w * IPW * RPL + lrow) * v_row_bytes + (uint32_t)(lpos ^ swz_v<D>(lrow)) * 16;
+  auto load_k_rsrc = [&](uint16_t* dst, rsrc_t r, uint32_t toff) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const uint32_t cx = (uint32_t)swz_k<D>((w * IPW + i) * RPL) * 16;  // wave-uniform
+      const uint32_t vo = k_dma + (k_dmx ^ cx) + (uint32_t)(i * RPL) * k_row_bytes + toff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + (w * IPW + i) * 512), 16, vo, 0, 0, 0);
+    }
+  };
+  auto load_v_rsrc = [&](uint16_t* dst, rsrc_t r, uint32_t toff) {
+    static_assert(D == 128 || D == 64, "the V swizzle has no load-index part for these widths");
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const uint32_t vo = v_dma + (uint32_t)(i * RPL) * v_row_bytes + toff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + (w * IPW + i) * 512), 16, vo, 0, 0, 0);
+    }
+  };
+  auto load_k = [&](uint16_t* dst, int t) {
+    if constexpr (CHUNKED) load_k_rsrc(dst, page_rsrc(a.k, a.k_pages, a.k_pool_pages, a.k_sb, a.k_sh, a.k_ss, t), 0u);
+    else load_k_rsrc(dst, rk, (uint32_t)t * k_tile_bytes);
+  };
+  auto load_v = [&](uint16_t* dst, int t) {
+    if constexpr (CHUNKED) load_v_rsrc(dst, page_rsrc(a.v, a.v_pages, a.v_pool_pages, a.v_sb, a.v_sh, a.v_ss, t), 0u);
+    else load_v_rsrc(dst, rv, (uint32_t)t * v_tile_bytes);
+  };
 
-  auto load_tile = [&](int t) {
-    rsrc_t rkt = rk, rvt = rv;
-    uint32_t tk = (uint32_t)t * k_tile_bytes, tv = (uint32_t)t * v_tile_bytes;
-    if constexpr (CHUNKED) {
-      rkt = page_rsrc(a.k, a.k_pages, a.k_pool_pages, a.k_sb, a.k_sh, a.k_ss, t);
-      rvt = page_rsrc(a.v, a.v_pages, a.v_pool_pages, a.v_sb, a.v_sh, a.v_ss, t);
-      tk = tv = 0;
-    }
-    const uint32_t kb = koff0 + tk;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) kst[i] = buffer_load_16(rkt, kb + i * kstep);
-    const uint32_t vb = voff + tv;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (VW % 4 == 0) {
-#pragma unroll
-        for (int c4 = 0; c4 < VW; c4 += 4) {
-          const u32x4 x = buffer_load_16(rvt, vb + r * vrow + c4 * 4);
-          vst[r][c4] = x[0]; vst[r][c4 + 1] = x[1]; vst[r][c4 + 2] = x[2]; vst[r][c4 + 3] = x[3];
-        }
-      } else {
-        static_assert(VW == 2, "4 channels per thread use one 8-byte load");
-        const u32x2 x = buffer_load_8(rvt, vb + r * vrow);
-        vst[r][0] = x[0]; vst[r][1] = x[1];
-      }
-    }
+  // ---- operand reads.  Byte offsets inside a tile buffer: per lane one base, per operand an XOR with a
+  // constant on bits that neither the base's row part nor the added constants touch.
+  // K (S^T's A operand): lane (col, half) reads row kb*32 + col, logical chunk 2*ks + half, i.e. byte
+  // (kb*32 + col)*ROWB + 16*((2ks + half) ^ swz_k(col)) = (k_opb ^ 32*ks) + kb*32*ROWB.
+  const int xk = swz_k<D>(col);
+  uint32_t k_opb = (uint32_t)(col * ROWB + 32 * (xk >> 1) + 16 * (half ^ (xk & 1)));
+  // V^T (O^T's A operand) by transposing reads: in each 16-lane group, lane 4j + m names 4 channels
+  // (4m .. 4m+3 of the group's 16) of key row k0 + j and receives channel (lane & 15) of the 4 rows.
+  // Group gq covers channels 16*(gq & 1) of each 32-channel block and the keys of half gq >> 1.  The
+  // logical chunk of channel block cb is 4cb + vch/8, and swz_v(k0 + vrow) = swz_v(vrow) is a multiple of
+  // 4, so the byte is (v_opb ^ 64*cb) + k0*ROWB.
+  const int gq = lane >> 4, li = lane & 15;
+  const int vrow = li >> 2;                       // row inside the 4-row gather
+  const int vch = 16 * (gq & 1) + 4 * (li & 3);   // channel inside the 32-channel block
+  uint32_t v_opb = (uint32_t)(vrow * ROWB + 64 * (swz_v<D>(vrow) >> 2) + 16 * (vch >> 3) + 2 * (vch & 7));
+  auto kop = [&](const uint16_t* kl, int ks, int kb) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kl) + ((k_opb ^ (32u * ks)) + kb * 32 * ROWB));
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(&k_lds[buf][klds0 + i * KSTRIDE * KROW]) = kst[i];
-#pragma unroll
-    for (int p = 0; p < VW; ++p) {
-      const int c0 = vcg * CPT + 2 * p;
-      const u32x2 even = {pack_lo16(vst[0][p], vst[1][p]), pack_lo16(vst[2][p], vst[3][p])};
-      const u32x2 odd = {pack_hi16(vst[0][p], vst[1][p]), pack_hi16(vst[2][p], vst[3][p])};
-      *reinterpret_cast<u32x2*>(&v_lds[buf][c0 * VROW + vpos]) = even;
-      *reinterpret_cast<u32x2*>(&v_lds[buf][(c0 + 1) * VROW + vpos]) = odd;
-    }
+  auto vop = [&](const uint16_t* vl, int cb, int st) {
+    // the S^T accumulator layout that P^T comes from: half hf holds keys 4hf..4hf+3 and 8+4hf..8+4hf+3
+    // of each 16-key step
+    const char* base = reinterpret_cast<const char*>(vl) + (v_opb ^ (64u * cb)) + (16 * st + 4 * (gq >> 1)) * ROWB;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)base);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + 8 * ROWB));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
+  // opaque copies of the per-lane bases, taken once per tile, so that the addresses derived from them are
+  // formed next to their use instead of being kept in registers across the loop
+  auto refresh = [&]() { asm volatile("" : "+v"(k_opb), "+v"(v_opb), "+v"(k_dma), "+v"(k_dmx), "+v"(v_dma)); };
 
   // ---- running state of this lane's query row
   f32x16 acc[CB];
@@ -211,133 +240,190 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
   float m_true = neg_inf();  // running max of raw scores over kept tiles (the skip rule's m_{i-1})
   float m_ref = neg_inf();   // reference max of the exponentials (trails m_true by at most 8/c2)
+  float moff = 0.f;          // m_ref * c2 (0 while m_ref = -inf)
   float l_part = 0.f;        // this lane's half of the softmax denominator
   int n_exec = 0;
 
-  auto step = [&](int t, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    const int buf = t & 1;
-    if (t + 1 < T) load_tile(t + 1);
-
-    // S^T for keys t*64 .. t*64+63 (two 32-key blocks) x this wave's 32 query columns.  The two blocks'
-    // MFMA chains alternate k-step by k-step and each k-step's K operands are read from LDS two k-steps
-    // ahead, so neither an MFMA result nor an LDS read is waited for back to back.
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    {
-      const uint16_t* kl = &k_lds[buf][col * KROW + half * 8];
-      auto kop = [&](int kb, int ks) { return *reinterpret_cast<const u32x4*>(kl + kb * 32 * KROW + ks * 16); };
-      u32x4 x[KSTEPS][2];
+  // S^T for keys t*64 .. t*64+63 (two 32-key blocks) x this wave's 32 query columns from the K tile at
+  // `kl`; MFMA j is (k-step j/2, key block j%2): the two chains alternate and each operand is read
+  // AHEAD MFMAs before its use.
+  auto qk = [&](const uint16_t* kl, f32x16 (&s)[2]) {
+    constexpr int NM = 2 * KSTEPS;
+    u32x4 x[NM];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) x[ks][0] = kop(0, ks), x[ks][1] = kop(1, ks);
+    for (int j = 0; j < AHEAD; ++j) x[j] = kop(kl, j >> 1, j & 1);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        if (ks + 2 < KSTEPS) x[ks + 2][0] = kop(0, ks + 2), x[ks + 2][1] = kop(1, ks + 2);
-        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[ks][0]), qreg[ks], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[ks][1]), qreg[ks], s[1], 0, 0, 0);
-      }
+    for (int j = 0; j < NM; ++j) {
+      if (j + AHEAD < NM) x[j + AHEAD] = kop(kl, (j + AHEAD) >> 1, (j + AHEAD) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int ks = j >> 1, kb = j & 1;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[j]), qreg[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
     }
-    if constexpr (MASK) {
-      // key offset o inside the tile is valid for this row iff o <= lim
-      const int key_base = t * kTK;
-      const int lim = !row_ok ? -1 : (a.causal ? iq + off - key_base : Sk - 1 - key_base);
+  };
+  // exponential pair n/2 (n even, P^T operand order) of the scores s
+  auto exp_pair = [&](const f32x16 (&s)[2], uint32_t (&pk)[4][4], int n, float eo) {
+    const int st = n >> 3, e = n & 7;  // 16-key step, position inside it
+    const float p0 = exp2_fast(fmaf(s[st >> 1][8 * (st & 1) + e], c2, -eo));
+    const float p1 = exp2_fast(fmaf(s[st >> 1][8 * (st & 1) + e + 1], c2, -eo));
+    pk[st][e >> 1] = pack_bf16x2(p0, p1);
+    l_part = dot2_bf16_sum(pk[st][e >> 1], l_part);
+  };
+  // keep the exponentials where they are issued (next to the MFMAs they overlap) instead of letting
+  // them sink towards their use one iteration later
+  auto pin = [&](uint32_t (&pk)[4][4]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int st = 0; st < 4; ++st) asm volatile("" ::"v"(pk[st][0]), "v"(pk[st][1]), "v"(pk[st][2]), "v"(pk[st][3]));
+    asm volatile("" : "+v"(l_part));
+  };
+  // O^T += V^T . P^T from the V tile at `vl`; MFMA j is (16-key step j/CB, channel block j%CB).  The
+  // exponentials of the current tile's scores `s` against offset `eo` (into `pk_out`) are spread over
+  // the MFMAs.  One instance per tile serves kept and skipped current tiles (a skipped one uses
+  // eo = +inf: every exponential is exactly 0 and the row sums do not change), so the accumulators keep
+  // a single register home.
+  auto pv = [&](const uint16_t* vl, const uint32_t (&pk)[4][4], float alpha, bool rescale, const f32x16 (&s)[2],
+                float eo, uint32_t (&pk_out)[4][4]) {
+    constexpr int NM = 4 * CB;
+    constexpr int PPM = 16 / NM;  // exponential pairs per MFMA
+    if (rescale) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int o = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          s[kb][i] = o <= lim ? s[kb][i] : neg_inf();
-        }
+      for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
     }
+    bf16x8 vx[NM];
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j) vx[j] = vop(vl, j % CB, j / CB);
+#pragma unroll
+    for (int j = 0; j < NM; ++j) {
+      if (j + AHEAD < NM) vx[j + AHEAD] = vop(vl, (j + AHEAD) % CB, (j + AHEAD) / CB);
+      __builtin_amdgcn_sched_barrier(0);
+      const int st = j / CB, cb = j % CB;
+      const bf16x8 pb = as_bf16x8(u32x4{pk[st][0], pk[st][1], pk[st][2], pk[st][3]});
+      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[j], pb, acc[cb], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < PPM; ++q) exp_pair(s, pk_out, 2 * (j * PPM + q), eo);
+    }
+    pin(pk_out);
+  };
+  // key offset o inside tile t is valid for this row iff o <= lim
+  auto mask = [&](f32x16 (&s)[2], int t) {
+    const int key_base = t * kTK;
+    // offset o = kb*32 + 8*(i/4) + 4*half + i%4; the lane's part 4*half moves into the limit so that
+    // each comparison is against a constant
+    const int lim = (!row_ok ? -1 : (a.causal ? iq + off - key_base : Sk - 1 - key_base)) - 4 * half;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = kb * 32 + 8 * (i >> 2) + (i & 3) <= lim ? s[kb][i] : neg_inf();
+  };
+  auto row_max = [&](const f32x16 (&s)[2]) {
     float mx = neg_inf();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmax3(mx, s[kb][i], s[kb][i + 1]);
-    mx = pair_max(mx);
-
-    // ---- the skip vote against the running max of the kept tiles so far
-    const bool abstain = mx == neg_inf();
-    const float gap = mx - m_true;  // +inf while the row has seen no valid key
-    const uint64_t ball = wave_ballot(!abstain && !(gap < a.tau_raw));
-    if (lane == 0) votes[buf][w] = ball != 0;
-    if (a.unit_gap) {
-      float gg = abstain ? neg_inf() : gap;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) gg = fmaxf(gg, __shfl_xor(gg, off, 64));
-      if (lane == 0) wave_gap[buf][w] = gg;
-    }
-    __syncthreads();
-    bool keep = false;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) keep |= votes[buf][i] != 0;
-    if (tid == 0) {
-      if (a.tile_state) a.tile_state[unit * a.nkt + t] = keep ? 1 : 2;
-      if (a.unit_gap) {
-        float gg = wave_gap[buf][0];
-#pragma unroll
-        for (int i = 1; i < NW; ++i) gg = fmaxf(gg, wave_gap[buf][i]);
-        a.unit_gap[unit * a.nkt + t] = gg == __builtin_inff() ? gg : gg * a.scale;
-      }
-    }
-
-    if (keep) {
-      ++n_exec;
-      // online softmax: advance the true max; move the reference max (and rescale) only when it trails by > 8
-      m_true = fmaxf(m_true, mx);
-      const bool move = (m_true - m_ref) * c2 > kRefSlack;  // also true while m_ref = -inf and m_true finite
-      if (wave_ballot(move)) {
-        const float alpha = move ? exp2_fast((m_ref - m_true) * c2) : 1.f;  // 0 when m_ref = -inf
-        l_part *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
-        m_ref = move ? m_true : m_ref;
-      }
-      const float moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
-      // V^T operands of the first 16-key step, read now so that they land during the exponentials
-      const uint16_t* vl = &v_lds[buf][col * VROW + 8 * half];
-      auto vop = [&](int cb, int st) { return *reinterpret_cast<const u32x4*>(vl + cb * 32 * VROW + 16 * st); };
-      u32x4 vx[4][CB];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) vx[0][cb] = vop(cb, 0);
-      bf16x8 pb[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = exp2_fast(fmaf(s[st >> 1][8 * (st & 1) + e], c2, -moff));
-          const float p1 = exp2_fast(fmaf(s[st >> 1][8 * (st & 1) + e + 1], c2, -moff));
-          pk[e >> 1] = pack_bf16x2(p0, p1);
-          l_part = dot2_bf16_sum(pk[e >> 1], l_part);
-        }
-        pb[st] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-      }
-      // O^T += V^T . P^T: the CB accumulator chains alternate step by step; the next step's operands are
-      // read while the current step's MFMAs issue
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        if (st + 1 < 4)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) vx[st + 1][cb] = vop(cb, st + 1);
-        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vx[st][cb]), pb[st], acc[cb], 0, 0, 0);
-      }
-    }
-    if (t + 1 < T) store_tile(buf ^ 1);
-    __syncthreads();
+    return pair_max(mx);
   };
 
-  load_tile(0);
-  store_tile(0);
-  // every load issued so far (Q operand, tile 0) has landed: without this the wait-count pass treats
-  // the Q registers as pending inside the loop and stalls each QK^T MFMA on the next tile's prefetch
-  wait_vmem_all();
-  __syncthreads();
-  for (int t = 0; t < T_in; ++t) step(t, false_type{});
-  for (int t = T_in; t < T; ++t) step(t, true_type{});
+  // ---- one iteration per key tile t (parity P = t & 1, known at compile time):
+  //  (1) S(t) = K(t) Q^T; row max; the skip vote against the running max of the kept tiles so far
+  //      (tau <= 0: the prefix max); wait for this wave's loads of the previous iteration; barrier;
+  //  (2) the unit's decision; statistics; online-softmax update (the output factor is applied before
+  //      the next P.V, after the previous one);
+  //  (3) loads of K(t+2) into K(t)'s buffer and, if the tile is kept, of V(t) into V(t-2)'s;
+  //  (4) the exponentials of tile t (if kept) spread over the P.V MFMAs of tile t-1 (if kept).
+  // The barrier of iteration t makes the loads issued in iteration t-1 (K(t+1), V(t-1)) visible and
+  // ends every read of the buffers that iteration t's loads replace (K(t) in step 1 of this iteration,
+  // V(t-2) in step 4 of the previous one).
+  uint32_t pka[4][4], pkb[4][4];
+  bool keep_prev = false;  // tile t-1 was kept: its P.V is pending
+  float alpha_prev = 1.f;  // output factor to apply before that P.V
+  bool resc_prev = false;
+  auto iteration = [&](int t, uint32_t (&pk_cur)[4][4], uint32_t (&pk_prev)[4][4], auto parity) {
+    constexpr int P = decltype(parity)::value ? 1 : 0;
+    uint16_t* k_cur = P ? k_lds1 : k_lds0;
+    uint16_t* v_cur = P ? v_lds1 : v_lds0;
+    const uint16_t* v_prev = P ? v_lds0 : v_lds1;
+    f32x16 s[2];
+    bool keep = false;
+    float alpha = 1.f;
+    bool resc = false;
+    if (t < T) {
+      refresh();
+      qk(k_cur, s);
+      if (t >= T_in) mask(s, t);
+      const float mx = row_max(s);
+      const int vb = t & 1;
+      {
+        const bool abstain = mx == neg_inf();
+        const float gap = mx - m_true;  // +inf while the row has seen no valid key
+        const uint64_t ball = wave_ballot(!abstain && !(gap < a.tau_raw));
+        if (lane == 0) votes[vb][w] = ball != 0;
+        if (a.unit_gap) {
+          float gg = abstain ? neg_inf() : gap;
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) gg = fmaxf(gg, __shfl_xor(gg, o, 64));
+          if (lane == 0) wave_gap[vb][w] = gg;
+        }
+      }
+      wait_vmem_all();
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NW; ++i) keep |= votes[vb][i] != 0;
+      if (tid == 0) {
+        if (a.tile_state) a.tile_state[unit * a.nkt + t] = keep ? 1 : 2;
+        if (a.unit_gap) {
+          float gg = wave_gap[vb][0];
+#pragma unroll
+          for (int i = 1; i < NW; ++i) gg = fmaxf(gg, wave_gap[vb][i]);
+          a.unit_gap[unit * a.nkt + t] = gg == __builtin_inff() ? gg : gg * a.scale;
+        }
+      }
+      if (t + 2 < T) load_k(k_cur, t + 2);
+      if (keep) {
+        load_v(v_cur, t);
+        ++n_exec;
+        // advance the true max; move the reference max only when it trails by > 8
+        m_true = fmaxf(m_true, mx);
+        const bool move = (m_true - m_ref) * c2 > kRefSlack;  // also true while m_ref = -inf and m_true finite
+        alpha = move ? exp2_fast((m_ref - m_true) * c2) : 1.f;  // 0 when m_ref = -inf
+        resc = wave_ballot(move) != 0;
+        l_part *= alpha;
+        m_ref = move ? m_true : m_ref;
+        moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+      }
+    } else {
+      // past the last tile: only the pending P.V; its V tile was loaded in the previous iteration
+      wait_vmem_all();
+      __syncthreads();
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+    }
+    // exponentials of a skipped tile use offset +inf: exactly 0, so they add nothing to the row sums and
+    // give the zero P^T that the next tile's P.V must not accumulate
+    // the P.V of the previous tile (if kept) with this tile's exponentials between its MFMAs, else this
+    // tile's exponentials alone
+    if (keep_prev) {
+      pv(v_prev, pk_prev, alpha_prev, resc_prev, s, keep ? moff : __builtin_inff(), pk_cur);
+    } else if (keep) {
+#pragma unroll
+      for (int n = 0; n < 32; n += 2) exp_pair(s, pk_cur, n, moff);
+      pin(pk_cur);
+    }
+    keep_prev = keep;
+    alpha_prev = alpha;
+    resc_prev = resc;
+  };
+
+  if (T > 0) {
+    load_k(k_lds0, 0);
+    if (T > 1) load_k(k_lds1, 1);
+    wait_vmem_all();  // Q and the first key tiles
+    __syncthreads();
+    // iterations t = 0 .. T; iteration T only completes the P.V of tile T-1
+    for (int t = 0; t <= T; t += 2) {
+      iteration(t, pka, pkb, false_type{});
+      if (t + 1 <= T) iteration(t + 1, pkb, pka, true_type{});
+    }
+  }
 
   // ---- epilogue: O = acc / l, bf16
   const float l_tot = pair_sum(l_part);
@@ -348,10 +434,10 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int ch = cb * 32 + 8 * gq + 4 * half;
-        const u32x2 x = {pack_bf16x2(acc[cb][4 * gq] * inv, acc[cb][4 * gq + 1] * inv),
-                         pack_bf16x2(acc[cb][4 * gq + 2] * inv, acc[cb][4 * gq + 3] * inv)};
+      for (int gq4 = 0; gq4 < 4; ++gq4) {
+        const int ch = cb * 32 + 8 * gq4 + 4 * half;
+        const u32x2 x = {pack_bf16x2(acc[cb][4 * gq4] * inv, acc[cb][4 * gq4 + 1] * inv),
+                         pack_bf16x2(acc[cb][4 * gq4 + 2] * inv, acc[cb][4 * gq4 + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + ch) = x;
       }
   }
