@@ -21,6 +21,7 @@ import argparse
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -59,6 +60,15 @@ def recorded_traffic(path_kind):
     except (OSError, KeyError, ValueError):
         return None
     return rec["bytes_per_launch"] if rec.get("source_sha256") == sources_sha(path_kind) else None
+
+
+def recorded_mfma_ceiling():
+    """Random-operand MFMA rate recorded in profiles/mfma_ceiling.json (None if absent)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "mfma_ceiling.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        return json.load(f).get("random_operands_tflops")
 
 
 def summarize_traffic(fetch_dir, write_dir, command):
@@ -341,10 +351,17 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output directories and exit")
     ap.add_argument("--traffic-command", default="", help="command line recorded with --summarize-traffic")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="run the standalone MFMA-rate program (zero vs random bf16 operands), print its JSON and exit")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.traffic_command)
         return
+    if args.mfma_ceiling:
+        exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_flash_amd", "mfma_ceiling")
+        if not os.path.exists(exe):
+            sys.exit(f"{exe} is missing: build with `python -m long_context_flash_amd.build`")
+        sys.exit(subprocess.run([exe]).returncode)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
@@ -447,6 +464,13 @@ def main():
                            "traffic": recorded_traffic("prefill"), "kernel": PREFILL_KERNEL,
                            "per_launch_flop": executed, "note": "executed = 2*128*64*128 FLOP per visited "
                            "tile (QK^T) + the same per kept tile (PV)"}
+        ceiling = recorded_mfma_ceiling()
+        if ceiling:
+            # the rate this GPU sustains on random bf16 operands (power-limited clock), recorded by
+            # `bench.py --mfma-ceiling`; reported beside the published peak, which stays the roofline's peak
+            res["roofline"]["measured_ceiling"] = {
+                "random_operands_tflops": ceiling, "frac": round(executed / t / 1e12 / ceiling, 4),
+                "source": "profiles/mfma_ceiling.json"}
     if run_prefill and not args.main_only:
         res["prefill_chunked_paged"] = time_chunked_prefill(ssm, torch, np, pw, pdata, tau_p, args.steps, dev)
     if run_decode:

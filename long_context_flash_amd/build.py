@@ -14,6 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm.so")
 SOURCES = ["prefill.hip", "decode.hip", "ssm_api.cpp"]
+# standalone measurement program (not linked into the library): the MFMA rate with zero and random operands
+CEILING = os.path.join(HERE, "mfma_ceiling")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 vector ops (v_pk_*_f32).
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -51,6 +53,11 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [cc, *HIPCC_FLAGS, os.path.join(CSRC, "mfma_ceiling.hip"), "-o", CEILING + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for mfma_ceiling.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(CEILING + ".tmp", CEILING)
     return LIB
 
 
