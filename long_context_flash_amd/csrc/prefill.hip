@@ -247,8 +247,11 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   // S^T for keys t*64 .. t*64+63 (two 32-key blocks) x this wave's 32 query columns from the K tile at
   // `kl`; MFMA j is (k-step j/2, key block j%2): the two chains alternate and each operand is read
   // AHEAD MFMAs before its use.
+  // Both MFMA streams (QK^T and P.V) raise the wave's issue priority: of the two waves sharing a SIMD,
+  // the one with MFMAs to issue goes first and the other's VALU work fills the MFMA shadow.
   auto qk = [&](const uint16_t* kl, f32x16 (&s)[2]) {
     constexpr int NM = 2 * KSTEPS;
+    __builtin_amdgcn_s_setprio(1);
     u32x4 x[NM];
 #pragma unroll
     for (int j = 0; j < AHEAD; ++j) x[j] = kop(kl, j >> 1, j & 1);
@@ -259,6 +262,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
       const int ks = j >> 1, kb = j & 1;
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[j]), qreg[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // exponential pair n/2 (n even, P^T operand order) of the scores s
   auto exp_pair = [&](const f32x16 (&s)[2], uint32_t (&pk)[4][4], int n, float eo) {
@@ -288,6 +292,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
     }
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 vx[NM];
 #pragma unroll
     for (int j = 0; j < AHEAD; ++j) vx[j] = vop(vl, j % CB, j / CB);
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
       for (int q = 0; q < PPM; ++q) exp_pair(s, pk_out, 2 * (j * PPM + q), eo);
     }
     pin(pk_out);
+    __builtin_amdgcn_s_setprio(0);
   };
   // key offset o inside tile t is valid for this row iff o <= lim
   auto mask = [&](f32x16 (&s)[2], int t) {
