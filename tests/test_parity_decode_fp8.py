@@ -65,3 +65,31 @@ def test_decode_128k_paged_sampled():
         r = check_decode(data, tau=tau, num_splits=w.num_splits, paged=True, batches=np.array([2, 17, 29]), fp8=f8,
                          where=f"fp8 128k tau={tau}")
         log(f"fp8 128k tau={tau}: sparsity {r['sparsity']:.3f}")
+
+
+def test_every_value_code_exact():
+    """Each finite e4m3 code reaches the output exactly: one key per sequence (its softmax weight is 1), V rows
+    holding all 254 finite codes (the two NaN codes replaced by 0), scale 1.  The output in bf16 must equal
+    torch's float8_e4m3fn decoding of the code, which bf16 represents exactly."""
+    import torch
+    import long_context_flash_amd as ssm
+    B, Hq, Hkv, d = 2, 8, 1, 128
+    codes = np.arange(256, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    v = np.zeros((B, Hkv, 64, d), np.uint8)
+    v[:, 0, 0, :] = codes.reshape(B, d)
+    k = np.zeros((B, Hkv, 64, d), np.uint8)
+    rng = np.random.default_rng(7)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32))
+    dev = "cuda"
+    vc = torch.from_numpy(v).to(dev).view(torch.float8_e4m3fn)
+    kc = torch.from_numpy(k).to(dev).view(torch.float8_e4m3fn)
+    lens = torch.ones(B, dtype=torch.int32, device=dev)
+    for P in (1, 16):
+        out = ssm.ssm_decode(ssm.bf16_from_bits(q, dev), kc, vc, lens, tau=-LN1000, num_splits=P, k_scale=1.0,
+                             v_scale=1.0)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        want = torch.from_numpy(codes.reshape(B, d)).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+        for h in range(Hq):
+            assert np.array_equal(got[:, h, :], want), f"P={P} head {h}: {np.argwhere(got[:, h, :] != want)[:8]}"
