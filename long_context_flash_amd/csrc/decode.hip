@@ -59,7 +59,7 @@ __device__ __forceinline__ rsrc_t decode_tile_rsrc(const void* pool, const int32
   int64_t elem;
   if (pages) {
     // the page id is wave-uniform: keep it (and the resource) in scalar registers
-    const int pg = __builtin_amdgcn_readfirstlane(pages[(int64_t)b * max_pages + t]);
+    const int pg = __builtin_amdgcn_readfirstlane(load_uniform_i32(pages, (int64_t)b * max_pages + t));
     if (pg < 0 || pg >= pool_pages) return make_rsrc(pool, 0u);
     elem = (int64_t)pg * sb + (int64_t)g * sh;
   } else {

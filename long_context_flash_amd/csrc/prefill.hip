@@ -152,7 +152,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   // chunked: the resource of key tile t of this KV head (rows past Sk and bad page ids read as zero)
   auto page_rsrc = [&](const uint16_t* pool, const int32_t* pages, int64_t pool_pages, int64_t sb, int64_t sh,
                        int64_t ss, int t) {
-    const int pg = __builtin_amdgcn_readfirstlane(pages[(int64_t)b * a.max_pages + t]);
+    const int pg = __builtin_amdgcn_readfirstlane(load_uniform_i32(pages, (int64_t)b * a.max_pages + t));
     if (pg < 0 || pg >= pool_pages) return make_rsrc(pool, 0u);
     return make_rsrc(pool + (int64_t)pg * sb + (int64_t)g * sh, rows_bytes(min(kTK, Sk - t * kTK), ss, D));
   };

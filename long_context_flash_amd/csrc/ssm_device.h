@@ -60,6 +60,14 @@ __device__ __forceinline__ float dot2_bf16_sum(uint32_t pk, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
 }
 
+// Wave-uniform read of p[i] from memory the kernel never writes (page tables, sequence lengths), through
+// the constant address space: the compiler emits a scalar load, counted apart from the vector loads, so
+// the read does not wait for the tile loads already in flight (a vector load would need vmcnt(0)).
+__device__ __forceinline__ int load_uniform_i32(const int32_t* p, int64_t i) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  return ((cptr)p)[i];
+}
+
 // ---- buffer loads: a resource covers [base, base + num_bytes); dwords outside read as 0.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data format)
