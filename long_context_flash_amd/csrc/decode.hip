@@ -33,6 +33,9 @@
 // scale per tensor.  Half the bytes of a bf16 cache are read; each code is
 // converted exactly to bf16 in registers and the same bf16 MFMAs run.  The key
 // scale is folded into the logit scale, the value scale into the split output.
+// The QK^T contraction takes the channels in an order where each lane's 16-byte
+// key load holds two k-steps, so a key row is fetched in 64-byte pieces as for
+// bf16 (8-byte loads fetch 32-byte pieces and cap the read rate well below HBM's).
 //
 // Sink-seeded split-K (optional): a split after the first starts its prefix
 // maximum at key tile 0's per-query maxima instead of -inf; each wave scores
@@ -157,19 +160,24 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     return;
   }
 
-  // Q^T operand: lane (qc, grp) holds Q[qc][ks*32 + grp*8 .. +8]; columns >= G are zero
+  // Channel order of the QK^T contraction: k-step ks, lane group grp, element e covers channel
+  // ks*32 + grp*8 + e for a bf16 cache, and (ks/2)*64 + grp*16 + (ks%2)*8 + e for an fp8 cache, so that one
+  // 16-byte load per lane brings two k-steps of fp8 codes and a key row is read in 64-byte pieces (any
+  // order of the channels gives the same dot products; Q and K use the same one).
+  auto chan = [&](int ks) { return ES == 2 ? ks * 32 + grp * 8 : (ks >> 1) * 64 + grp * 16 + (ks & 1) * 8; };
+  // Q^T operand: lane (qc, grp) holds Q[qc][chan(ks) .. +8]; columns >= G are zero
   bf16x8 qreg[KS];
   {
     const rsrc_t rq = make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)g * G * a.q_sh, rows_bytes(G, a.q_sh, D));
-    const uint32_t qoff = qc < G ? (uint32_t)(qc * a.q_sh * 2 + grp * 16) : 0xffffffffu;
+    const uint32_t qoff = qc < G ? (uint32_t)(qc * a.q_sh * 2) : 0xffffffffu;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(buffer_load_16(rq, qc < G ? qoff + ks * 64 : qoff));
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(buffer_load_16(rq, qc < G ? qoff + chan(ks) * 2 : qoff));
   }
 
   // lane offsets inside a tile (bytes), fixed for the whole scan
-  uint32_t kvo[4];  // K: row kb*16 + qc, channels grp*8 + ks*32 (+ ks*32*ES bytes as an immediate)
+  uint32_t kvo[4];  // K: row kb*16 + qc, channel chan(0) (the other k-steps add immediates)
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) kvo[kb] = (uint32_t)(((kb * 16 + qc) * a.k_ss + grp * 8) * ES);
+  for (int kb = 0; kb < 4; ++kb) kvo[kb] = (uint32_t)(((kb * 16 + qc) * a.k_ss + chan(0)) * ES);
   // V: lane (m = qc, grp) loads keys st*32 + 16*(e/4) + 4*grp + (e%4), channels 8m .. 8m+7 (zero for 8m >= D)
   const bool v_ch_ok = qc * 8 < D;
   uint32_t vvo[2][2];
@@ -182,8 +190,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
 
   const int nchunks = (s_end - s_begin + kDecWaves - 1) / kDecWaves;
   // A operand of the QK^T MFMAs, key block kb, k-step ks: bf16 as loaded, or fp8 codes converted at use
-  u32x4 kreg[4][KS];
-  u32x2 kraw[4][KS];
+  u32x4 kreg[4][KS];       // bf16: one k-step per register
+  u32x4 kraw[4][KS / 2];   // fp8: k-steps 2j and 2j+1 in register j (bytes 0-7 and 8-15)
   auto load_k = [&](int t) {
     const rsrc_t r = decode_tile_rsrc<ES>(a.k, a.k_pages, a.k_max_pages, k_pool_pages, a.k_sb, a.k_sh, a.k_ss, b, g,
                                           t, len, D);
@@ -192,12 +200,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if constexpr (ES == 2) kreg[kb][ks] = buffer_load_16(r, kvo[kb] + ks * 64);
-        else kraw[kb][ks] = buffer_load_8(r, kvo[kb] + ks * 32);
+        else if (ks % 2 == 0) kraw[kb][ks / 2] = buffer_load_16(r, kvo[kb] + ks * 32);
       }
   };
   auto k_operand = [&](int kb, int ks) {
     if constexpr (ES == 2) return as_bf16x8(kreg[kb][ks]);
-    else return as_bf16x8(fp8x8_to_bf16x8(kraw[kb][ks]));
+    else return as_bf16x8(fp8x8_to_bf16x8(u32x2{kraw[kb][ks / 2][2 * (ks % 2)], kraw[kb][ks / 2][2 * (ks % 2) + 1]}));
   };
   u32x4 vreg[2][8];  // 8 key rows x 8 channels per st (bf16), converted from vraw for an fp8 cache
   u32x2 vraw[2][8];
