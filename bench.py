@@ -62,13 +62,22 @@ def recorded_traffic(path_kind):
     return rec["bytes_per_launch"] if rec.get("source_sha256") == sources_sha(path_kind) else None
 
 
-def recorded_mfma_ceiling():
-    """Random-operand MFMA rate recorded in profiles/mfma_ceiling.json (None if absent)."""
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "mfma_ceiling.json")
+def _recorded(name, key):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        return json.load(f).get("random_operands_tflops")
+        return json.load(f).get(key)
+
+
+def recorded_mfma_ceiling():
+    """Random-operand MFMA rate recorded in profiles/mfma_ceiling.json (None if absent)."""
+    return _recorded("mfma_ceiling.json", "random_operands_tflops")
+
+
+def recorded_read_ceiling():
+    """Best streaming-read rate of the decode's load shapes recorded in profiles/read_ceiling.json (None if absent)."""
+    return _recorded("read_ceiling.json", "best_gbps")
 
 
 def summarize_traffic(fetch_dir, write_dir, command):
@@ -353,12 +362,16 @@ def main():
     ap.add_argument("--traffic-command", default="", help="command line recorded with --summarize-traffic")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="run the standalone MFMA-rate program (zero vs random bf16 operands), print its JSON and exit")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="run the standalone HBM streaming-read program (the decode's load shapes), print its JSON "
+                         "and exit")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.traffic_command)
         return
-    if args.mfma_ceiling:
-        exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_flash_amd", "mfma_ceiling")
+    if args.mfma_ceiling or args.read_ceiling:
+        exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_flash_amd",
+                           "mfma_ceiling" if args.mfma_ceiling else "read_ceiling")
         if not os.path.exists(exe):
             sys.exit(f"{exe} is missing: build with `python -m long_context_flash_amd.build`")
         sys.exit(subprocess.run([exe]).returncode)
@@ -499,6 +512,13 @@ def main():
                                   "traffic": recorded_traffic("decode"),
                                   "kernel": f"{DECODE_SPLIT_KERNEL} + {DECODE_COMBINE_KERNEL}",
                                   "per_launch_bytes": kb + vk + small}
+        read_ceiling = recorded_read_ceiling()
+        if read_ceiling:
+            # the best rate at which this GPU streams reads in the decode's load shapes (no compute), recorded by
+            # `bench.py --read-ceiling`; reported beside the published peak, which stays the roofline's peak
+            res["roofline_decode"]["measured_ceiling"] = {
+                "read_gbps": read_ceiling, "frac": round((kb + vk + small) / t / 1e9 / read_ceiling, 4),
+                "source": "profiles/read_ceiling.json"}
         if "value" not in res:
             res["value"] = res["decode_kv_gbps"]
             res["unit"] = "GB/s"
@@ -509,6 +529,10 @@ def main():
         res["decode_fp8_kv"] = time_fp8_decode(ssm, torch, np, dw, ddata, dq, kp, vp, pt, lens, dout, ws, dstate, tau_d,
                                                args.steps, dev)
         res["decode_fp8_kv"]["speedup_vs_bf16"] = round(res["decode_ms"] / res["decode_fp8_kv"]["ms"], 3)
+        read_ceiling = recorded_read_ceiling()
+        if read_ceiling:
+            for leg in ("decode_sink_seeded", "decode_fp8_kv"):
+                res[leg]["read_ceiling_frac"] = round(res[leg]["total_gbps"] / read_ceiling, 4)
     res["config"] = cfg
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)

@@ -14,8 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm.so")
 SOURCES = ["prefill.hip", "decode.hip", "ssm_api.cpp"]
-# standalone measurement program (not linked into the library): the MFMA rate with zero and random operands
-CEILING = os.path.join(HERE, "mfma_ceiling")
+# standalone measurement programs (not linked into the library): the MFMA rate with zero and random operands,
+# and the HBM streaming-read rate in the decode's load shapes
+PROGRAMS = ["mfma_ceiling", "read_ceiling"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 vector ops (v_pk_*_f32).
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -53,11 +54,17 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
-    cmd = [cc, *HIPCC_FLAGS, os.path.join(CSRC, "mfma_ceiling.hip"), "-o", CEILING + ".tmp"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for mfma_ceiling.hip:\n{r.stdout}\n{r.stderr}")
-    os.replace(CEILING + ".tmp", CEILING)
+
+    def build_program(name):
+        exe = os.path.join(HERE, name)
+        cmd = [cc, *HIPCC_FLAGS, os.path.join(CSRC, name + ".hip"), "-o", exe + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {name}.hip:\n{r.stdout}\n{r.stderr}")
+        os.replace(exe + ".tmp", exe)
+
+    with ThreadPoolExecutor(max_workers=len(PROGRAMS)) as ex:
+        list(ex.map(build_program, PROGRAMS))
     return LIB
 
 
