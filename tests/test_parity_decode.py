@@ -66,3 +66,25 @@ def test_decode_128k_paged_sampled():
     batches = np.array([0, 7, 19, 31])
     for tau in w.taus:
         check_decode(data, tau=tau, num_splits=w.num_splits, paged=True, batches=batches, where=f"128k tau={tau}")
+
+
+def test_batch_beyond_dispatch_sort():
+    """Batches above 1024 sequences skip the longest-first dispatch order (plain workgroup order): the outputs
+    of such a batch equal those of the same sequences run as a batch of 1024 (sorted order) bit for bit, and a
+    sample of its sequences (both sides of the 1024 boundary) agrees with the oracle."""
+    import torch
+    import long_context_flash_amd as ssm
+    B = 1100
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 400, size=B).astype(np.int32)
+    w = _small(B=B, Hq=8, Hkv=1, d=64, seed=77)
+    data = synth.gen_decode(w, kv_lens=lens, contiguous=True, paged=False)
+    sample = np.array([0, 1, 500, 1022, 1023, 1024, 1025, 1099])
+    r = check_decode(data, tau=-LN1000, num_splits=4, paged=False, batches=sample, where="B=1100 unsorted dispatch")
+    dev = "cuda"
+    q = ssm.bf16_from_bits(data["q"][:1024], dev)
+    kc = ssm.bf16_from_bits(data["k_cache"][:1024], dev)
+    vc = ssm.bf16_from_bits(data["v_cache"][:1024], dev)
+    out = ssm.ssm_decode(q, kc, vc, torch.from_numpy(lens[:1024]).to(dev), tau=-LN1000, num_splits=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), r["out"][:1024]), "dispatch order changed the outputs"
