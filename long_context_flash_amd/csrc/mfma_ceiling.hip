@@ -3,7 +3,9 @@
 // chip's clock depends on its power draw, which depends on the operand bits, so the second figure is the
 // practical ceiling for a kernel that multiplies real data; the first approaches the published peak.
 //
-// Standalone measurement program (not part of libssm.so).  Prints one JSON line.
+// Standalone measurement program (not part of libssm.so).  Prints one JSON line.  It also times the VALU
+// rate of v_fma_f32 and of v_exp_f32 (the exponential of the softmax step) followed by an add, and reports
+// how many fma issue slots one exponential with its add takes.
 //   mfma_ceiling [iterations]
 //
 // Each of 512 workgroups (two per compute unit, four waves each, i.e. two waves per SIMD, the occupancy
@@ -53,6 +55,23 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_loop(const u32x4* __restrict
   out[tid] = r;
 }
 
+// VALU issue rate of one instruction kind: 8 independent chains per lane, OP 0 = v_fma_f32, 1 = v_exp_f32
+// (each exponential followed by one v_add_f32 that keeps its argument in range)
+template <int OP>
+__global__ __launch_bounds__(256) void valu_loop(float* __restrict__ out, int iters) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (float)(threadIdx.x + i) * 1e-6f - 1.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = OP == 0 ? __builtin_fmaf(a[i], 0.999f, -0.001f) : __builtin_amdgcn_exp2f(a[i]) - 1.5f;
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r += a[i];
+  out[blockIdx.x * 256 + threadIdx.x] = r;
+}
+
 #define CHECK(x)                                                                        \
   do {                                                                                  \
     const hipError_t e_ = (x);                                                          \
@@ -81,6 +100,29 @@ double rate(const u32x4* src, float* out, int iters) {
   CHECK(hipEventDestroy(e1));
   const double waves = (double)kGrid * kThreads / 64;
   return waves * iters * kMfmaPerIter * kFlopPerMfma / (ms * 1e-3) / 1e12;
+}
+
+// wave instructions per second per SIMD of valu_loop<OP> (OP 1 counts the exponential and its add as two)
+template <int OP>
+double valu_rate(float* out, int num_simds) {
+  const int grid = 2048, iters = 4096;
+  hipLaunchKernelGGL(valu_loop<OP>, dim3(grid), dim3(256), 0, 0, out, 16);
+  CHECK(hipGetLastError());
+  CHECK(hipDeviceSynchronize());
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  CHECK(hipEventRecord(e0, 0));
+  hipLaunchKernelGGL(valu_loop<OP>, dim3(grid), dim3(256), 0, 0, out, iters);
+  CHECK(hipGetLastError());
+  CHECK(hipEventRecord(e1, 0));
+  CHECK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  const double insts = (double)grid * 4 * iters * 8 * (OP == 0 ? 1 : 2);
+  return insts / num_simds / (ms * 1e-3);
 }
 
 // SplitMix64 (Steele, Lea, Flood 2014), used here only to fill operand registers with varied bits
@@ -122,10 +164,16 @@ int main(int argc, char** argv) {
     z = rz > z ? rz : z;
     r = rr > r ? rr : r;
   }
+  // VALU: the exponential's cost relative to an fma follows from the two rates (the clock is the same)
+  int dev = 0, num_cus = 0;
+  CHECK(hipGetDevice(&dev));
+  CHECK(hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev));
+  const double fma_rate = valu_rate<0>(out, num_cus * 4), pair_rate = valu_rate<1>(out, num_cus * 4) / 2.0;
   std::printf("{\"instruction\": \"v_mfma_f32_32x32x16_bf16\", \"zero_operands_tflops\": %.1f, "
               "\"random_operands_tflops\": %.1f, \"published_peak_tflops\": 2500.0, \"workgroups\": %d, "
-              "\"waves_per_simd\": 2, \"iterations\": %d}\n",
-              z, r, kGrid, iters);
+              "\"waves_per_simd\": 2, \"iterations\": %d, \"valu_fma_f32_per_us_per_simd\": %.1f, "
+              "\"valu_exp_f32_plus_add_per_us_per_simd\": %.1f, \"exp_plus_add_in_fma_times\": %.2f}\n",
+              z, r, kGrid, iters, fma_rate * 1e-6, pair_rate * 1e-6, fma_rate / pair_rate);
   CHECK(hipFree(zero));
   CHECK(hipFree(rnd));
   CHECK(hipFree(out));
