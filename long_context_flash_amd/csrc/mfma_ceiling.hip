@@ -22,6 +22,7 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -46,6 +47,35 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_loop(const u32x4* __restrict
       acc[(2 * j + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[(j + 3) & 7]),
                                                                      __builtin_bit_cast(bf16x8, b[j]), acc[(2 * j + 1) & 3], 0, 0, 0);
     }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += acc[c][i];
+  out[tid] = r;
+}
+
+// the same with v_mfma_f32_32x32x64_f8f6f4 on OCP e4m3 operands (32 bytes per lane and operand): four A and
+// four B operands from the same 16 registers, 8 MFMAs per iteration on four chains
+constexpr double kFlopPerMfmaF8 = 2.0 * 32 * 32 * 64;
+__global__ __launch_bounds__(kThreads, 2) void mfma_loop_f8(const u32x4* __restrict__ src, float* __restrict__ out,
+                                                            int iters) {
+  const int tid = blockIdx.x * kThreads + threadIdx.x;
+  i32x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 lo = src[(size_t)tid * kOps + 2 * i], hi = src[(size_t)tid * kOps + 2 * i + 1];
+    const u32x4 lo2 = src[(size_t)tid * kOps + 8 + 2 * i], hi2 = src[(size_t)tid * kOps + 9 + 2 * i];
+    a[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    b[i] = i32x8{(int)lo2[0], (int)lo2[1], (int)lo2[2], (int)lo2[3], (int)hi2[0], (int)hi2[1], (int)hi2[2], (int)hi2[3]};
+  }
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[j & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 3], b[(j + (j >> 2)) & 3], acc[j & 3], 0, 0, 0, 0,
+                                                                   0, 0);
   }
   float r = 0.f;
 #pragma unroll
@@ -81,16 +111,20 @@ __global__ __launch_bounds__(256) void valu_loop(float* __restrict__ out, int it
     }                                                                                   \
   } while (0)
 
-// TFLOP/s of one timed launch (after one short warm-up launch) over the operands at `src`
-double rate(const u32x4* src, float* out, int iters) {
-  hipLaunchKernelGGL(mfma_loop, dim3(kGrid), dim3(kThreads), 0, 0, src, out, 64);
+// TFLOP/s of one timed launch (after one short warm-up launch) over the operands at `src`; f8: the fp8 loop
+double rate(const u32x4* src, float* out, int iters, bool f8 = false) {
+  auto launch = [&](int n) {
+    if (f8) hipLaunchKernelGGL(mfma_loop_f8, dim3(kGrid), dim3(kThreads), 0, 0, src, out, n);
+    else hipLaunchKernelGGL(mfma_loop, dim3(kGrid), dim3(kThreads), 0, 0, src, out, n);
+  };
+  launch(64);
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
   CHECK(hipEventRecord(e0, 0));
-  hipLaunchKernelGGL(mfma_loop, dim3(kGrid), dim3(kThreads), 0, 0, src, out, iters);
+  launch(iters);
   CHECK(hipGetLastError());
   CHECK(hipEventRecord(e1, 0));
   CHECK(hipEventSynchronize(e1));
@@ -99,7 +133,8 @@ double rate(const u32x4* src, float* out, int iters) {
   CHECK(hipEventDestroy(e0));
   CHECK(hipEventDestroy(e1));
   const double waves = (double)kGrid * kThreads / 64;
-  return waves * iters * kMfmaPerIter * kFlopPerMfma / (ms * 1e-3) / 1e12;
+  return f8 ? waves * iters * 8 * kFlopPerMfmaF8 / (ms * 1e-3) / 1e12
+            : waves * iters * kMfmaPerIter * kFlopPerMfma / (ms * 1e-3) / 1e12;
 }
 
 // wave instructions per second per SIMD of valu_loop<OP> (OP 1 counts the exponential and its add as two)
@@ -151,18 +186,34 @@ int main(int argc, char** argv) {
     }
     host[i] = w;
   }
-  u32x4 *zero = nullptr, *rnd = nullptr;
+  // random OCP e4m3 codes for the fp8 loop (the two NaN codes replaced by the largest finite ones)
+  std::vector<uint32_t> host8(n * 4);
+  for (size_t i = 0; i < host8.size(); ++i) {
+    uint32_t w = 0;
+    for (int h = 0; h < 4; ++h) {
+      uint32_t c = (uint32_t)(splitmix64(state) >> 56);
+      if ((c & 0x7F) == 0x7F) c -= 1;
+      w |= c << (8 * h);
+    }
+    host8[i] = w;
+  }
+  u32x4 *zero = nullptr, *rnd = nullptr, *rnd8 = nullptr;
   float* out = nullptr;
   CHECK(hipMalloc(&zero, n * sizeof(u32x4)));
   CHECK(hipMalloc(&rnd, n * sizeof(u32x4)));
+  CHECK(hipMalloc(&rnd8, n * sizeof(u32x4)));
+  CHECK(hipMemcpy(rnd8, host8.data(), n * sizeof(u32x4), hipMemcpyHostToDevice));
   CHECK(hipMalloc(&out, (size_t)kGrid * kThreads * sizeof(float)));
   CHECK(hipMemset(zero, 0, n * sizeof(u32x4)));
   CHECK(hipMemcpy(rnd, host.data(), n * sizeof(u32x4), hipMemcpyHostToDevice));
-  double z = 0, r = 0;
+  double z = 0, r = 0, z8 = 0, r8 = 0;
   for (int rep = 0; rep < 2; ++rep) {  // the better of two runs each
     const double rz = rate(zero, out, iters), rr = rate(rnd, out, iters);
+    const double rz8 = rate(zero, out, iters, true), rr8 = rate(rnd8, out, iters, true);
     z = rz > z ? rz : z;
     r = rr > r ? rr : r;
+    z8 = rz8 > z8 ? rz8 : z8;
+    r8 = rr8 > r8 ? rr8 : r8;
   }
   // VALU: the exponential's cost relative to an fma follows from the two rates (the clock is the same)
   int dev = 0, num_cus = 0;
@@ -172,10 +223,13 @@ int main(int argc, char** argv) {
   std::printf("{\"instruction\": \"v_mfma_f32_32x32x16_bf16\", \"zero_operands_tflops\": %.1f, "
               "\"random_operands_tflops\": %.1f, \"published_peak_tflops\": 2500.0, \"workgroups\": %d, "
               "\"waves_per_simd\": 2, \"iterations\": %d, \"valu_fma_f32_per_us_per_simd\": %.1f, "
-              "\"valu_exp_f32_plus_add_per_us_per_simd\": %.1f, \"exp_plus_add_in_fma_times\": %.2f}\n",
-              z, r, kGrid, iters, fma_rate * 1e-6, pair_rate * 1e-6, fma_rate / pair_rate);
+              "\"valu_exp_f32_plus_add_per_us_per_simd\": %.1f, \"exp_plus_add_in_fma_times\": %.2f, "
+              "\"fp8\": {\"instruction\": \"v_mfma_f32_32x32x64_f8f6f4\", \"zero_operands_tflops\": %.1f, "
+              "\"random_operands_tflops\": %.1f, \"published_peak_tflops\": 5000.0}}\n",
+              z, r, kGrid, iters, fma_rate * 1e-6, pair_rate * 1e-6, fma_rate / pair_rate, z8, r8);
   CHECK(hipFree(zero));
   CHECK(hipFree(rnd));
+  CHECK(hipFree(rnd8));
   CHECK(hipFree(out));
   return 0;
 }
