@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 enum {
   SSM_OK = 0,
@@ -54,7 +54,7 @@ enum { SSM_BF16 = 0, SSM_FP32 = 1, SSM_FP8_E4M3 = 2 /* OCP 8-bit float, 4 expone
  * 16-byte pieces. */
 typedef struct {
   void* data;
-  int32_t dtype;    /* SSM_BF16 or SSM_FP32 */
+  int32_t dtype;    /* SSM_BF16, SSM_FP32 or SSM_FP8_E4M3 (where an entry point accepts it) */
   int32_t ndim;
   int64_t shape[4];
   int64_t stride[4];
@@ -125,6 +125,19 @@ typedef struct {
  * its key tiles are scanned in ascending order and the first is never skipped. */
 int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, int32_t seqlen, int32_t causal,
                 float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream, const ssm_opts* opts);
+
+/* ssm_prefill with 8-bit queries and keys: the scores QK^T, which every visited tile needs (a skipped tile
+ * still needs them to decide), run on the FP8 matrix instructions at twice the bf16 rate, while V, the
+ * softmax weights and P*V stay bf16.  Follows the FP8 attention context of the "Approximating Softmax in
+ * Pretrained LLMs" page (Abstract) as applied to the Skip Softmax forward above.
+ *   q [B, S, Hq, d] and k [B, S, Hkv, d]: SSM_FP8_E4M3 codes (OCP e4m3: bias 7, subnormals, no infinities,
+ *     S.1111.111 is NaN) with per-tensor dequantisation factors: query = q_scale * code, key = k_scale * code
+ *     (finite, > 0); strides multiples of 16 elements, data 16-byte aligned.
+ *   v [B, S, Hkv, d] bf16, out [B, S, Hq, d] bf16; everything else as ssm_prefill (same units, statistics,
+ *   options and errors).  The skip rule and the softmax apply to the logits scale * query . key. */
+int ssm_prefill_fp8qk(const ssm_tensor* q, float q_scale, const ssm_tensor* k, float k_scale, const ssm_tensor* v,
+                      int32_t seqlen, int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats,
+                      void* stream, const ssm_opts* opts);
 
 /* Single-token GQA decode with split-K and a log-sum-exp combine.
  *   q [B, Hq, d] bf16; out [B, Hq, d] bf16; K/V caches bf16 or fp8 e4m3 (see ssm_kv_cache: an fp8

@@ -7,6 +7,8 @@ fallback path: if the library is missing or a call fails, an exception is raised
 
 Entry points (same names as the C ABI):
     ssm_prefill(q, k, v, causal=True, tau=-ln(1000), ...)       -> out [B,S,Hq,d] bf16
+    ssm_prefill_fp8qk(q8, q_scale, k8, k_scale, v, ...)         -> out (fp8 e4m3 queries and keys)
+    ssm_prefill_paged(q, k_cache, v_cache, page_table, ...)     -> out [total_q,Hq,d] bf16
     ssm_decode(q, k_cache, v_cache, kv_lens, tau=..., ...)      -> out [B,Hq,d] bf16
     ssm_decode_workspace_bytes(B, Hq, d, num_splits)
     ssm_strerror(code), ssm_last_error(), ssm_abi_version()
@@ -26,8 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 SSM_BF16, SSM_FP32, SSM_FP8_E4M3 = 0, 1, 2
-EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror",
-                    "ssm_last_error", "ssm_abi_version")
+EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_prefill_fp8qk", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes",
+                    "ssm_strerror", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -57,7 +59,7 @@ class Opts(ctypes.Structure):
                 ("decode_flags", ctypes.c_int32)]
 
 
-ABI_VERSION = 4               # the layout above matches SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 5               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
 DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
 
 
@@ -76,6 +78,9 @@ def lib():
     L.ssm_prefill.restype = ctypes.c_int
     L.ssm_prefill.argtypes = [P(Tensor), P(Tensor), P(Tensor), ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                               P(Tensor), P(SkipStatsC), ctypes.c_void_p, P(Opts)]
+    L.ssm_prefill_fp8qk.restype = ctypes.c_int
+    L.ssm_prefill_fp8qk.argtypes = [P(Tensor), ctypes.c_float, P(Tensor), ctypes.c_float, P(Tensor), ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_float, P(Tensor), P(SkipStatsC), ctypes.c_void_p, P(Opts)]
     L.ssm_decode.restype = ctypes.c_int
     L.ssm_decode.argtypes = [P(Tensor), P(KvCache), P(KvCache), ctypes.c_void_p, ctypes.c_float, P(Tensor),
                              P(SkipStatsC), ctypes.c_void_p, P(Opts)]
@@ -168,6 +173,25 @@ def ssm_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     rc = lib().ssm_prefill(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), int(q.shape[1]) if q.dim() == 4 else 0,
                            int(bool(causal)), float(tau), ctypes.byref(od), ctypes.byref(st) if st else None,
                            _stream_handle(stream), ctypes.byref(opts))
+    _check(rc)
+    return out
+
+
+def ssm_prefill_fp8qk(q: torch.Tensor, q_scale: float, k: torch.Tensor, k_scale: float, v: torch.Tensor,
+                      causal: bool = True, tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
+                      skip_stats: Optional[SkipStats] = None, stream=None, tile_q: int = 128, tile_k: int = 64,
+                      scale: float = 0.0) -> torch.Tensor:
+    """Skip Softmax prefill with 8-bit scores: q [B,S,Hq,d] and k [B,S,Hkv,d] torch.float8_e4m3fn codes (query =
+    q_scale * code, key = k_scale * code), v [B,S,Hkv,d] bf16 on the GPU -> out [B,S,Hq,d] bf16."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    qd, kd, vd, od = describe(q), describe(k), describe(v), describe(out)
+    opts = Opts(float(scale), int(tile_q), int(tile_k), 0, None, 0)
+    st = skip_stats.c() if skip_stats is not None else None
+    rc = lib().ssm_prefill_fp8qk(ctypes.byref(qd), float(q_scale), ctypes.byref(kd), float(k_scale), ctypes.byref(vd),
+                                 int(q.shape[1]) if q.dim() == 4 else 0, int(bool(causal)), float(tau),
+                                 ctypes.byref(od), ctypes.byref(st) if st else None, _stream_handle(stream),
+                                 ctypes.byref(opts))
     _check(rc)
     return out
 
@@ -286,6 +310,6 @@ def bf16_from_bits(a, device=None) -> torch.Tensor:
     return t.to(device) if device is not None else t
 
 
-__all__ = ["ssm_prefill", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
+__all__ = ["ssm_prefill", "ssm_prefill_fp8qk", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
            "ssm_abi_version", "SkipStats", "SsmError", "prefill_stats_shape", "decode_workspace", "bf16_from_bits",
            "lib", "describe", "LIB_PATH", "EXPORTED_SYMBOLS"]

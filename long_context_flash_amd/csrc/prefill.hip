@@ -40,6 +40,11 @@
 // the other inside each wave.  Tiles wholly inside the causal triangle run
 // without masking code; only the diagonal/ragged tiles mask.
 //
+// FP8 scores (QK8): Q and K as OCP e4m3 codes with one dequantisation scale each (folded into the logit
+// scale); S^T on v_mfma_f32_32x32x64_f8f6f4, twice the bf16 rate, for the QK^T that every visited tile
+// pays.  K tiles sit in LDS as 8-bit rows (D bytes); each lane reads 32 bytes of one key row per MFMA, and
+// Q and K use the same channel order (any order gives the same dot products).  V, P and P.V stay bf16.
+//
 // Exponentials use a lazily moved reference maximum: P = 2^(S*c - m_ref*c) with
 // m_ref only raised when the true running maximum exceeds it by more than 8
 // (log2 units), which bounds P by 256 and makes the rescale of the output
@@ -84,26 +89,35 @@ __device__ __forceinline__ void map_prefill_unit(int bid, const PrefillArgs& a, 
 // read land on 4 distinct 4-chunk groups.
 template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+// 8-bit K tile (rows of D bytes): the 16 rows of one 16-lane phase of an operand read hit 16 distinct 4-bank groups
+template <int D> __device__ __forceinline__ int swz_k8(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // CHUNKED: queries of each sequence are the last ones of its cached keys (bottom-right causal), packed
-// ragged rows of q/o, K/V read through a page table (see PrefillArgs).
-template <int D, int TQ, bool CHUNKED>
+// ragged rows of q/o, K/V read through a page table (see PrefillArgs).  QK8: q and k hold e4m3 codes.
+template <int D, int TQ, bool CHUNKED, bool QK8>
 __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
+  static_assert(!(CHUNKED && QK8), "8-bit scores are implemented for the contiguous prefill only");
   constexpr int NW = TQ / 32;             // waves per workgroup
-  constexpr int ROWB = 2 * D;             // bytes per key row of a tile in LDS
-  constexpr int KSTEPS = D / 16;          // k-steps of the QK^T MFMA
+  constexpr int ROWB = 2 * D;             // bytes per key row of a V tile in LDS
+  constexpr int ESK = QK8 ? 1 : 2;        // bytes per Q/K element
+  constexpr int ROWK = ESK * D;           // bytes per key row of a K tile in LDS
+  constexpr int KSTEPS = QK8 ? D / 64 : D / 16;  // k-steps of the QK^T MFMA
   constexpr int CB = D / 32;              // 32-channel blocks of the output
-  constexpr int IPW = kTK * ROWB / 1024 / NW;  // 1 KB direct-to-LDS loads per wave, tensor and tile
+  constexpr int IPW = kTK * ROWB / 1024 / NW;   // 1 KB direct-to-LDS loads per wave and V tile
+  constexpr int IPWK = kTK * ROWK / 1024 / NW;  // the same per K tile
   static_assert(IPW >= 1 && kTK * ROWB % (1024 * NW) == 0, "tile split");
+  static_assert(IPWK >= 1 && kTK * ROWK % (1024 * NW) == 0, "tile split");
   constexpr int AHEAD = 2;                // MFMAs an LDS operand read runs ahead of its use
+  auto swzk = [](int r) { return QK8 ? swz_k8<D>(r) : swz_k<D>(r); };
 
   // separate arrays per buffer: the wait-count pass then sees that a load into one buffer does not
   // alias reads of the other
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kTK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kTK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kTK * ROWK / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kTK * ROWK / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kTK * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kTK * D];
   __shared__ uint32_t votes[2][NW];
@@ -145,9 +159,13 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 
   // ---- buffer resources: one (b, head) slice each (chunked: K/V per tile, below); bytes past the last row
   // read as zero (also for the direct-to-LDS loads)
+  // bytes spanned by rows [0, n) of a Q/K slice with row stride ss elements
+  auto qk_rows_bytes = [&](int n, int64_t ss) { return n <= 0 ? 0u : (uint32_t)(((int64_t)(n - 1) * ss + D) * ESK); };
+  const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q);
+  const uint8_t* k8 = reinterpret_cast<const uint8_t*>(a.k);
   const rsrc_t rq = CHUNKED ? make_rsrc(a.q + (int64_t)qrow0 * a.q_ss + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D))
-                            : make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D));
-  const rsrc_t rk = make_rsrc(a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh, CHUNKED ? 0u : rows_bytes(S, a.k_ss, D));
+                            : make_rsrc(q8 + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ESK, qk_rows_bytes(S, a.q_ss));
+  const rsrc_t rk = make_rsrc(k8 + ((int64_t)b * a.k_sb + (int64_t)g * a.k_sh) * ESK, CHUNKED ? 0u : qk_rows_bytes(S, a.k_ss));
   const rsrc_t rv = make_rsrc(a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh, CHUNKED ? 0u : rows_bytes(S, a.v_ss, D));
   // chunked: the resource of key tile t of this KV head (rows past Sk and bad page ids read as zero)
   auto page_rsrc = [&](const uint16_t* pool, const int32_t* pages, int64_t pool_pages, int64_t sb, int64_t sh,
@@ -157,34 +175,46 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     return make_rsrc(pool + (int64_t)pg * sb + (int64_t)g * sh, rows_bytes(min(kTK, Sk - t * kTK), ss, D));
   };
 
-  // ---- Q operand: lane (col, half) holds Q[row][ks*16 + half*8 .. +8] for every k-step
+  // ---- Q operand: lane (col, half) holds Q[row][ks*16 + half*8 .. +8] for every k-step (QK8: the 32
+  // codes Q[row][ks*64 + half*32 .. +32])
   const int iq = q0 + w * 32 + col;
   const bool row_ok = iq < S;
-  bf16x8 qreg[KSTEPS];
+  bf16x8 qreg[QK8 ? 1 : KSTEPS];
+  i32x8 qreg8[QK8 ? KSTEPS : 1];
   {
-    const uint32_t qoff = row_ok ? (uint32_t)iq * (uint32_t)(a.q_ss * 2) + half * 16 : 0xffffffffu;
+    const uint32_t qoff = row_ok ? (uint32_t)iq * (uint32_t)(a.q_ss * ESK) + half * (QK8 ? 32 : 16) : 0xffffffffu;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = as_bf16x8(buffer_load_16(rq, row_ok ? qoff + ks * 32 : qoff));
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if constexpr (QK8) {
+        const u32x4 lo = buffer_load_16(rq, row_ok ? qoff + ks * 64 : qoff);
+        const u32x4 hi = buffer_load_16(rq, row_ok ? qoff + ks * 64 + 16 : qoff);
+        qreg8[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      } else {
+        qreg[ks] = as_bf16x8(buffer_load_16(rq, row_ok ? qoff + ks * 32 : qoff));
+      }
+    }
   }
 
   // ---- tile loads, straight into LDS: load i of wave w fills LDS bytes [(w*IPW + i) KB, +1 KB) of the
   // tile, lane l the 16 bytes at l*16 of it, i.e. chunk position p of row r; it fetches the logical chunk
   // p ^ swz(r) of that key row.
-  constexpr int RPL = 1024 / ROWB;  // key rows per load
+  constexpr int RPL = 1024 / ROWB;   // key rows per load (V)
+  constexpr int RPLK = 1024 / ROWK;  // the same for K
   const int lrow = lane / (ROWB / 16), lpos = lane % (ROWB / 16);
-  const uint32_t k_row_bytes = (uint32_t)(a.k_ss * 2), v_row_bytes = (uint32_t)(a.v_ss * 2);
+  const int lrowk = lane / (ROWK / 16), lposk = lane % (ROWK / 16);
+  const uint32_t k_row_bytes = (uint32_t)(a.k_ss * ESK), v_row_bytes = (uint32_t)(a.v_ss * 2);
   const uint32_t k_tile_bytes = kTK * k_row_bytes, v_tile_bytes = kTK * v_row_bytes;
-  // Row (w*IPW + i)*RPL + lrow: both swizzles split into a per-lane part and a part of the load index
+  // Row (w*IPW + i)*RPL + lrow: every swizzle splits into a per-lane part and a part of the load index
   // (their bit fields do not overlap), so the chunk offset is (lane part) ^ (uniform part).
-  uint32_t k_dma = (uint32_t)(w * IPW * RPL + lrow) * k_row_bytes;   // row part of this lane's K loads
-  uint32_t k_dmx = (uint32_t)(lpos ^ swz_k<D>(lrow)) * 16;           // chunk part
+  uint32_t k_dma = (uint32_t)(w * IPWK * RPLK + lrowk) * k_row_bytes;   // row part of this lane's K loads
+  uint32_t k_dmx = (uint32_t)(lposk ^ swzk(lrowk)) * 16;                // chunk part
   uint32_t v_dma = (uint32_t)(w * IPW * RPL + lrow) * v_row_bytes + (uint32_t)(lpos ^ swz_v<D>(lrow)) * 16;
   auto load_k_rsrc = [&](uint16_t* dst, rsrc_t r, uint32_t toff) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const uint32_t cx = (uint32_t)swz_k<D>((w * IPW + i) * RPL) * 16;  // wave-uniform
-      const uint32_t vo = k_dma + (k_dmx ^ cx) + (uint32_t)(i * RPL) * k_row_bytes + toff;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + (w * IPW + i) * 512), 16, vo, 0, 0, 0);
+    for (int i = 0; i < IPWK; ++i) {
+      const uint32_t cx = (uint32_t)swzk((w * IPWK + i) * RPLK) * 16;  // wave-uniform
+      const uint32_t vo = k_dma + (k_dmx ^ cx) + (uint32_t)(i * RPLK) * k_row_bytes + toff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + (w * IPWK + i) * 512), 16, vo, 0, 0, 0);
     }
   };
   auto load_v_rsrc = [&](uint16_t* dst, rsrc_t r, uint32_t toff) {
@@ -196,7 +226,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
   auto load_k = [&](uint16_t* dst, int t) {
-    if constexpr (CHUNKED) load_k_rsrc(dst, page_rsrc(a.k, a.k_pages, a.k_pool_pages, a.k_sb, a.k_sh, a.k_ss, t), 0u);
+    if constexpr (CHUNKED && !QK8) load_k_rsrc(dst, page_rsrc(a.k, a.k_pages, a.k_pool_pages, a.k_sb, a.k_sh, a.k_ss, t), 0u);
     else load_k_rsrc(dst, rk, (uint32_t)t * k_tile_bytes);
   };
   auto load_v = [&](uint16_t* dst, int t) {
@@ -208,8 +238,11 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   // constant on bits that neither the base's row part nor the added constants touch.
   // K (S^T's A operand): lane (col, half) reads row kb*32 + col, logical chunk 2*ks + half, i.e. byte
   // (kb*32 + col)*ROWB + 16*((2ks + half) ^ swz_k(col)) = (k_opb ^ 32*ks) + kb*32*ROWB.
-  const int xk = swz_k<D>(col);
-  uint32_t k_opb = (uint32_t)(col * ROWB + 32 * (xk >> 1) + 16 * (half ^ (xk & 1)));
+  // QK8: lane (col, half) reads row kb*32 + col, logical chunks 4ks + 2half and 4ks + 2half + 1 (32 codes),
+  // i.e. bytes (kb*32 + col)*D + 16*((4ks + 2half + j) ^ swz_k8(col)) = (k_opb ^ 16*(4ks + j)) + kb*32*D.
+  const int xk = swzk(col);
+  uint32_t k_opb = QK8 ? (uint32_t)(col * ROWK + 16 * ((2 * half) ^ xk))
+                       : (uint32_t)(col * ROWB + 32 * (xk >> 1) + 16 * (half ^ (xk & 1)));
   // V^T (O^T's A operand) by transposing reads: in each 16-lane group, lane 4j + m names 4 channels
   // (4m .. 4m+3 of the group's 16) of key row k0 + j and receives channel (lane & 15) of the 4 rows.
   // Group gq covers channels 16*(gq & 1) of each 32-channel block and the keys of half gq >> 1.  The
@@ -221,6 +254,12 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   uint32_t v_opb = (uint32_t)(vrow * ROWB + 64 * (swz_v<D>(vrow) >> 2) + 16 * (vch >> 3) + 2 * (vch & 7));
   auto kop = [&](const uint16_t* kl, int ks, int kb) {
     return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kl) + ((k_opb ^ (32u * ks)) + kb * 32 * ROWB));
+  };
+  auto kop8 = [&](const uint16_t* kl, int ks, int kb) {
+    const char* base = reinterpret_cast<const char*>(kl) + kb * 32 * ROWK;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + (k_opb ^ (64u * ks)));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (k_opb ^ (64u * ks + 16u)));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   auto vop = [&](const uint16_t* vl, int cb, int st) {
     // the S^T accumulator layout that P^T comes from: half hf holds keys 4hf..4hf+3 and 8+4hf..8+4hf+3
@@ -252,15 +291,27 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   auto qk = [&](const uint16_t* kl, f32x16 (&s)[2]) {
     constexpr int NM = 2 * KSTEPS;
     __builtin_amdgcn_s_setprio(1);
-    u32x4 x[NM];
+    if constexpr (QK8) {
+      i32x8 x[NM];
 #pragma unroll
-    for (int j = 0; j < AHEAD; ++j) x[j] = kop(kl, j >> 1, j & 1);
+      for (int j = 0; j < NM; ++j) x[j] = kop8(kl, j >> 1, j & 1);
 #pragma unroll
-    for (int j = 0; j < NM; ++j) {
-      if (j + AHEAD < NM) x[j + AHEAD] = kop(kl, (j + AHEAD) >> 1, (j + AHEAD) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      const int ks = j >> 1, kb = j & 1;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[j]), qreg[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
+      for (int j = 0; j < NM; ++j) {
+        const int ks = j >> 1, kb = j & 1;
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x[j], qreg8[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0, 0,
+                                                                0, 0);
+      }
+    } else {
+      u32x4 x[NM];
+#pragma unroll
+      for (int j = 0; j < AHEAD; ++j) x[j] = kop(kl, j >> 1, j & 1);
+#pragma unroll
+      for (int j = 0; j < NM; ++j) {
+        if (j + AHEAD < NM) x[j + AHEAD] = kop(kl, (j + AHEAD) >> 1, (j + AHEAD) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = j >> 1, kb = j & 1;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x[j]), qreg[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -462,15 +513,17 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, bool qk8, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hq * a.nqt);
   if (grid == 0) return hipSuccess;
+  if (chunked && qk8) return hipErrorInvalidValue;
   const dim3 blk(tile_q * 2);
-#define SSM_PREFILL_LAUNCH(D, TQ)                                                                        \
-  if (d == D && tile_q == TQ) {                                                                          \
-    if (chunked) hipLaunchKernelGGL((prefill_kernel<D, TQ, true>), dim3(grid), blk, 0, stream, a);       \
-    else hipLaunchKernelGGL((prefill_kernel<D, TQ, false>), dim3(grid), blk, 0, stream, a);              \
-    return hipGetLastError();                                                                            \
+#define SSM_PREFILL_LAUNCH(D, TQ)                                                                            \
+  if (d == D && tile_q == TQ) {                                                                              \
+    if (chunked) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, false>), dim3(grid), blk, 0, stream, a);    \
+    else if (qk8) hipLaunchKernelGGL((prefill_kernel<D, TQ, false, true>), dim3(grid), blk, 0, stream, a);   \
+    else hipLaunchKernelGGL((prefill_kernel<D, TQ, false, false>), dim3(grid), blk, 0, stream, a);           \
+    return hipGetLastError();                                                                                \
   }
   SSM_PREFILL_LAUNCH(128, 128)
   SSM_PREFILL_LAUNCH(128, 64)

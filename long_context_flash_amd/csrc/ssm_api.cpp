@@ -89,13 +89,18 @@ size_t ssm_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int32_t num_
   return lse_off + rows * sizeof(float);
 }
 
-int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, int32_t seqlen, int32_t causal,
-                float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream, const ssm_opts* opts) {
+// qk8: q and k hold e4m3 codes with dequantisation factors q_scale, k_scale (ssm_prefill_fp8qk)
+static int prefill_impl(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, int32_t seqlen, int32_t causal,
+                        float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream, const ssm_opts* opts,
+                        bool qk8, float q_scale, float k_scale) {
   int rc;
-  if ((rc = check_tensor(q, "q", 4, SSM_BF16)) || (rc = check_tensor(k, "k", 4, SSM_BF16)) ||
+  const int qk_dt = qk8 ? SSM_FP8_E4M3 : SSM_BF16;
+  if ((rc = check_tensor(q, "q", 4, qk_dt)) || (rc = check_tensor(k, "k", 4, qk_dt)) ||
       (rc = check_tensor(v, "v", 4, SSM_BF16)) || (rc = check_tensor(out, "out", 4, SSM_BF16)))
     return rc;
   if ((rc = check_tau(tau))) return rc;
+  if (qk8 && !(q_scale > 0.f && std::isfinite(q_scale) && k_scale > 0.f && std::isfinite(k_scale)))
+    return fail(SSM_EINVAL, "q_scale and k_scale must be finite and > 0");
   const int64_t B = q->shape[0], S = q->shape[1], Hq = q->shape[2], d = q->shape[3];
   const int64_t Hkv = k->shape[2];
   if (seqlen != S) return fail(SSM_EINVAL, "seqlen %d != q.shape[1] %lld", (int)seqlen, (long long)S);
@@ -120,7 +125,8 @@ int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, i
   if (units > INT32_MAX) return fail(SSM_EUNSUPPORTED, "too many query tiles");
   // the kernels address each (batch, head) slice with 32-bit byte offsets
   for (const ssm_tensor* t : {q, k, v}) {
-    if ((S + 128) * t->stride[1] * 2 + d * 2 > (int64_t)UINT32_MAX)
+    const int64_t es = t->dtype == SSM_FP8_E4M3 ? 1 : 2;
+    if ((S + 128) * t->stride[1] * es + d * es > (int64_t)UINT32_MAX)
       return fail(SSM_EUNSUPPORTED, "sequence too long for 32-bit slice offsets (S=%lld, row stride %lld)",
                   (long long)S, (long long)t->stride[1]);
   }
@@ -147,15 +153,29 @@ int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, i
   a.causal = causal != 0;
   const int64_t groups = B * Hkv;
   a.xcd_groups = groups % 8 == 0 ? (int)(groups / 8) : 0;
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.tau_raw = std::isinf(tau) ? tau : tau / scale;
+  // the kernels score raw code products; the dequantisation factors join the logit scale
+  const float lscale = qk8 ? scale * q_scale * k_scale : scale;
+  if (!(lscale > 0.f) || !std::isfinite(lscale)) return fail(SSM_EINVAL, "scale * q_scale * k_scale out of range");
+  a.scale = lscale;
+  a.scale_log2 = lscale * 1.4426950408889634f;
+  a.tau_raw = std::isinf(tau) ? tau : tau / lscale;
   if (skip_stats) {
     a.tile_state = skip_stats->tile_state;
     a.unit_gap = skip_stats->unit_gap;
     a.counters = skip_stats->counters;
   }
-  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, false, static_cast<hipStream_t>(stream)));
+  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, false, qk8, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, int32_t seqlen, int32_t causal,
+                float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream, const ssm_opts* opts) {
+  return prefill_impl(q, k, v, seqlen, causal, tau, out, skip_stats, stream, opts, false, 1.f, 1.f);
+}
+
+int ssm_prefill_fp8qk(const ssm_tensor* q, float q_scale, const ssm_tensor* k, float k_scale, const ssm_tensor* v,
+                      int32_t seqlen, int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats,
+                      void* stream, const ssm_opts* opts) {
+  return prefill_impl(q, k, v, seqlen, causal, tau, out, skip_stats, stream, opts, true, q_scale, k_scale);
 }
 
 static int check_cache(const ssm_kv_cache* c, const char* name, int64_t B, int64_t d, int* kv_cap, int64_t* pool_rows,
@@ -348,7 +368,7 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
   a.total_q = (int)total_q;
   a.k_pool_pages = krows;
   a.v_pool_pages = vrows;
-  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, true, static_cast<hipStream_t>(stream)));
+  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, true, false, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -6,7 +6,7 @@
 namespace ssm {
 
 struct PrefillArgs {
-  const uint16_t* q;
+  const uint16_t* q;         // bf16, or e4m3 codes (prefill_kernel<..., QK8 = true>; strides then count bytes)
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
@@ -65,7 +65,7 @@ struct DecodeArgs {
   unsigned long long* counters;
 };
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, bool qk8, hipStream_t stream);
 hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
                               hipStream_t stream);
 

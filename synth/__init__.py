@@ -270,6 +270,18 @@ def fp8_kv(data: dict) -> dict:
     return out
 
 
+def fp8_qk(data: dict) -> dict:
+    """fp8 e4m3 copies of the Q and K of a gen_prefill() result with one scale per tensor (amax / 448, as
+    float32): q, k (uint8 codes) and q_scale, k_scale."""
+    out = {}
+    for name in ("q", "k"):
+        amax = _amax_bf16(data[name])
+        scale = float(np.float32(amax / FP8_E4M3_MAX)) if amax > 0 else 1.0
+        out[f"{name}_scale"] = scale
+        out[name] = quantize_fp8_e4m3(data[name], scale)
+    return out
+
+
 def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     return (a.astype(np.uint32) << 16).view(np.float32)
@@ -282,6 +294,6 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return (x >> 16).astype(np.uint16)
 
 
-__all__ = ["quantize_fp8_e4m3", "fp8_kv", "FP8_E4M3_MAX", "PrefillWorkload", "DecodeWorkload", "WORKLOADS", "TINY_PREFILL", "DECODE_32K", "PREFILL_16K",
+__all__ = ["quantize_fp8_e4m3", "fp8_kv", "fp8_qk", "FP8_E4M3_MAX", "PrefillWorkload", "DecodeWorkload", "WORKLOADS", "TINY_PREFILL", "DECODE_32K", "PREFILL_16K",
            "PREFILL_128K", "DECODE_128K", "gen_prefill", "gen_decode", "kv_lens_for", "bf16_bits_to_f32",
            "f32_to_bf16_bits", "build", "default_threads", "replace"]

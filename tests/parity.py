@@ -73,22 +73,59 @@ def unit_ids(B, Hq, nqt, units):
     return units // (Hq * nqt), (units // nqt) % Hq, units % nqt
 
 
-def run_prefill_gpu(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, device="cuda"):
-    q = ssm.bf16_from_bits(data["q"], device)
-    k = ssm.bf16_from_bits(data["k"], device)
+def run_prefill_gpu(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, device="cuda", fp8qk=None):
+    """fp8qk: the synth.fp8_qk() codes and scales of q and k (ssm_prefill_fp8qk), else the bf16 prefill."""
     v = ssm.bf16_from_bits(data["v"], device)
     units, nkt = ssm.prefill_stats_shape(B, S, Hq, tile_q)
     stats = ssm.SkipStats.alloc(units, nkt, device, gaps=True)
-    out = ssm.ssm_prefill(q, k, v, causal=causal, tau=tau, skip_stats=stats, tile_q=tile_q)
+    if fp8qk is not None:
+        q, k = fp8_device(fp8qk["q"], device), fp8_device(fp8qk["k"], device)
+        out = ssm.ssm_prefill_fp8qk(q, fp8qk["q_scale"], k, fp8qk["k_scale"], v, causal=causal, tau=tau,
+                                    skip_stats=stats, tile_q=tile_q)
+    else:
+        q = ssm.bf16_from_bits(data["q"], device)
+        k = ssm.bf16_from_bits(data["k"], device)
+        out = ssm.ssm_prefill(q, k, v, causal=causal, tau=tau, skip_stats=stats, tile_q=tile_q)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
             stats.counters.cpu().numpy())
 
 
-def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, where="prefill", threads=None):
-    """Run the GPU prefill on the whole input and compare the listed units (all when None) with the oracle."""
-    log(f"{where}: GPU prefill B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} tau={tau} tile_q={tile_q}")
-    out, st, gap, cnt = run_prefill_gpu(data, B=B, S=S, Hq=Hq, Hkv=Hkv, d=d, causal=causal, tau=tau, tile_q=tile_q)
+def dequant_fp8(codes, scale):
+    """float64 values of OCP e4m3 codes times a scale (torch's float8_e4m3fn decoding)."""
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale
+
+
+def oracle_prefill_fp8qk(data, f8, *, B, S, Hq, Hkv, causal, tau, tile_q, units, override=None, threads=None):
+    """oracle.prefill on the dequantised query/key codes and the bf16 values (widened), one query head at a time
+    (float64 copies of one head's q and its KV head's k, v only).  Same result layout as oracle.prefill."""
+    nqt, G = -(-S // tile_q), Hq // Hkv
+    bb, hh, qq = unit_ids(B, Hq, nqt, units)
+    res = None
+    for h in np.unique(hh):
+        sel = np.nonzero(hh == h)[0]
+        g = h // G
+        q64 = dequant_fp8(f8["q"][:, :, h:h + 1], f8["q_scale"])
+        k64 = dequant_fp8(f8["k"][:, :, g:g + 1], f8["k_scale"])
+        v64 = (data["v"][:, :, g:g + 1].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ov = None if override is None else override[sel]
+        r = oracle.prefill(q64, k64, v64, causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
+                           units=bb[sel] * nqt + qq[sel], override=ov, threads=threads)
+        if res is None:
+            res = {key: np.empty((len(units),) + val.shape[1:], val.dtype) for key, val in r.items()}
+        for key, val in r.items():
+            res[key][sel] = val
+    return res
+
+
+def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, where="prefill", threads=None,
+                  fp8qk=None):
+    """Run the GPU prefill on the whole input and compare the listed units (all when None) with the oracle.
+    fp8qk: the synth.fp8_qk() codes and scales of q and k; both sides then score the same 8-bit values."""
+    log(f"{where}: GPU prefill B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} tau={tau} tile_q={tile_q} "
+        f"fp8qk={fp8qk is not None}")
+    out, st, gap, cnt = run_prefill_gpu(data, B=B, S=S, Hq=Hq, Hkv=Hkv, d=d, causal=causal, tau=tau, tile_q=tile_q,
+                                        fp8qk=fp8qk)
     nqt = -(-S // tile_q)
     vis = int((st > 0).sum())
     skipped = int((st == 2).sum())
@@ -97,14 +134,19 @@ def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, wh
         units = np.arange(B * Hq * nqt)
     units = np.asarray(units, np.int64)
     log(f"{where}: oracle on {len(units)} units")
-    ref = oracle.prefill(data["q"], data["k"], data["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
-                         units=units, threads=threads)
+
+    def run_oracle(ov=None):
+        if fp8qk is not None:
+            return oracle_prefill_fp8qk(data, fp8qk, B=B, S=S, Hq=Hq, Hkv=Hkv, causal=causal, tau=tau, tile_q=tile_q,
+                                        units=units, override=ov, threads=threads)
+        return oracle.prefill(data["q"], data["k"], data["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
+                              units=units, override=ov, threads=threads)
+
+    ref = run_oracle()
     flips, n_amb = compare_masks(st[units], ref["state"], ref["gamma"], tau, where)
     compare_gaps(gap[units], ref["gamma"], ref["state"], where)
     if flips.any():
-        ov = np.where(flips, np.where(st[units] == 2, 1, 0), -1).astype(np.int8)
-        ref = oracle.prefill(data["q"], data["k"], data["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
-                             units=units, override=ov, threads=threads)
+        ref = run_oracle(np.where(flips, np.where(st[units] == 2, 1, 0), -1).astype(np.int8))
     bb, hh, qq = unit_ids(B, Hq, nqt, units)
     got = np.zeros_like(ref["out"])
     for n in range(len(units)):

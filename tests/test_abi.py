@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 4
+    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 5
     for code in range(5):
         assert ssm.ssm_strerror(code)
     assert "unknown" in ssm.ssm_strerror(99)
@@ -113,6 +113,56 @@ def test_prefill_rejects(lib, case, code):
     elif case == "out_shape":
         kw["o"] = desc([1, 256, 4, 128])
     rc = call_prefill(lib, **kw)
+    assert rc == code, (rc, ssm.ssm_last_error())
+    assert ssm.ssm_last_error()
+
+
+def call_prefill_fp8qk(lib, q=None, k=None, v=None, o=None, q_scale=0.05, k_scale=0.02, seqlen=256, tau=-6.9,
+                      opts=None):
+    q = q or desc([1, 256, 8, 128], dtype=ssm.SSM_FP8_E4M3)
+    k = k or desc([1, 256, 2, 128], dtype=ssm.SSM_FP8_E4M3)
+    v = v or desc([1, 256, 2, 128])
+    o = o or desc([1, 256, 8, 128])
+    return lib.ssm_prefill_fp8qk(ctypes.byref(q), q_scale, ctypes.byref(k), k_scale, ctypes.byref(v), seqlen, 1, tau,
+                                 ctypes.byref(o), None, None, ctypes.byref(opts) if opts else None)
+
+
+@pytest.mark.parametrize("case,code", [
+    ("bf16_q", ssm.SSM_EUNSUPPORTED), ("bf16_k", ssm.SSM_EUNSUPPORTED), ("fp8_v", ssm.SSM_EUNSUPPORTED),
+    ("zero_scale", ssm.SSM_EINVAL), ("nan_scale", ssm.SSM_EINVAL), ("inf_scale", ssm.SSM_EINVAL),
+    ("neg_scale", ssm.SSM_EINVAL), ("fp8_stride", ssm.SSM_EUNSUPPORTED), ("head_dim", ssm.SSM_EUNSUPPORTED),
+    ("pos_tau", ssm.SSM_EINVAL), ("gqa", ssm.SSM_EINVAL), ("tile_q", ssm.SSM_EUNSUPPORTED),
+])
+def test_prefill_fp8qk_rejects(lib, case, code):
+    kw = {}
+    f8 = ssm.SSM_FP8_E4M3
+    if case == "bf16_q":
+        kw["q"] = desc([1, 256, 8, 128])
+    elif case == "bf16_k":
+        kw["k"] = desc([1, 256, 2, 128])
+    elif case == "fp8_v":
+        kw["v"] = desc([1, 256, 2, 128], dtype=f8)
+    elif case == "zero_scale":
+        kw["q_scale"] = 0.0
+    elif case == "nan_scale":
+        kw["k_scale"] = math.nan
+    elif case == "inf_scale":
+        kw["q_scale"] = math.inf
+    elif case == "neg_scale":
+        kw["k_scale"] = -1.0
+    elif case == "fp8_stride":  # 136 codes per row: not a multiple of 16 bytes
+        kw["k"] = desc([1, 256, 2, 128], dtype=f8, stride=[256 * 2 * 136, 2 * 136, 136, 1])
+    elif case == "head_dim":
+        kw["q"], kw["k"] = desc([1, 256, 8, 96], dtype=f8), desc([1, 256, 2, 96], dtype=f8)
+        kw["v"], kw["o"] = desc([1, 256, 2, 96]), desc([1, 256, 8, 96])
+    elif case == "pos_tau":
+        kw["tau"] = 0.1
+    elif case == "gqa":
+        kw["k"] = desc([1, 256, 3, 128], dtype=f8)
+        kw["v"] = desc([1, 256, 3, 128])
+    elif case == "tile_q":
+        kw["opts"] = ssm.Opts(0.0, 32, 0, 0, None, 0)
+    rc = call_prefill_fp8qk(lib, **kw)
     assert rc == code, (rc, ssm.ssm_last_error())
     assert ssm.ssm_last_error()
 
