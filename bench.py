@@ -243,6 +243,58 @@ def time_fp8_decode(ssm, torch, np, w, data, dq, kp, vp, pt, lens, dout, ws, dst
             "speedup_vs_bf16": None}
 
 
+def recorded_fp8_mfma_ceiling():
+    """Random-operand fp8 MFMA rate recorded in profiles/mfma_ceiling.json (None if absent)."""
+    rec = _recorded("mfma_ceiling.json", "fp8")
+    return rec.get("random_operands_tflops") if rec else None
+
+
+def time_fp8qk_prefill(ssm, torch, np, w, q, k, v, out, tau, bf16_ms, steps, dev):
+    """The same prefill with 8-bit queries and keys (NEXT row, FP8 MFMA): q and k quantised on the GPU to OCP
+    e4m3 codes with amax/448 scales before timing, v bf16; timed on its own after the steps with HIP events,
+    skip counters in the timed calls.  The MFMA work splits into fp8 QK^T (every visited tile) and bf16 P.V
+    (kept tiles); `mfma_frac` is the time those would take at the published peaks over the measured time."""
+    def quant(x):
+        amax = float(x.abs().max().float())
+        scale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+        codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev)
+        for i in range(0, x.shape[1], 8192):
+            codes[:, i:i + 8192] = (x[:, i:i + 8192].float() / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return codes, scale
+    q8, qs = quant(q)
+    k8, ks = quant(k)
+    cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+    run = lambda: ssm.ssm_prefill_fp8qk(q8, qs, k8, ks, v, causal=True, tau=tau, out=out,
+                                        skip_stats=ssm.SkipStats(counters=cnt), tile_q=w.tile_q)
+    run()
+    torch.cuda.synchronize()
+    cnt.zero_()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    c = cnt.cpu().numpy() / steps
+    visited, skipped = float(c[0]), float(c[1])
+    dense, executed = prefill_flops(w, visited, visited - skipped)
+    qk_flop = 2.0 * w.tile_q * w.tile_k * w.d * visited
+    pv_flop = executed - qk_flop
+    t = ms / 1e3
+    ideal = qk_flop / (2 * MFMA_BF16_PEAK_TFLOPS * 1e12) + pv_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    res = {"workload": f"{w.name} with e4m3 q/k (amax/448 scales), bf16 v", "ms": round(ms, 3),
+           "dense_tflops": round(dense / t / 1e12, 2), "executed_tflops": round(executed / t / 1e12, 2),
+           "qk_fp8_tflops": round(qk_flop / t / 1e12, 2), "pv_bf16_tflops": round(pv_flop / t / 1e12, 2),
+           "mfma_frac": round(ideal / t, 4), "sparsity": round(skipped / visited, 4), "tau": tau,
+           "q_scale": qs, "k_scale": ks, "speedup_vs_bf16": round(bf16_ms / ms, 3)}
+    c8, c16 = recorded_fp8_mfma_ceiling(), recorded_mfma_ceiling()
+    if c8 and c16:
+        res["mfma_frac_of_measured_ceilings"] = round((qk_flop / (c8 * 1e12) + pv_flop / (c16 * 1e12)) / t, 4)
+    del q8, k8
+    return res
+
+
 CHUNK_Q = 8192  # the chunked-prefill leg: the last 8192 queries of the 128K input against all of its keys
 
 
@@ -486,6 +538,8 @@ def main():
                 "source": "profiles/mfma_ceiling.json"}
     if run_prefill and not args.main_only:
         res["prefill_chunked_paged"] = time_chunked_prefill(ssm, torch, np, pw, pdata, tau_p, args.steps, dev)
+        res["prefill_fp8_qk"] = time_fp8qk_prefill(ssm, torch, np, pw, q, k, v, pout, tau_p, res["prefill_ms"],
+                                                   args.steps, dev)
     if run_decode:
         c = dcnt.cpu().numpy() / args.steps
         ssm.ssm_decode(dq, kp, vp, lens, tau=tau_d, out=dout, page_table=pt, num_splits=dw.num_splits,
