@@ -59,3 +59,22 @@ def test_designed_transitions_causal(T, d, tile_q):
     data = designed(T, Hq=4, Hkv=1, d=d, seed=200 + T)
     check_prefill(data, B=1, S=64 * T, Hq=4, Hkv=1, d=d, causal=True, tau=-LN1000, tile_q=tile_q,
                   where=f"designed causal T={T} d={d} tq={tile_q}")
+
+
+@pytest.mark.parametrize("T", [12, 13])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_designed_transitions_fp8qk(T, d, causal):
+    """The same designed scans through the 8-bit-score prefill (q and k quantised with amax/448 scales; the
+    designed tile logits keep their decisions after quantisation, so non-causal units show the sequence).  The
+    whole logit sits in channel 0 here, the worst case for the fp8 MFMA's truncated in-group sums (logit errors
+    near 0.008 at logit 60), so the outputs are held to the bar derived from that error bound only."""
+    data = designed(T, Hq=4, Hkv=1, d=d, seed=300 + T)
+    f8 = synth.fp8_qk(data)
+    S = 64 * T
+    if not causal:
+        _, st, _, _ = run_prefill_gpu(data, B=1, S=S, Hq=4, Hkv=1, d=d, causal=False, tau=-LN1000, tile_q=128,
+                                      fp8qk=f8)
+        assert (st == np.asarray(EXPECTED[:T], np.uint8)[None, :]).all(), f"tile states {st[0].tolist()}"
+    check_prefill(data, B=1, S=S, Hq=4, Hkv=1, d=d, causal=causal, tau=-LN1000, tile_q=128, fp8qk=f8, strict=False,
+                  where=f"designed fp8qk causal={causal} T={T} d={d}")
