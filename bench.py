@@ -38,7 +38,7 @@ KERNEL_SOURCES = {"prefill": ["prefill.hip", "ssm_device.h", "ssm_launch.h", "ss
                   "decode": ["decode.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"]}
 COPY_PROBE_BYTES = 1 << 30
 # the step's kernels as the profiler names them (d = 128, tile_q = 128, plain prefill, bf16 cache)
-PREFILL_KERNEL = "prefill_kernel<128, 128, false>"
+PREFILL_KERNEL = "prefill_kernel<128, 128, false, false>"
 DECODE_SPLIT_KERNEL = "decode_split_kernel<128, 2>"
 DECODE_COMBINE_KERNEL = "decode_combine_kernel<128>"
 
