@@ -428,8 +428,8 @@ def main():
             sys.exit(f"{exe} is missing: build with `python -m long_context_flash_amd.build`")
         sys.exit(subprocess.run([exe]).returncode)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each GPU would run the same "
+              "kernels on its shard of KV groups or sequence). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
