@@ -88,3 +88,23 @@ def test_batch_beyond_dispatch_sort():
     out = ssm.ssm_decode(q, kc, vc, torch.from_numpy(lens[:1024]).to(dev), tau=-LN1000, num_splits=4)
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy(), r["out"][:1024]), "dispatch order changed the outputs"
+
+
+def test_strided_query_and_output_match_contiguous():
+    """q and out as views with padded head and batch strides give the same bits as contiguous tensors."""
+    import torch
+    import long_context_flash_amd as ssm
+    data = synth.gen_decode(_small(B=2, Hq=16, Hkv=2, d=128, seed=21), contiguous=True, paged=False)
+    dev = "cuda"
+    q = ssm.bf16_from_bits(data["q"], dev)
+    kc, vc = ssm.bf16_from_bits(data["k_cache"], dev), ssm.bf16_from_bits(data["v_cache"], dev)
+    lens = torch.from_numpy(data["kv_lens"]).to(dev)
+    ref = ssm.ssm_decode(q, kc, vc, lens, tau=-LN1000, num_splits=8)
+    big_q = torch.zeros(2, 20, 144, dtype=q.dtype, device=dev)
+    qv = big_q[:, :16, :128]
+    qv.copy_(q)
+    big_o = torch.zeros(2, 20, 144, dtype=q.dtype, device=dev)
+    ov = big_o[:, :16, :128]
+    ssm.ssm_decode(qv, kc, vc, lens, tau=-LN1000, num_splits=8, out=ov)
+    torch.cuda.synchronize()
+    assert torch.equal(ov, ref), "strided q/out changed the result"

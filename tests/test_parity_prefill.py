@@ -76,3 +76,35 @@ def test_prefill_128k_sampled():
     r = check_prefill(data, B=1, S=w.S, Hq=w.Hq, Hkv=w.Hkv, d=w.d, causal=True, tau=w.taus[0], tile_q=128,
                       units=units, where="128k")
     assert r["sparsity"] >= 0.45, "the calibrated workload skips about half of its tiles"
+
+
+def test_batch3_causal_gqa2_odd_length():
+    w = synth.replace(synth.PREFILL_16K, B=3, S=515, Hq=8, Hkv=4, d=64, seed=8)
+    check_prefill(_data(w), B=3, S=515, Hq=8, Hkv=4, d=64, causal=True, tau=-LN1000, tile_q=64,
+                  where="b3 causal gqa2")
+
+
+def test_strided_views_match_contiguous():
+    """q/k/v/out as views into wider buffers (row strides padded by 16 elements, heads interleaved with a gap):
+    the kernels address through the descriptors' strides, so the outputs equal the contiguous run bit for bit."""
+    import torch
+    import long_context_flash_amd as ssm
+    w = synth.replace(synth.PREFILL_16K, S=700, Hq=8, Hkv=2, d=128, seed=12)
+    data = _data(w)
+    dev = "cuda"
+    q, k, v = (ssm.bf16_from_bits(data[x], dev) for x in ("q", "k", "v"))
+    ref = ssm.ssm_prefill(q, k, v, causal=True, tau=-LN1000)
+
+    def padded(t):
+        B, S, H, d = t.shape
+        big = torch.zeros(B, S, H + 1, d + 16, dtype=t.dtype, device=dev)
+        view = big[:, :, :H, :d]
+        view.copy_(t)
+        return view
+
+    qv, kv, vv = padded(q), padded(k), padded(v)
+    out = padded(torch.zeros_like(q))
+    assert qv.stride(1) == 9 * 144 and not qv.is_contiguous()
+    ssm.ssm_prefill(qv, kv, vv, causal=True, tau=-LN1000, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "strided views changed the result"
