@@ -337,3 +337,36 @@ def test_prefill_paged_rejects(lib, case, code):
 def test_prefill_paged_empty_batch_is_a_no_op(lib):
     assert call_prefill_paged(lib, batch=0) == ssm.SSM_OK
     assert call_prefill_paged(lib, max_q=0) == ssm.SSM_OK
+
+
+def test_c_program_links_and_validates(tmp_path):
+    """A plain C99 program (no C++ or torch) includes ssm.h, links libssm.so and gets error codes and messages
+    back from argument validation (which returns before any device call)."""
+    src = tmp_path / "use.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "ssm.h"
+int main(void) {
+  ssm_tensor q, k, v, o;
+  memset(&q, 0, sizeof q); memset(&k, 0, sizeof k); memset(&v, 0, sizeof v); memset(&o, 0, sizeof o);
+  if (ssm_abi_version() != SSM_ABI_VERSION) return 10;
+  /* NULL data pointers: every entry point must refuse without touching the device */
+  int rc = ssm_prefill(&q, &k, &v, 1, 1, -6.9f, &o, NULL, NULL, NULL);
+  if (rc != SSM_EINVAL || strlen(ssm_last_error()) == 0) return 11;
+  rc = ssm_prefill_fp8qk(&q, 1.0f, &k, 1.0f, &v, 1, 1, -6.9f, &o, NULL, NULL, NULL);
+  if (rc != SSM_EINVAL) return 12;
+  rc = ssm_decode(&q, NULL, NULL, NULL, -6.9f, &o, NULL, NULL, NULL);
+  if (rc != SSM_EINVAL) return 13;
+  if (ssm_decode_workspace_bytes(1, 8, 128, 16) == 0) return 14;
+  printf("%s | %s\n", ssm_strerror(rc), ssm_last_error());
+  return 0;
+}
+''')
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(ssm.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-lssm", f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "q" in r.stdout
