@@ -38,7 +38,7 @@ KERNEL_SOURCES = {"prefill": ["prefill.hip", "ssm_device.h", "ssm_launch.h", "ss
                   "decode": ["decode.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"]}
 COPY_PROBE_BYTES = 1 << 30
 # the step's kernels as the profiler names them (d = 128, tile_q = 128, plain prefill, bf16 cache)
-PREFILL_KERNEL = "prefill_kernel<128, 128, false, false>"
+PREFILL_KERNEL = "prefill_kernel<128, 128, false, 0>"
 DECODE_SPLIT_KERNEL = "decode_split_kernel<128, 2>"
 DECODE_COMBINE_KERNEL = "decode_combine_kernel<128>"
 
@@ -339,11 +339,39 @@ def time_chunked_prefill(ssm, torch, np, w, data, tau, steps, dev):
     dense = 4.0 * w.Hq * w.d * (nq * off + nq * (nq + 1) / 2)  # query i sees off + i + 1 keys
     executed = 2.0 * w.tile_q * w.tile_k * w.d * (2 * visited - skipped)
     t = ms / 1e3
-    del pool_k, pool_v, q, out
-    return {"workload": f"chunk q{nq} of kv{S} (paged, 64-token pages)", "ms": round(ms, 3),
-            "dense_tflops": round(dense / t / 1e12, 2), "executed_tflops": round(executed / t / 1e12, 2),
-            "mfma_frac": round(executed / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "sparsity": round(skipped / visited, 4),
-            "tau": tau}
+    res = {"workload": f"chunk q{nq} of kv{S} (paged, 64-token pages)", "ms": round(ms, 3),
+           "dense_tflops": round(dense / t / 1e12, 2), "executed_tflops": round(executed / t / 1e12, 2),
+           "mfma_frac": round(executed / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "sparsity": round(skipped / visited, 4),
+           "tau": tau}
+    # the same chunk over an fp8 e4m3 copy of the pools (amax/448 scales, quantised on the GPU before timing)
+    def quant(pool):
+        amax = float(pool.abs().max().float())
+        scale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+        codes = torch.empty(pool.shape, dtype=torch.float8_e4m3fn, device=dev)
+        for i in range(0, pool.shape[0], 4096):
+            codes[i:i + 4096] = (pool[i:i + 4096].float() / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return codes, scale
+    k8, ks = quant(pool_k)
+    v8, vs = quant(pool_v)
+    cnt8 = torch.zeros(4, dtype=torch.int64, device=dev)
+    run8 = lambda: ssm.ssm_prefill_paged(q, k8, v8, pt, qs, kl, nq, causal=True, tau=tau, out=out,
+                                         skip_stats=ssm.SkipStats(counters=cnt8), tile_q=w.tile_q, k_scale=ks,
+                                         v_scale=vs)
+    run8()
+    torch.cuda.synchronize()
+    cnt8.zero_()
+    for i in range(steps):
+        ev[i][0].record()
+        run8()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms8 = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    c8 = cnt8.cpu().numpy() / steps
+    res["fp8_cache"] = {"ms": round(ms8, 3), "dense_tflops": round(dense / (ms8 / 1e3) / 1e12, 2),
+                        "sparsity": round(float(c8[1]) / float(c8[0]), 4), "k_scale": ks, "v_scale": vs,
+                        "speedup_vs_bf16_cache": round(ms / ms8, 3)}
+    del pool_k, pool_v, k8, v8, q, out
+    return res
 
 
 def cpu_baseline_prefill(w, data, threads, n_units=256):

@@ -157,8 +157,10 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
  * context and to each other).  A ragged batch of `batch` sequences:
  *   q, out [total_q, Hq, d] bf16: sequence b's n_b = q_start[b+1] - q_start[b] query rows are rows
  *     q_start[b] .. q_start[b+1]-1 (q_start: device int32 [batch+1], 0 <= n_b <= max_q_len);
- *   k_cache, v_cache: paged bf16 pools [pages, Hkv, 64, d] with page tables of equal length (see
- *     ssm_kv_cache); sequence b has kv_lens[b] (device int32 [batch]) keys, the last n_b of which are its
+ *   k_cache, v_cache: paged pools [pages, Hkv, 64, d] with page tables of equal length (see ssm_kv_cache),
+ *     both bf16 or both SSM_FP8_E4M3 with their scales (the same cache the decode reads; each code is
+ *     converted exactly to bf16 for the bf16 MFMAs); sequence b has kv_lens[b] (device int32 [batch]) keys,
+ *     the last n_b of which are its
  *     new tokens (already written to the cache): query i of sequence b sits at key position
  *     kv_lens[b] - n_b + i and, with causal != 0, attends to keys j <= that position (bottom-right
  *     aligned); otherwise to all kv_lens[b] keys.

@@ -212,10 +212,12 @@ def ssm_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       q_start: torch.Tensor, kv_lens: torch.Tensor, max_q_len: int, causal: bool = True,
                       tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
                       skip_stats: Optional[SkipStats] = None, stream=None, tile_q: int = 128, scale: float = 0.0,
-                      v_page_table: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      v_page_table: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                      v_scale: float = 1.0) -> torch.Tensor:
     """Chunked prefill against a paged cache: q/out [total_q,Hq,d] bf16 (sequence b's rows q_start[b] ..
-    q_start[b+1]-1, the last of its kv_lens[b] cached keys); k_cache/v_cache [pages,Hkv,64,d] bf16 with
-    page_table int32 [B,max_pages]; q_start int32 [B+1] and kv_lens int32 [B] on the GPU."""
+    q_start[b+1]-1, the last of its kv_lens[b] cached keys); k_cache/v_cache [pages,Hkv,64,d] bf16, or
+    torch.float8_e4m3fn codes (key = k_scale * code, value = v_scale * code), with page_table int32
+    [B,max_pages]; q_start int32 [B+1] and kv_lens int32 [B] on the GPU."""
     if out is None:
         out = torch.empty_like(q)
     for name, t in (("q_start", q_start), ("kv_lens", kv_lens)):
@@ -224,8 +226,8 @@ def ssm_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     B = kv_lens.shape[0]
     if q_start.shape[0] != B + 1:
         raise ValueError("q_start must have batch + 1 entries")
-    kc = _paged_cache(k_cache, page_table)
-    vc = _paged_cache(v_cache, page_table if v_page_table is None else v_page_table)
+    kc = _paged_cache(k_cache, page_table, k_scale)
+    vc = _paged_cache(v_cache, page_table if v_page_table is None else v_page_table, v_scale)
     qd, od = describe(q), describe(out)
     opts = Opts(float(scale), int(tile_q), 64, 0, None, 0, 0)
     st = skip_stats.c() if skip_stats is not None else None

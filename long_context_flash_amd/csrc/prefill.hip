@@ -40,6 +40,11 @@
 // the other inside each wave.  Tiles wholly inside the causal triangle run
 // without masking code; only the diagonal/ragged tiles mask.
 //
+// FP8 cache for the chunked prefill (KV8): K and V pages hold e4m3 codes; their tiles sit in LDS as 8-bit
+// rows and every operand read converts its 8 codes exactly to bf16 (K: one 8-byte read; V^T: one 8-bit
+// transposing read, ds_read_b64_tr_b8, of 8 key rows), so the bf16 MFMAs and the rest are unchanged.  The
+// key scale joins the logit scale, the value scale multiplies the output.
+//
 // FP8 scores (QK8): Q and K as OCP e4m3 codes with one dequantisation scale each (folded into the logit
 // scale); S^T on v_mfma_f32_32x32x64_f8f6f4, twice the bf16 rate, for the QK^T that every visited tile
 // pays.  K tiles sit in LDS as 8-bit rows (D bytes); each lane reads 32 bytes of one key row per MFMA, and
@@ -91,19 +96,28 @@ template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ?
 template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 // 8-bit K tile (rows of D bytes): the 16 rows of one 16-lane phase of an operand read hit 16 distinct 4-bank groups
 template <int D> __device__ __forceinline__ int swz_k8(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+// 8-bit V tile: the 8 key rows r0..r0+3, r0+8..r0+11 (r0 % 4 == 0) that one 16-lane group of a transposing read
+// gathers land on distinct 4-bank groups
+template <int D> __device__ __forceinline__ int swz_v8(int r) {
+  return D == 128 ? (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) : ((r >> 3) & 1);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // CHUNKED: queries of each sequence are the last ones of its cached keys (bottom-right causal), packed
-// ragged rows of q/o, K/V read through a page table (see PrefillArgs).  QK8: q and k hold e4m3 codes.
-template <int D, int TQ, bool CHUNKED, bool QK8>
+// ragged rows of q/o, K/V read through a page table (see PrefillArgs).  MODE 0: bf16; 1 (QK8): q and k hold
+// e4m3 codes, QK^T on the fp8 MFMA; 2 (KV8, chunked only): the K/V pages hold e4m3 codes.
+template <int D, int TQ, bool CHUNKED, int MODE>
 __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr bool QK8 = MODE == 1, KV8 = MODE == 2;
   static_assert(!(CHUNKED && QK8), "8-bit scores are implemented for the contiguous prefill only");
+  static_assert(!KV8 || CHUNKED, "the 8-bit cache is implemented for the chunked prefill");
   constexpr int NW = TQ / 32;             // waves per workgroup
-  constexpr int ROWB = 2 * D;             // bytes per key row of a V tile in LDS
-  constexpr int ESK = QK8 ? 1 : 2;        // bytes per Q/K element
+  constexpr int ROWB = (KV8 ? 1 : 2) * D; // bytes per key row of a V tile in LDS
+  constexpr int ESK = QK8 || KV8 ? 1 : 2; // bytes per K element
+  constexpr int ESQ = QK8 ? 1 : 2;        // bytes per Q element
   constexpr int ROWK = ESK * D;           // bytes per key row of a K tile in LDS
   constexpr int KSTEPS = QK8 ? D / 64 : D / 16;  // k-steps of the QK^T MFMA
   constexpr int CB = D / 32;              // 32-channel blocks of the output
@@ -112,14 +126,15 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   static_assert(IPW >= 1 && kTK * ROWB % (1024 * NW) == 0, "tile split");
   static_assert(IPWK >= 1 && kTK * ROWK % (1024 * NW) == 0, "tile split");
   constexpr int AHEAD = 2;                // MFMAs an LDS operand read runs ahead of its use
-  auto swzk = [](int r) { return QK8 ? swz_k8<D>(r) : swz_k<D>(r); };
+  auto swzk = [](int r) { return QK8 || KV8 ? swz_k8<D>(r) : swz_k<D>(r); };
+  auto swzv = [](int r) { return KV8 ? swz_v8<D>(r) : swz_v<D>(r); };
 
   // separate arrays per buffer: the wait-count pass then sees that a load into one buffer does not
   // alias reads of the other
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kTK * ROWK / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kTK * ROWK / 2];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kTK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kTK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kTK * ROWB / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kTK * ROWB / 2];
   __shared__ uint32_t votes[2][NW];
   __shared__ float wave_gap[2][NW];
 
@@ -160,19 +175,28 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   // ---- buffer resources: one (b, head) slice each (chunked: K/V per tile, below); bytes past the last row
   // read as zero (also for the direct-to-LDS loads)
   // bytes spanned by rows [0, n) of a Q/K slice with row stride ss elements
-  auto qk_rows_bytes = [&](int n, int64_t ss) { return n <= 0 ? 0u : (uint32_t)(((int64_t)(n - 1) * ss + D) * ESK); };
+  auto qk_rows_bytes = [&](int n, int64_t ss, int es) {
+    return n <= 0 ? 0u : (uint32_t)(((int64_t)(n - 1) * ss + D) * es);
+  };
   const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q);
   const uint8_t* k8 = reinterpret_cast<const uint8_t*>(a.k);
   const rsrc_t rq = CHUNKED ? make_rsrc(a.q + (int64_t)qrow0 * a.q_ss + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D))
-                            : make_rsrc(q8 + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ESK, qk_rows_bytes(S, a.q_ss));
-  const rsrc_t rk = make_rsrc(k8 + ((int64_t)b * a.k_sb + (int64_t)g * a.k_sh) * ESK, CHUNKED ? 0u : qk_rows_bytes(S, a.k_ss));
+                            : make_rsrc(q8 + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ESQ, qk_rows_bytes(S, a.q_ss, ESQ));
+  const rsrc_t rk = make_rsrc(k8 + ((int64_t)b * a.k_sb + (int64_t)g * a.k_sh) * ESK,
+                              CHUNKED ? 0u : qk_rows_bytes(S, a.k_ss, ESK));
   const rsrc_t rv = make_rsrc(a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh, CHUNKED ? 0u : rows_bytes(S, a.v_ss, D));
   // chunked: the resource of key tile t of this KV head (rows past Sk and bad page ids read as zero)
   auto page_rsrc = [&](const uint16_t* pool, const int32_t* pages, int64_t pool_pages, int64_t sb, int64_t sh,
                        int64_t ss, int t) {
     const int pg = __builtin_amdgcn_readfirstlane(load_uniform_i32(pages, (int64_t)b * a.max_pages + t));
     if (pg < 0 || pg >= pool_pages) return make_rsrc(pool, 0u);
-    return make_rsrc(pool + (int64_t)pg * sb + (int64_t)g * sh, rows_bytes(min(kTK, Sk - t * kTK), ss, D));
+    if constexpr (KV8) {  // pools of e4m3 codes: strides count bytes
+      const int n = min(kTK, Sk - t * kTK);
+      return make_rsrc(reinterpret_cast<const uint8_t*>(pool) + (int64_t)pg * sb + (int64_t)g * sh,
+                       n <= 0 ? 0u : (uint32_t)((int64_t)(n - 1) * ss + D));
+    } else {
+      return make_rsrc(pool + (int64_t)pg * sb + (int64_t)g * sh, rows_bytes(min(kTK, Sk - t * kTK), ss, D));
+    }
   };
 
   // ---- Q operand: lane (col, half) holds Q[row][ks*16 + half*8 .. +8] for every k-step (QK8: the 32
@@ -182,7 +206,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   bf16x8 qreg[QK8 ? 1 : KSTEPS];
   i32x8 qreg8[QK8 ? KSTEPS : 1];
   {
-    const uint32_t qoff = row_ok ? (uint32_t)iq * (uint32_t)(a.q_ss * ESK) + half * (QK8 ? 32 : 16) : 0xffffffffu;
+    const uint32_t qoff = row_ok ? (uint32_t)iq * (uint32_t)(a.q_ss * ESQ) + half * (QK8 ? 32 : 16) : 0xffffffffu;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       if constexpr (QK8) {
@@ -202,13 +226,15 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int RPLK = 1024 / ROWK;  // the same for K
   const int lrow = lane / (ROWB / 16), lpos = lane % (ROWB / 16);
   const int lrowk = lane / (ROWK / 16), lposk = lane % (ROWK / 16);
-  const uint32_t k_row_bytes = (uint32_t)(a.k_ss * ESK), v_row_bytes = (uint32_t)(a.v_ss * 2);
+  const uint32_t k_row_bytes = (uint32_t)(a.k_ss * ESK), v_row_bytes = (uint32_t)(a.v_ss * (KV8 ? 1 : 2));
   const uint32_t k_tile_bytes = kTK * k_row_bytes, v_tile_bytes = kTK * v_row_bytes;
   // Row (w*IPW + i)*RPL + lrow: every swizzle splits into a per-lane part and a part of the load index
   // (their bit fields do not overlap), so the chunk offset is (lane part) ^ (uniform part).
   uint32_t k_dma = (uint32_t)(w * IPWK * RPLK + lrowk) * k_row_bytes;   // row part of this lane's K loads
   uint32_t k_dmx = (uint32_t)(lposk ^ swzk(lrowk)) * 16;                // chunk part
-  uint32_t v_dma = (uint32_t)(w * IPW * RPL + lrow) * v_row_bytes + (uint32_t)(lpos ^ swz_v<D>(lrow)) * 16;
+  // bf16: row part + chunk part in one offset (the V swizzle has no load-index part); KV8: kept apart
+  uint32_t v_dma = (uint32_t)(w * IPW * RPL + lrow) * v_row_bytes + (KV8 ? 0u : (uint32_t)(lpos ^ swzv(lrow)) * 16);
+  uint32_t v_dmx = KV8 ? (uint32_t)(lpos ^ swzv(lrow)) * 16 : 0u;
   auto load_k_rsrc = [&](uint16_t* dst, rsrc_t r, uint32_t toff) {
 #pragma unroll
     for (int i = 0; i < IPWK; ++i) {
@@ -218,15 +244,17 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
   auto load_v_rsrc = [&](uint16_t* dst, rsrc_t r, uint32_t toff) {
-    static_assert(D == 128 || D == 64, "the V swizzle has no load-index part for these widths");
+    static_assert(D == 128 || D == 64, "the bf16 V swizzle has no load-index part for these widths");
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const uint32_t vo = v_dma + (uint32_t)(i * RPL) * v_row_bytes + toff;
+      // 8-bit V tiles at D = 128: the swizzle's bit 1 comes from the load index (wave-uniform)
+      const uint32_t cx = KV8 ? (uint32_t)swzv((w * IPW + i) * RPL) * 16 : 0u;
+      const uint32_t vo = v_dma + (KV8 ? (v_dmx ^ cx) : 0u) + (uint32_t)(i * RPL) * v_row_bytes + toff;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + (w * IPW + i) * 512), 16, vo, 0, 0, 0);
     }
   };
   auto load_k = [&](uint16_t* dst, int t) {
-    if constexpr (CHUNKED && !QK8) load_k_rsrc(dst, page_rsrc(a.k, a.k_pages, a.k_pool_pages, a.k_sb, a.k_sh, a.k_ss, t), 0u);
+    if constexpr (CHUNKED) load_k_rsrc(dst, page_rsrc(a.k, a.k_pages, a.k_pool_pages, a.k_sb, a.k_sh, a.k_ss, t), 0u);
     else load_k_rsrc(dst, rk, (uint32_t)t * k_tile_bytes);
   };
   auto load_v = [&](uint16_t* dst, int t) {
@@ -240,8 +268,11 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   // (kb*32 + col)*ROWB + 16*((2ks + half) ^ swz_k(col)) = (k_opb ^ 32*ks) + kb*32*ROWB.
   // QK8: lane (col, half) reads row kb*32 + col, logical chunks 4ks + 2half and 4ks + 2half + 1 (32 codes),
   // i.e. bytes (kb*32 + col)*D + 16*((4ks + 2half + j) ^ swz_k8(col)) = (k_opb ^ 16*(4ks + j)) + kb*32*D.
+  // KV8: lane (col, half) reads 8 codes of row kb*32 + col, channels ks*16 + half*8 .. +8, i.e. byte
+  // (kb*32 + col)*D + 16*(ks ^ swz_k8(col)) + 8*half = (k_opb ^ 16*ks) + kb*32*D.
   const int xk = swzk(col);
   uint32_t k_opb = QK8 ? (uint32_t)(col * ROWK + 16 * ((2 * half) ^ xk))
+                 : KV8 ? (uint32_t)(col * ROWK + 16 * xk + 8 * half)
                        : (uint32_t)(col * ROWB + 32 * (xk >> 1) + 16 * (half ^ (xk & 1)));
   // V^T (O^T's A operand) by transposing reads: in each 16-lane group, lane 4j + m names 4 channels
   // (4m .. 4m+3 of the group's 16) of key row k0 + j and receives channel (lane & 15) of the 4 rows.
@@ -251,9 +282,19 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   const int gq = lane >> 4, li = lane & 15;
   const int vrow = li >> 2;                       // row inside the 4-row gather
   const int vch = 16 * (gq & 1) + 4 * (li & 3);   // channel inside the 32-channel block
-  uint32_t v_opb = (uint32_t)(vrow * ROWB + 64 * (swz_v<D>(vrow) >> 2) + 16 * (vch >> 3) + 2 * (vch & 7));
+  // KV8: an 8-bit transposing read gathers 8 rows per 16-lane group; lane 2j + m names row vkey(j) (the S^T
+  // accumulator's key order: 4hf + j, then 8 + 4hf + j - 4) and codes 8m..8m+7 of the group's 16 channels
+  // (logical chunk 2cb + (gq & 1)); byte (v_opb ^ 32*cb) + 16*st*D.
+  const int vj = li >> 1, vkey = (vj < 4 ? 0 : 4) + 4 * (gq >> 1) + vj;
+  uint32_t v_opb = KV8 ? (uint32_t)(vkey * ROWB + 16 * ((gq & 1) ^ swz_v8<D>(vkey)) + 8 * (li & 1))
+                       : (uint32_t)(vrow * ROWB + 64 * (swz_v<D>(vrow) >> 2) + 16 * (vch >> 3) + 2 * (vch & 7));
   auto kop = [&](const uint16_t* kl, int ks, int kb) {
-    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kl) + ((k_opb ^ (32u * ks)) + kb * 32 * ROWB));
+    if constexpr (KV8) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(kl) + ((k_opb ^ (16u * ks)) + kb * 32 * ROWK));
+      return fp8x8_to_bf16x8(x);
+    } else {
+      return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kl) + ((k_opb ^ (32u * ks)) + kb * 32 * ROWB));
+    }
   };
   auto kop8 = [&](const uint16_t* kl, int ks, int kb) {
     const char* base = reinterpret_cast<const char*>(kl) + kb * 32 * ROWK;
@@ -262,16 +303,26 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   auto vop = [&](const uint16_t* vl, int cb, int st) {
-    // the S^T accumulator layout that P^T comes from: half hf holds keys 4hf..4hf+3 and 8+4hf..8+4hf+3
-    // of each 16-key step
-    const char* base = reinterpret_cast<const char*>(vl) + (v_opb ^ (64u * cb)) + (16 * st + 4 * (gq >> 1)) * ROWB;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)base);
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + 8 * ROWB));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (KV8) {
+      typedef int v2i __attribute__((ext_vector_type(2)));
+      const char* base = reinterpret_cast<const char*>(vl) + (v_opb ^ (32u * cb)) + 16 * st * ROWB;
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)base);
+      return as_bf16x8(fp8x8_to_bf16x8(u32x2{(uint32_t)x[0], (uint32_t)x[1]}));
+    } else {
+      // the S^T accumulator layout that P^T comes from: half hf holds keys 4hf..4hf+3 and 8+4hf..8+4hf+3
+      // of each 16-key step
+      const char* base = reinterpret_cast<const char*>(vl) + (v_opb ^ (64u * cb)) + (16 * st + 4 * (gq >> 1)) * ROWB;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)base);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + 8 * ROWB));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
   };
   // opaque copies of the per-lane bases, taken once per tile, so that the addresses derived from them are
   // formed next to their use instead of being kept in registers across the loop
-  auto refresh = [&]() { asm volatile("" : "+v"(k_opb), "+v"(v_opb), "+v"(k_dma), "+v"(k_dmx), "+v"(v_dma)); };
+  auto refresh = [&]() {
+    asm volatile("" : "+v"(k_opb), "+v"(v_opb), "+v"(k_dma), "+v"(k_dmx), "+v"(v_dma));
+    if constexpr (KV8) asm volatile("" : "+v"(v_dmx));
+  };
 
   // ---- running state of this lane's query row
   f32x16 acc[CB];
@@ -484,7 +535,8 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 
   // ---- epilogue: O = acc / l, bf16
   const float l_tot = pair_sum(l_part);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // KV8: the values are v_scale * code
+  const float inv = l_tot > 0.f ? (KV8 ? a.v_scale : 1.f) / l_tot : 0.f;
   if (row_ok) {
     uint16_t* op = a.o + (CHUNKED ? (int64_t)(qrow0 + iq) * a.o_ss : (int64_t)b * a.o_sb + (int64_t)iq * a.o_ss) +
                    (int64_t)h * a.o_sh;
@@ -513,17 +565,18 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, bool qk8, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, int mode, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hq * a.nqt);
   if (grid == 0) return hipSuccess;
-  if (chunked && qk8) return hipErrorInvalidValue;
+  if (chunked ? mode == 1 : mode == 2) return hipErrorInvalidValue;
   const dim3 blk(tile_q * 2);
-#define SSM_PREFILL_LAUNCH(D, TQ)                                                                            \
-  if (d == D && tile_q == TQ) {                                                                              \
-    if (chunked) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, false>), dim3(grid), blk, 0, stream, a);    \
-    else if (qk8) hipLaunchKernelGGL((prefill_kernel<D, TQ, false, true>), dim3(grid), blk, 0, stream, a);   \
-    else hipLaunchKernelGGL((prefill_kernel<D, TQ, false, false>), dim3(grid), blk, 0, stream, a);           \
-    return hipGetLastError();                                                                                \
+#define SSM_PREFILL_LAUNCH(D, TQ)                                                                                \
+  if (d == D && tile_q == TQ) {                                                                                  \
+    if (chunked && mode == 2) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 2>), dim3(grid), blk, 0, stream, a); \
+    else if (chunked) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 0>), dim3(grid), blk, 0, stream, a);       \
+    else if (mode == 1) hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 1>), dim3(grid), blk, 0, stream, a);    \
+    else hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 0>), dim3(grid), blk, 0, stream, a);                   \
+    return hipGetLastError();                                                                                    \
   }
   SSM_PREFILL_LAUNCH(128, 128)
   SSM_PREFILL_LAUNCH(128, 64)

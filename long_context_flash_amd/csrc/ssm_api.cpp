@@ -159,12 +159,13 @@ static int prefill_impl(const ssm_tensor* q, const ssm_tensor* k, const ssm_tens
   a.scale = lscale;
   a.scale_log2 = lscale * 1.4426950408889634f;
   a.tau_raw = std::isinf(tau) ? tau : tau / lscale;
+  a.v_scale = 1.f;
   if (skip_stats) {
     a.tile_state = skip_stats->tile_state;
     a.unit_gap = skip_stats->unit_gap;
     a.counters = skip_stats->counters;
   }
-  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, false, qk8, static_cast<hipStream_t>(stream)));
+  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, false, qk8 ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 
 int ssm_prefill(const ssm_tensor* q, const ssm_tensor* k, const ssm_tensor* v, int32_t seqlen, int32_t causal,
@@ -309,8 +310,8 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
   if ((rc = check_cache(k_cache, "k_cache", batch, d, &kcap, &krows, &hk)) ||
       (rc = check_cache(v_cache, "v_cache", batch, d, &vcap, &vrows, &hv)))
     return rc;
-  if (k_cache->pool.dtype != SSM_BF16 || v_cache->pool.dtype != SSM_BF16)
-    return fail(SSM_EUNSUPPORTED, "chunked prefill reads bf16 caches");
+  if (k_cache->pool.dtype != v_cache->pool.dtype) return fail(SSM_EINVAL, "k and v caches must share one dtype");
+  const bool kv8 = k_cache->pool.dtype == SSM_FP8_E4M3;
   if (k_cache->max_pages != v_cache->max_pages) return fail(SSM_EINVAL, "k and v page tables differ in length");
   if (hk != hv) return fail(SSM_EINVAL, "k/v head counts differ");
   const int64_t Hkv = hk;
@@ -352,9 +353,13 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
   a.causal = causal != 0;
   const int64_t groups = (int64_t)batch * Hkv;
   a.xcd_groups = groups % 8 == 0 ? (int)(groups / 8) : 0;
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.tau_raw = std::isinf(tau) ? tau : tau / scale;
+  // an fp8 cache: the key scale joins the logit scale, the value scale the output
+  const float lscale = kv8 ? scale * k_cache->scale : scale;
+  if (!(lscale > 0.f) || !std::isfinite(lscale)) return fail(SSM_EINVAL, "scale * k_scale out of range");
+  a.scale = lscale;
+  a.scale_log2 = lscale * 1.4426950408889634f;
+  a.tau_raw = std::isinf(tau) ? tau : tau / lscale;
+  a.v_scale = kv8 ? v_cache->scale : 1.f;
   if (skip_stats) {
     a.tile_state = skip_stats->tile_state;
     a.unit_gap = skip_stats->unit_gap;
@@ -368,7 +373,7 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
   a.total_q = (int)total_q;
   a.k_pool_pages = krows;
   a.v_pool_pages = vrows;
-  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, true, false, static_cast<hipStream_t>(stream)));
+  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, true, kv8 ? 2 : 0, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

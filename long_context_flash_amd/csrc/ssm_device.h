@@ -68,6 +68,21 @@ __device__ __forceinline__ int load_uniform_i32(const int32_t* p, int64_t i) {
   return ((cptr)p)[i];
 }
 
+// Two OCP fp8 e4m3 codes (bytes 0-1, or 2-3 when hi, of w) as two packed bf16, with gfx950's
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1: exact, since every e4m3 value has at most four significant bits
+// and an exponent inside bf16's range.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+// Eight e4m3 codes (bytes 0..7 of x) as eight bf16
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 x) {
+  return u32x4{fp8x2_to_bf16x2(x[0], false), fp8x2_to_bf16x2(x[0], true), fp8x2_to_bf16x2(x[1], false),
+               fp8x2_to_bf16x2(x[1], true)};
+}
+
 // ---- buffer loads: a resource covers [base, base + num_bytes); dwords outside read as 0.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data format)

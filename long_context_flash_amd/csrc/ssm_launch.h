@@ -21,6 +21,7 @@ struct PrefillArgs {
   float scale;               // softmax scale (natural-log logits = scale * q.k)
   float scale_log2;          // scale * log2(e)
   float tau_raw;             // tau / scale: threshold on raw q.k gaps; -inf never skips
+  float v_scale;             // e4m3 V pages (mode 2): value = v_scale * code
   uint8_t* tile_state;       // nullable [units, nkt]
   float* unit_gap;           // nullable [units, nkt]
   unsigned long long* counters;  // nullable [4]
@@ -65,7 +66,8 @@ struct DecodeArgs {
   unsigned long long* counters;
 };
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, bool qk8, hipStream_t stream);
+// mode 0: bf16; 1: e4m3 q/k scores (contiguous only); 2: e4m3 K/V pages (chunked only)
+hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, int mode, hipStream_t stream);
 hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
                               hipStream_t stream);
 

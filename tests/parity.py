@@ -331,10 +331,41 @@ def chunk_batch(w, seqs, seed=0, extra_pages=3):
             "kv_lens": np.array([nk for _, nk in seqs], np.int32), "max_q": max(nq for nq, _ in seqs)}
 
 
-def run_prefill_paged_gpu(cb, *, Hq, causal, tau, tile_q, device="cuda"):
+def fp8_pools(cb):
+    """e4m3 copies of a chunk_batch()'s K/V pools with amax/448 scales (the fp8 cache a decode reads):
+    k_pool, v_pool (uint8 codes), k_scale, v_scale."""
+    import synth as _synth
+    out = {}
+    for name in ("k", "v"):
+        amax = float(np.abs(_synth.bf16_bits_to_f32(cb[f"{name}_pool"])).max(initial=0.0))
+        scale = float(np.float32(amax / _synth.FP8_E4M3_MAX)) if amax > 0 else 1.0
+        out[f"{name}_scale"] = scale
+        out[f"{name}_pool"] = _synth.quantize_fp8_e4m3(cb[f"{name}_pool"], scale)
+    return out
+
+
+def seq_kv_fp8(cb, f8, b):
+    """float64 K/V [1, n_k, Hkv, d] of sequence b, dequantised from the fp8 pools (torch's float8_e4m3fn
+    decoding times the scales), gathered through its page table."""
+    nk = int(cb["kv_lens"][b])
+    pages = cb["page_table"][b, :-(-nk // 64)]
+    res = []
+    for name in ("k", "v"):
+        x = dequant_fp8(f8[f"{name}_pool"][pages], f8[f"{name}_scale"])  # [np, Hkv, 64, d]
+        res.append(np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(1, -1, x.shape[1], x.shape[3])[:, :nk]))
+    return res
+
+
+def run_prefill_paged_gpu(cb, *, Hq, causal, tau, tile_q, device="cuda", fp8=None):
+    """fp8: the fp8_pools() of cb (the GPU then reads the e4m3 pools with their scales)."""
     q = ssm.bf16_from_bits(cb["q"], device)
-    kc = ssm.bf16_from_bits(cb["k_pool"], device)
-    vc = ssm.bf16_from_bits(cb["v_pool"], device)
+    if fp8 is not None:
+        kc, vc = fp8_device(fp8["k_pool"], device), fp8_device(fp8["v_pool"], device)
+        scales = dict(k_scale=fp8["k_scale"], v_scale=fp8["v_scale"])
+    else:
+        kc = ssm.bf16_from_bits(cb["k_pool"], device)
+        vc = ssm.bf16_from_bits(cb["v_pool"], device)
+        scales = {}
     pt = torch.from_numpy(cb["page_table"]).to(device)
     qs = torch.from_numpy(cb["q_start"]).to(device)
     kl = torch.from_numpy(cb["kv_lens"]).to(device)
@@ -342,19 +373,21 @@ def run_prefill_paged_gpu(cb, *, Hq, causal, tau, tile_q, device="cuda"):
     nqt = -(-cb["max_q"] // tile_q)
     stats = ssm.SkipStats.alloc(B * Hq * nqt, pt.shape[1], device, gaps=True)
     out = ssm.ssm_prefill_paged(q, kc, vc, pt, qs, kl, cb["max_q"], causal=causal, tau=tau, skip_stats=stats,
-                                tile_q=tile_q)
+                                tile_q=tile_q, **scales)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
             stats.counters.cpu().numpy())
 
 
-def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads=None, sample=None):
+def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads=None, sample=None, fp8=None):
     """GPU chunked prefill on the whole ragged batch vs the oracle on each sequence (all its units, or the
-    (h, q_tile) pairs listed in sample[b])."""
+    (h, q_tile) pairs listed in sample[b]).  fp8: the fp8_pools() of cb; the oracle then reads the
+    dequantised pools (every e4m3 value is exact in bf16, so the plain bar applies)."""
     seqs = cb["seqs"]
     B = len(seqs)
-    log(f"{where}: GPU chunked prefill seqs={seqs} Hq={Hq} causal={causal} tau={tau} tile_q={tile_q}")
-    out, st, gap, cnt = run_prefill_paged_gpu(cb, Hq=Hq, causal=causal, tau=tau, tile_q=tile_q)
+    log(f"{where}: GPU chunked prefill seqs={seqs} Hq={Hq} causal={causal} tau={tau} tile_q={tile_q} "
+        f"fp8={fp8 is not None}")
+    out, st, gap, cnt = run_prefill_paged_gpu(cb, Hq=Hq, causal=causal, tau=tau, tile_q=tile_q, fp8=fp8)
     vis, skipped = int((st > 0).sum()), int((st == 2).sum())
     assert list(cnt) == [vis, skipped, vis, vis - skipped], f"{where}: counters {list(cnt)} vs tile_state"
     nqt_max = -(-cb["max_q"] // tile_q)
@@ -374,8 +407,13 @@ def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads
         else:
             ounits = None
             u = rows[:, :nqt].ravel()
-        ref = oracle.prefill(qb, dat["k"], dat["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
-                             units=ounits, threads=threads)
+        if fp8 is not None:
+            qb = (qb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            kb, vb = seq_kv_fp8(cb, fp8, b)
+        else:
+            kb, vb = dat["k"], dat["v"]
+        ref = oracle.prefill(qb, kb, vb, causal=causal, tau=tau, tile_q=tile_q, tile_k=64, units=ounits,
+                             threads=threads)
         nkt = ref["state"].shape[1]
         st_g = st[u][:, :nkt]
         assert not st[u][:, nkt:].any(), f"{where}: key tiles past sequence {b} marked visited"
@@ -383,8 +421,8 @@ def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads
         compare_gaps(gap[u][:, :nkt], ref["gamma"], ref["state"], f"{where} seq {b}")
         if flips.any():
             ov = np.where(flips, np.where(st_g == 2, 1, 0), -1).astype(np.int8)
-            ref = oracle.prefill(qb, dat["k"], dat["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
-                                 units=ounits, override=ov, threads=threads)
+            ref = oracle.prefill(qb, kb, vb, causal=causal, tau=tau, tile_q=tile_q, tile_k=64, units=ounits,
+                                 override=ov, threads=threads)
         got = np.zeros_like(ref["out"])
         q0 = cb["q_start"][b]
         pairs = [(h, qt) for h in range(Hq) for qt in range(nqt)] if sample is None else [tuple(x) for x in hq]

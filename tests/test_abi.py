@@ -300,7 +300,8 @@ def call_prefill_paged(lib, q=None, kc=None, vc=None, q_start=FAKE, kv_lens=FAKE
 @pytest.mark.parametrize("case,code", [
     ("contiguous_cache", ssm.SSM_EINVAL), ("null_q_start", ssm.SSM_EINVAL), ("null_kv_lens", ssm.SSM_EINVAL),
     ("neg_batch", ssm.SSM_EINVAL), ("pos_tau", ssm.SSM_EINVAL), ("page_tables_differ", ssm.SSM_EINVAL),
-    ("fp8_cache", ssm.SSM_EUNSUPPORTED), ("head_dim", ssm.SSM_EUNSUPPORTED), ("tile_q", ssm.SSM_EUNSUPPORTED),
+    ("fp8_k_bf16_v", ssm.SSM_EINVAL), ("fp8_zero_scale", ssm.SSM_EINVAL), ("fp8_stride", ssm.SSM_EUNSUPPORTED),
+    ("head_dim", ssm.SSM_EUNSUPPORTED), ("tile_q", ssm.SSM_EUNSUPPORTED),
     ("gqa", ssm.SSM_EINVAL), ("out_shape", ssm.SSM_EINVAL),
 ])
 def test_prefill_paged_rejects(lib, case, code):
@@ -317,9 +318,15 @@ def test_prefill_paged_rejects(lib, case, code):
         kw["tau"] = 0.5
     elif case == "page_tables_differ":
         kw["vc"] = cache([100, 2, 64, 128], paged=True, max_pages=32)
-    elif case == "fp8_cache":
+    elif case == "fp8_k_bf16_v":
         kw["kc"] = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=ssm.SSM_FP8_E4M3, scale=1.0)
-        kw["vc"] = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=ssm.SSM_FP8_E4M3, scale=1.0)
+    elif case == "fp8_zero_scale":
+        kw["kc"] = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=ssm.SSM_FP8_E4M3, scale=1.0)
+        kw["vc"] = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=ssm.SSM_FP8_E4M3, scale=0.0)
+    elif case == "fp8_stride":  # 136 codes per row: not a multiple of 16 bytes
+        st = [2 * 64 * 136, 64 * 136, 136, 1]
+        kw["kc"] = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=ssm.SSM_FP8_E4M3, scale=1.0, stride=st)
+        kw["vc"] = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=ssm.SSM_FP8_E4M3, scale=1.0, stride=st)
     elif case == "head_dim":
         kw["q"], kw["o"] = desc([300, 16, 96]), desc([300, 16, 96])
         kw["kc"] = cache([100, 2, 64, 96], paged=True, max_pages=64)

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from parity import chunk_batch, check_prefill_paged, run_prefill_paged_gpu
+from parity import chunk_batch, check_prefill_paged, fp8_pools, run_prefill_paged_gpu
 
 LN1000 = math.log(1000.0)
 pytestmark = pytest.mark.gpu
@@ -59,4 +59,37 @@ def test_chunk_8k_of_128k_sampled():
     sample = {0: [(0, 0), (9, 1), (17, 31), (40, 62), (63, 63)]}
     r = check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=w.taus[0], tile_q=128, sample=sample,
                             where="chunked 8k of 128k")
+    assert r["sparsity"] > 0.3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tile_q", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_batch_fp8_cache(d, tile_q, causal):
+    """The ragged batch over an fp8 e4m3 cache (amax/448 scales, the pools a decode reads); the oracle reads
+    the dequantised pools."""
+    w = synth.replace(SMALL, d=d)
+    seqs = [(129, 700), (1, 65), (300, 300), (63, 1000), (0, 77), (200, 263)]
+    cb = chunk_batch(w, seqs, seed=5)
+    f8 = fp8_pools(cb)
+    for tau in (-LN1000, -math.inf):
+        check_prefill_paged(cb, Hq=w.Hq, causal=causal, tau=tau, tile_q=tile_q, fp8=f8,
+                            where=f"chunked fp8 d={d} tq={tile_q} causal={causal} tau={tau}")
+
+
+def test_llama_shape_long_context_chunk_fp8_cache():
+    w = synth.replace(synth.PREFILL_16K, S=0, seed=311)
+    cb = chunk_batch(w, [(2048, 16384), (1024, 4096)], seed=6)
+    r = check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=w.taus[2], tile_q=128, fp8=fp8_pools(cb),
+                            where="chunked fp8 llama 16k")
+    assert r["sparsity"] > 0.3
+
+
+def test_chunk_8k_of_128k_sampled_fp8_cache():
+    """The benchmark's chunked workload over an fp8 cache; sampled units."""
+    w = synth.PREFILL_128K
+    cb = chunk_batch(w, [(8192, w.S)], seed=4)
+    sample = {0: [(0, 0), (17, 31), (63, 63)]}
+    r = check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=w.taus[0], tile_q=128, sample=sample, fp8=fp8_pools(cb),
+                            where="chunked fp8 8k of 128k")
     assert r["sparsity"] > 0.3
