@@ -69,3 +69,33 @@ def test_prefill_128k_sampled():
                       units=units, fp8qk=f8, where="fp8qk 128k")
     log(f"fp8qk 128k: sparsity {r['sparsity']:.3f}")
     assert r["sparsity"] >= 0.45
+
+
+def test_strided_views_match_contiguous():
+    """e4m3 q/k and bf16 v/out as views into wider buffers (rows padded by 32 elements, one spare head): the
+    same bits as contiguous tensors."""
+    import torch
+    import long_context_flash_amd as ssm
+    from parity import fp8_device
+    w = synth.replace(synth.PREFILL_16K, S=600, Hq=8, Hkv=2, d=128, seed=13)
+    data, f8 = _case(w)
+    dev = "cuda"
+    q8, k8 = fp8_device(f8["q"], dev), fp8_device(f8["k"], dev)
+    v = ssm.bf16_from_bits(data["v"], dev)
+    ref = ssm.ssm_prefill_fp8qk(q8, f8["q_scale"], k8, f8["k_scale"], v, causal=True, tau=-LN1000)
+
+    def padded(t):
+        B, S, H, d = t.shape
+        big = torch.zeros(B, S, H + 1, d + 32, dtype=torch.uint8 if t.dtype == torch.float8_e4m3fn else t.dtype,
+                          device=dev)
+        if t.dtype == torch.float8_e4m3fn:
+            big = big.view(torch.float8_e4m3fn)
+        view = big[:, :, :H, :d]
+        view.copy_(t)
+        return view
+
+    out = padded(torch.zeros(ref.shape, dtype=ref.dtype, device=dev))
+    ssm.ssm_prefill_fp8qk(padded(q8), f8["q_scale"], padded(k8), f8["k_scale"], padded(v), causal=True, tau=-LN1000,
+                          out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "strided views changed the result"
