@@ -370,7 +370,28 @@ def time_chunked_prefill(ssm, torch, np, w, data, tau, steps, dev):
     res["fp8_cache"] = {"ms": round(ms8, 3), "dense_tflops": round(dense / (ms8 / 1e3) / 1e12, 2),
                         "sparsity": round(float(c8[1]) / float(c8[0]), 4), "k_scale": ks, "v_scale": vs,
                         "speedup_vs_bf16_cache": round(ms / ms8, 3)}
-    del pool_k, pool_v, k8, v8, q, out
+    # and with the queries as e4m3 codes too (amax/448), QK^T on the fp8 MFMA (ssm_prefill_paged_fp8qk)
+    qamax = float(q.abs().max().float())
+    qsc = float(np.float32(qamax / 448.0)) if qamax > 0 else 1.0
+    q8 = (q.float() / qsc).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+    cnt88 = torch.zeros(4, dtype=torch.int64, device=dev)
+    run88 = lambda: ssm.ssm_prefill_paged_fp8qk(q8, qsc, k8, v8, pt, qs, kl, nq, k_scale=ks, v_scale=vs, causal=True,
+                                                tau=tau, out=out, skip_stats=ssm.SkipStats(counters=cnt88),
+                                                tile_q=w.tile_q)
+    run88()
+    torch.cuda.synchronize()
+    cnt88.zero_()
+    for i in range(steps):
+        ev[i][0].record()
+        run88()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms88 = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    c88 = cnt88.cpu().numpy() / steps
+    res["fp8_qk_fp8_cache"] = {"ms": round(ms88, 3), "dense_tflops": round(dense / (ms88 / 1e3) / 1e12, 2),
+                               "sparsity": round(float(c88[1]) / float(c88[0]), 4), "q_scale": qsc,
+                               "speedup_vs_bf16_cache": round(ms / ms88, 3)}
+    del pool_k, pool_v, k8, v8, q, q8, out
     return res
 
 

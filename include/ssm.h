@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 enum {
   SSM_OK = 0,
@@ -173,6 +173,15 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
                       const int32_t* q_start, const int32_t* kv_lens, int32_t batch, int32_t max_q_len,
                       int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
                       const ssm_opts* opts);
+
+/* ssm_prefill_paged with 8-bit queries over e4m3 pages (the serving path of an fp8 cache): q [total_q, Hq, d]
+ * holds SSM_FP8_E4M3 codes with dequantisation factor q_scale (finite, > 0); the K and V pools must be
+ * SSM_FP8_E4M3 (see ssm_kv_cache).  The scores run on the FP8 matrix instructions straight from the 8-bit key
+ * pages (as ssm_prefill_fp8qk); V and P*V stay bf16.  Everything else as ssm_prefill_paged. */
+int ssm_prefill_paged_fp8qk(const ssm_tensor* q, float q_scale, const ssm_kv_cache* k_cache,
+                            const ssm_kv_cache* v_cache, const int32_t* q_start, const int32_t* kv_lens, int32_t batch,
+                            int32_t max_q_len, int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats,
+                            void* stream, const ssm_opts* opts);
 
 /* Bytes of device workspace ssm_decode needs (fp32 partial outputs and
  * log-sum-exps per (b, query head, split)).  0 for invalid arguments. */

@@ -28,8 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 SSM_BF16, SSM_FP32, SSM_FP8_E4M3 = 0, 1, 2
-EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_prefill_fp8qk", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes",
-                    "ssm_strerror", "ssm_last_error", "ssm_abi_version")
+EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_prefill_fp8qk", "ssm_decode", "ssm_prefill_paged", "ssm_prefill_paged_fp8qk",
+                    "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -59,7 +59,7 @@ class Opts(ctypes.Structure):
                 ("decode_flags", ctypes.c_int32)]
 
 
-ABI_VERSION = 5               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 6               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
 DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
 
 
@@ -88,6 +88,10 @@ def lib():
     L.ssm_prefill_paged.argtypes = [P(Tensor), P(KvCache), P(KvCache), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P(Tensor), P(SkipStatsC),
                                     ctypes.c_void_p, P(Opts)]
+    L.ssm_prefill_paged_fp8qk.restype = ctypes.c_int
+    L.ssm_prefill_paged_fp8qk.argtypes = [P(Tensor), ctypes.c_float, P(KvCache), P(KvCache), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_float, P(Tensor), P(SkipStatsC), ctypes.c_void_p, P(Opts)]
     L.ssm_decode_workspace_bytes.restype = ctypes.c_size_t
     L.ssm_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 4
     L.ssm_strerror.restype = ctypes.c_char_p
@@ -239,6 +243,36 @@ def ssm_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     return out
 
 
+def ssm_prefill_paged_fp8qk(q: torch.Tensor, q_scale: float, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            page_table: torch.Tensor, q_start: torch.Tensor, kv_lens: torch.Tensor, max_q_len: int,
+                            k_scale: float, v_scale: float, causal: bool = True, tau: float = -math.log(1000.0),
+                            out: Optional[torch.Tensor] = None, skip_stats: Optional[SkipStats] = None, stream=None,
+                            tile_q: int = 128, scale: float = 0.0,
+                            v_page_table: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunked prefill with 8-bit queries over e4m3 pages: q [total_q,Hq,d] torch.float8_e4m3fn codes (query =
+    q_scale * code), k_cache/v_cache [pages,Hkv,64,d] torch.float8_e4m3fn codes with k_scale / v_scale; the rest
+    as ssm_prefill_paged.  out [total_q,Hq,d] bf16."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    for name, t in (("q_start", q_start), ("kv_lens", kv_lens)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    B = kv_lens.shape[0]
+    if q_start.shape[0] != B + 1:
+        raise ValueError("q_start must have batch + 1 entries")
+    kc = _paged_cache(k_cache, page_table, k_scale)
+    vc = _paged_cache(v_cache, page_table if v_page_table is None else v_page_table, v_scale)
+    qd, od = describe(q), describe(out)
+    opts = Opts(float(scale), int(tile_q), 64, 0, None, 0, 0)
+    st = skip_stats.c() if skip_stats is not None else None
+    rc = lib().ssm_prefill_paged_fp8qk(ctypes.byref(qd), float(q_scale), ctypes.byref(kc), ctypes.byref(vc),
+                                       q_start.data_ptr(), kv_lens.data_ptr(), int(B), int(max_q_len),
+                                       int(bool(causal)), float(tau), ctypes.byref(od),
+                                       ctypes.byref(st) if st else None, _stream_handle(stream), ctypes.byref(opts))
+    _check(rc)
+    return out
+
+
 def ssm_decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:
     return int(lib().ssm_decode_workspace_bytes(B, Hq, d, num_splits))
 
@@ -312,6 +346,6 @@ def bf16_from_bits(a, device=None) -> torch.Tensor:
     return t.to(device) if device is not None else t
 
 
-__all__ = ["ssm_prefill", "ssm_prefill_fp8qk", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
+__all__ = ["ssm_prefill", "ssm_prefill_fp8qk", "ssm_prefill_paged_fp8qk", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
            "ssm_abi_version", "SkipStats", "SsmError", "prefill_stats_shape", "decode_workspace", "bf16_from_bits",
            "lib", "describe", "LIB_PATH", "EXPORTED_SYMBOLS"]

@@ -108,11 +108,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // CHUNKED: queries of each sequence are the last ones of its cached keys (bottom-right causal), packed
 // ragged rows of q/o, K/V read through a page table (see PrefillArgs).  MODE 0: bf16; 1 (QK8): q and k hold
-// e4m3 codes, QK^T on the fp8 MFMA; 2 (KV8, chunked only): the K/V pages hold e4m3 codes.
+// e4m3 codes, QK^T on the fp8 MFMA; 2 (KV8, chunked only): the K/V pages hold e4m3 codes; 3 (chunked only):
+// both, i.e. e4m3 queries scored on the fp8 MFMA against e4m3 key pages, V pages converted as in 2.
 template <int D, int TQ, bool CHUNKED, int MODE>
 __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr bool QK8 = MODE == 1, KV8 = MODE == 2;
-  static_assert(!(CHUNKED && QK8), "8-bit scores are implemented for the contiguous prefill only");
+  constexpr bool QK8 = MODE == 1 || MODE == 3, KV8 = MODE == 2 || MODE == 3;
+  static_assert(!(CHUNKED && QK8 && !KV8), "8-bit scores over bf16 pages are not implemented");
   static_assert(!KV8 || CHUNKED, "the 8-bit cache is implemented for the chunked prefill");
   constexpr int NW = TQ / 32;             // waves per workgroup
   constexpr int ROWB = (KV8 ? 1 : 2) * D; // bytes per key row of a V tile in LDS
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   };
   const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q);
   const uint8_t* k8 = reinterpret_cast<const uint8_t*>(a.k);
-  const rsrc_t rq = CHUNKED ? make_rsrc(a.q + (int64_t)qrow0 * a.q_ss + (int64_t)h * a.q_sh, rows_bytes(S, a.q_ss, D))
+  const rsrc_t rq = CHUNKED ? make_rsrc(q8 + ((int64_t)qrow0 * a.q_ss + (int64_t)h * a.q_sh) * ESQ, qk_rows_bytes(S, a.q_ss, ESQ))
                             : make_rsrc(q8 + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ESQ, qk_rows_bytes(S, a.q_ss, ESQ));
   const rsrc_t rk = make_rsrc(k8 + ((int64_t)b * a.k_sb + (int64_t)g * a.k_sh) * ESK,
                               CHUNKED ? 0u : qk_rows_bytes(S, a.k_ss, ESK));
@@ -568,11 +569,12 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, int mode, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hq * a.nqt);
   if (grid == 0) return hipSuccess;
-  if (chunked ? mode == 1 : mode == 2) return hipErrorInvalidValue;
+  if (chunked ? mode == 1 : (mode == 2 || mode == 3)) return hipErrorInvalidValue;
   const dim3 blk(tile_q * 2);
 #define SSM_PREFILL_LAUNCH(D, TQ)                                                                                \
   if (d == D && tile_q == TQ) {                                                                                  \
     if (chunked && mode == 2) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 2>), dim3(grid), blk, 0, stream, a); \
+    else if (chunked && mode == 3) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 3>), dim3(grid), blk, 0, stream, a); \
     else if (chunked) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 0>), dim3(grid), blk, 0, stream, a);       \
     else if (mode == 1) hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 1>), dim3(grid), blk, 0, stream, a);    \
     else hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 0>), dim3(grid), blk, 0, stream, a);                   \

@@ -291,12 +291,15 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
   return launch_status(ssm::launch_decode_impl(a, (int)d, kv_cap, krows, vrows, static_cast<hipStream_t>(stream)));
 }
 
-int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
-                      const int32_t* q_start, const int32_t* kv_lens, int32_t batch, int32_t max_q_len,
-                      int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
-                      const ssm_opts* opts) {
+// qk8: q holds e4m3 codes with dequantisation factor q_scale and the caches must be e4m3 (ssm_prefill_paged_fp8qk)
+static int prefill_paged_impl(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+                              const int32_t* q_start, const int32_t* kv_lens, int32_t batch, int32_t max_q_len,
+                              int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+                              const ssm_opts* opts, bool qk8, float q_scale) {
   int rc;
-  if ((rc = check_tensor(q, "q", 3, SSM_BF16)) || (rc = check_tensor(out, "out", 3, SSM_BF16))) return rc;
+  if ((rc = check_tensor(q, "q", 3, qk8 ? SSM_FP8_E4M3 : SSM_BF16)) || (rc = check_tensor(out, "out", 3, SSM_BF16)))
+    return rc;
+  if (qk8 && !(q_scale > 0.f && std::isfinite(q_scale))) return fail(SSM_EINVAL, "q_scale must be finite and > 0");
   if (!q_start || !kv_lens) return fail(SSM_EINVAL, "q_start and kv_lens must be device arrays");
   if ((rc = check_tau(tau))) return rc;
   if (batch < 0 || max_q_len < 0) return fail(SSM_EINVAL, "batch and max_q_len must be >= 0");
@@ -312,6 +315,7 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
     return rc;
   if (k_cache->pool.dtype != v_cache->pool.dtype) return fail(SSM_EINVAL, "k and v caches must share one dtype");
   const bool kv8 = k_cache->pool.dtype == SSM_FP8_E4M3;
+  if (qk8 && !kv8) return fail(SSM_EUNSUPPORTED, "8-bit queries need e4m3 caches");
   if (k_cache->max_pages != v_cache->max_pages) return fail(SSM_EINVAL, "k and v page tables differ in length");
   if (hk != hv) return fail(SSM_EINVAL, "k/v head counts differ");
   const int64_t Hkv = hk;
@@ -328,7 +332,7 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
   const int64_t nqt = ((int64_t)max_q_len + tile_q - 1) / tile_q, nkt = k_cache->max_pages;
   const int64_t units = (int64_t)batch * Hq * nqt;
   if (units > INT32_MAX) return fail(SSM_EUNSUPPORTED, "too many query tiles");
-  if (((int64_t)max_q_len + 128) * q->stride[0] * 2 + d * 2 > (int64_t)UINT32_MAX)
+  if (((int64_t)max_q_len + 128) * q->stride[0] * (qk8 ? 1 : 2) + d * 2 > (int64_t)UINT32_MAX)
     return fail(SSM_EUNSUPPORTED, "max_q_len too long for 32-bit slice offsets");
   if (skip_stats) {
     if (skip_stats->tile_state && skip_stats->tile_state_len < units * nkt)
@@ -354,8 +358,9 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
   const int64_t groups = (int64_t)batch * Hkv;
   a.xcd_groups = groups % 8 == 0 ? (int)(groups / 8) : 0;
   // an fp8 cache: the key scale joins the logit scale, the value scale the output
-  const float lscale = kv8 ? scale * k_cache->scale : scale;
-  if (!(lscale > 0.f) || !std::isfinite(lscale)) return fail(SSM_EINVAL, "scale * k_scale out of range");
+  // same product order as ssm_prefill_fp8qk, so equal codes and scales give equal scores and decisions
+  const float lscale = qk8 ? scale * q_scale * k_cache->scale : (kv8 ? scale * k_cache->scale : scale);
+  if (!(lscale > 0.f) || !std::isfinite(lscale)) return fail(SSM_EINVAL, "scale * q_scale * k_scale out of range");
   a.scale = lscale;
   a.scale_log2 = lscale * 1.4426950408889634f;
   a.tau_raw = std::isinf(tau) ? tau : tau / lscale;
@@ -373,7 +378,24 @@ int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ss
   a.total_q = (int)total_q;
   a.k_pool_pages = krows;
   a.v_pool_pages = vrows;
-  return launch_status(ssm::launch_prefill(a, (int)d, tile_q, true, kv8 ? 2 : 0, static_cast<hipStream_t>(stream)));
+  return launch_status(
+      ssm::launch_prefill(a, (int)d, tile_q, true, qk8 ? 3 : (kv8 ? 2 : 0), static_cast<hipStream_t>(stream)));
+}
+
+int ssm_prefill_paged(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+                      const int32_t* q_start, const int32_t* kv_lens, int32_t batch, int32_t max_q_len,
+                      int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+                      const ssm_opts* opts) {
+  return prefill_paged_impl(q, k_cache, v_cache, q_start, kv_lens, batch, max_q_len, causal, tau, out, skip_stats,
+                            stream, opts, false, 1.f);
+}
+
+int ssm_prefill_paged_fp8qk(const ssm_tensor* q, float q_scale, const ssm_kv_cache* k_cache,
+                            const ssm_kv_cache* v_cache, const int32_t* q_start, const int32_t* kv_lens, int32_t batch,
+                            int32_t max_q_len, int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats,
+                            void* stream, const ssm_opts* opts) {
+  return prefill_paged_impl(q, k_cache, v_cache, q_start, kv_lens, batch, max_q_len, causal, tau, out, skip_stats,
+                            stream, opts, true, q_scale);
 }
 
 }  // extern "C"

@@ -66,7 +66,8 @@ struct DecodeArgs {
   unsigned long long* counters;
 };
 
-// mode 0: bf16; 1: e4m3 q/k scores (contiguous only); 2: e4m3 K/V pages (chunked only)
+// mode 0: bf16; 1: e4m3 q/k scores (contiguous only); 2: e4m3 K/V pages (chunked only); 3: e4m3 queries
+// scored against e4m3 K pages, e4m3 V pages (chunked only)
 hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, int mode, hipStream_t stream);
 hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
                               hipStream_t stream);

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 5
+    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 6
     for code in range(5):
         assert ssm.ssm_strerror(code)
     assert "unknown" in ssm.ssm_strerror(99)
@@ -338,6 +338,36 @@ def test_prefill_paged_rejects(lib, case, code):
     elif case == "out_shape":
         kw["o"] = desc([299, 16, 128])
     rc = call_prefill_paged(lib, **kw)
+    assert rc == code, (case, rc, ssm.ssm_last_error())
+
+
+@pytest.mark.parametrize("case,code", [
+    ("bf16_q", ssm.SSM_EUNSUPPORTED), ("bf16_cache", ssm.SSM_EUNSUPPORTED), ("zero_q_scale", ssm.SSM_EINVAL),
+    ("nan_q_scale", ssm.SSM_EINVAL), ("zero_k_scale", ssm.SSM_EINVAL), ("pos_tau", ssm.SSM_EINVAL),
+])
+def test_prefill_paged_fp8qk_rejects(lib, case, code):
+    f8 = ssm.SSM_FP8_E4M3
+    q = desc([300, 16, 128], dtype=f8)
+    kc = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=f8, scale=0.5)
+    vc = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=f8, scale=0.5)
+    q_scale, tau = 0.1, -6.9
+    if case == "bf16_q":
+        q = desc([300, 16, 128])
+    elif case == "bf16_cache":
+        kc = cache([100, 2, 64, 128], paged=True, max_pages=64)
+        vc = cache([100, 2, 64, 128], paged=True, max_pages=64)
+    elif case == "zero_q_scale":
+        q_scale = 0.0
+    elif case == "nan_q_scale":
+        q_scale = math.nan
+    elif case == "zero_k_scale":
+        kc = cache([100, 2, 64, 128], paged=True, max_pages=64, dtype=f8, scale=0.0)
+    elif case == "pos_tau":
+        tau = 0.3
+    o = desc([300, 16, 128])
+    opts = ssm.Opts(0.0, 0, 0, 0, None, 0, 0)
+    rc = lib.ssm_prefill_paged_fp8qk(ctypes.byref(q), q_scale, ctypes.byref(kc), ctypes.byref(vc), FAKE, FAKE, 2, 256,
+                                     1, tau, ctypes.byref(o), None, None, ctypes.byref(opts))
     assert rc == code, (case, rc, ssm.ssm_last_error())
 
 

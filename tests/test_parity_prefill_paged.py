@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from parity import chunk_batch, check_prefill_paged, fp8_pools, run_prefill_paged_gpu
+from parity import chunk_batch, check_prefill_paged, fp8_pools, fp8_q_packed, run_prefill_paged_gpu
 
 LN1000 = math.log(1000.0)
 pytestmark = pytest.mark.gpu
@@ -93,3 +93,59 @@ def test_chunk_8k_of_128k_sampled_fp8_cache():
     r = check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=w.taus[0], tile_q=128, sample=sample, fp8=fp8_pools(cb),
                             where="chunked fp8 8k of 128k")
     assert r["sparsity"] > 0.3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tile_q", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_batch_fp8_qk(d, tile_q, causal):
+    """The ragged batch with 8-bit queries (amax/448 scale) scored on the fp8 MFMA against the fp8 pools; the
+    oracle reads the dequantised queries and pools."""
+    w = synth.replace(SMALL, d=d)
+    seqs = [(129, 700), (1, 65), (300, 300), (63, 1000), (0, 77), (200, 263)]
+    cb = chunk_batch(w, seqs, seed=7)
+    f8, f8q = fp8_pools(cb), fp8_q_packed(cb)
+    for tau in (-LN1000, -math.inf):
+        check_prefill_paged(cb, Hq=w.Hq, causal=causal, tau=tau, tile_q=tile_q, fp8=f8, fp8q=f8q,
+                            where=f"chunked fp8qk d={d} tq={tile_q} causal={causal} tau={tau}")
+
+
+def test_llama_shape_long_context_chunk_fp8_qk():
+    w = synth.replace(synth.PREFILL_16K, S=0, seed=312)
+    cb = chunk_batch(w, [(2048, 16384), (1024, 4096)], seed=8)
+    r = check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=w.taus[2], tile_q=128, fp8=fp8_pools(cb),
+                            fp8q=fp8_q_packed(cb), where="chunked fp8qk llama 16k")
+    assert r["sparsity"] > 0.3
+
+
+def test_chunk_8k_of_128k_sampled_fp8_qk():
+    """The benchmark's chunked workload with 8-bit queries over an fp8 cache; sampled units."""
+    w = synth.PREFILL_128K
+    cb = chunk_batch(w, [(8192, w.S)], seed=4)
+    sample = {0: [(0, 0), (17, 31), (40, 62), (63, 63)]}
+    r = check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=w.taus[0], tile_q=128, sample=sample, fp8=fp8_pools(cb),
+                            fp8q=fp8_q_packed(cb), where="chunked fp8qk 8k of 128k")
+    assert r["sparsity"] > 0.3
+
+
+def test_fp8_qk_whole_sequence_chunk_matches_plain_fp8qk_prefill_decisions():
+    """A whole-sequence chunk with 8-bit queries over 8-bit pages takes the same skip decisions as the
+    non-paged 8-bit-score prefill on the same q/k codes (the scores are the same fp8 products; only V differs,
+    e4m3 pages here and bf16 there)."""
+    import long_context_flash_amd as ssm
+    import torch
+    from parity import fp8_device
+    w = synth.replace(SMALL, d=128)
+    cb = chunk_batch(w, [(512, 512)], seed=9)
+    f8, f8q = fp8_pools(cb), fp8_q_packed(cb)
+    _, st_p, _, _ = run_prefill_paged_gpu(cb, Hq=w.Hq, causal=True, tau=-LN1000, tile_q=128, fp8=f8, fp8q=f8q)
+    # the same k codes as the pool, in [1, S, Hkv, d] order
+    pages = cb["page_table"][0, :8]
+    k8 = np.ascontiguousarray(f8["k_pool"][pages].transpose(0, 2, 1, 3).reshape(1, 512, w.Hkv, w.d))
+    q8 = fp8_device(f8q["q"][None], "cuda")
+    v = ssm.bf16_from_bits(cb["per"][0]["v"], "cuda")
+    stats = ssm.SkipStats.alloc(*ssm.prefill_stats_shape(1, 512, w.Hq, 128), "cuda")
+    ssm.ssm_prefill_fp8qk(q8, f8q["q_scale"], fp8_device(k8, "cuda"), f8["k_scale"], v, causal=True, tau=-LN1000,
+                          skip_stats=stats, tile_q=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(stats.tile_state.cpu().numpy(), st_p)
