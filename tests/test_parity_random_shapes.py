@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import synth
-from parity import check_decode, check_prefill, check_prefill_paged, chunk_batch, fp8_pools
+from parity import check_decode, check_prefill, check_prefill_paged, chunk_batch, fp8_pools, fp8_q_packed
 
 pytestmark = pytest.mark.gpu
 TAUS = [-math.inf, -math.log(1000.0), -math.log(100.0), -3.0, 0.0]
@@ -66,6 +66,7 @@ def test_chunked_random(case):
     cb = chunk_batch(w, seqs, seed=case)
     causal, tile_q = bool(rng.integers(0, 2)), int(rng.choice([64, 128]))
     fp8 = fp8_pools(cb) if case % 2 == 1 else None
-    check_prefill_paged(cb, Hq=hkv * g, causal=causal, tau=tau, tile_q=tile_q, fp8=fp8,
+    fp8q = fp8_q_packed(cb) if case % 4 == 3 else None  # and 8-bit queries (ssm_prefill_paged_fp8qk)
+    check_prefill_paged(cb, Hq=hkv * g, causal=causal, tau=tau, tile_q=tile_q, fp8=fp8, fp8q=fp8q,
                         where=f"random chunked {case}: seqs={seqs} Hkv={hkv} G={g} d={d} causal={causal} "
-                              f"tq={tile_q} fp8={fp8 is not None}")
+                              f"tq={tile_q} fp8={fp8 is not None} fp8q={fp8q is not None}")
