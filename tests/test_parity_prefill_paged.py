@@ -149,3 +149,63 @@ def test_fp8_qk_whole_sequence_chunk_matches_plain_fp8qk_prefill_decisions():
                           skip_stats=stats, tile_q=128)
     torch.cuda.synchronize()
     assert np.array_equal(stats.tile_state.cpu().numpy(), st_p)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp8_cache", "fp8_qk"])
+def test_strided_views_match_contiguous(mode):
+    """q, out and both pools as views into wider buffers (rows padded by 32 elements, one spare head): the
+    same output bits and tile states as contiguous tensors, for bf16 pages, fp8 pages and 8-bit queries."""
+    import long_context_flash_amd as ssm
+    import torch
+    from parity import fp8_device
+    w = synth.replace(SMALL, d=128)
+    cb = chunk_batch(w, [(129, 700), (1, 65), (300, 300), (200, 263)], seed=10)
+    f8 = fp8_pools(cb) if mode != "bf16" else None
+    f8q = fp8_q_packed(cb) if mode == "fp8_qk" else None
+    dev = "cuda"
+    if f8q is not None:
+        q = fp8_device(f8q["q"], dev)
+    else:
+        q = ssm.bf16_from_bits(cb["q"], dev)
+    if f8 is not None:
+        kc, vc = fp8_device(f8["k_pool"], dev), fp8_device(f8["v_pool"], dev)
+        scales = dict(k_scale=f8["k_scale"], v_scale=f8["v_scale"])
+    else:
+        kc, vc = ssm.bf16_from_bits(cb["k_pool"], dev), ssm.bf16_from_bits(cb["v_pool"], dev)
+        scales = {}
+    pt = torch.from_numpy(cb["page_table"]).to(dev)
+    qs = torch.from_numpy(cb["q_start"]).to(dev)
+    kl = torch.from_numpy(cb["kv_lens"]).to(dev)
+    B, nqt = len(cb["seqs"]), -(-cb["max_q"] // 128)
+
+    def padded(t, head_dim):
+        """a view of t inside a buffer with one more head (dim head_dim) and 32 more elements per row"""
+        shape = list(t.shape)
+        shape[head_dim] += 1
+        shape[-1] += 32
+        raw = torch.zeros(shape, dtype=torch.uint8 if t.dtype == torch.float8_e4m3fn else t.dtype, device=dev)
+        big = raw.view(torch.float8_e4m3fn) if t.dtype == torch.float8_e4m3fn else raw
+        idx = [slice(None)] * t.dim()
+        idx[head_dim] = slice(0, t.shape[head_dim])
+        idx[-1] = slice(0, t.shape[-1])
+        view = big[tuple(idx)]
+        view.copy_(t)
+        return view
+
+    def run(q_, kc_, vc_, out_):
+        stats = ssm.SkipStats.alloc(B * w.Hq * nqt, pt.shape[1], dev, gaps=True)
+        if f8q is not None:
+            ssm.ssm_prefill_paged_fp8qk(q_, f8q["q_scale"], kc_, vc_, pt, qs, kl, cb["max_q"], causal=True,
+                                        tau=-LN1000, out=out_, skip_stats=stats, **scales)
+        else:
+            ssm.ssm_prefill_paged(q_, kc_, vc_, pt, qs, kl, cb["max_q"], causal=True, tau=-LN1000, out=out_,
+                                  skip_stats=stats, **scales)
+        torch.cuda.synchronize()
+        return out_.float().cpu().numpy(), stats.tile_state.cpu().numpy()
+
+    out_c, st_c = run(q, kc, vc, torch.zeros(q.shape, dtype=torch.bfloat16, device=dev))
+    out_v = padded(torch.zeros(q.shape, dtype=torch.bfloat16, device=dev), 1)
+    out_s, st_s = run(padded(q, 1), padded(kc, 1), padded(vc, 1), out_v)
+    assert (st_c == 2).any(), "no tile skipped: the case does not exercise the skip path"
+    assert np.array_equal(st_s, st_c), "strided views changed the decisions"
+    assert np.array_equal(out_s, out_c), "strided views changed the result"
