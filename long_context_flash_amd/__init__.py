@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
     ssm_prefill(q, k, v, causal=True, tau=-ln(1000), ...)       -> out [B,S,Hq,d] bf16
     ssm_prefill_fp8qk(q8, q_scale, k8, k_scale, v, ...)         -> out (fp8 e4m3 queries and keys)
     ssm_prefill_paged(q, k_cache, v_cache, page_table, ...)     -> out [total_q,Hq,d] bf16
+    ssm_prefill_paged_fp8qk(q8, q_scale, k_cache8, v_cache8, ...) -> out (fp8 e4m3 queries over fp8 pages)
     ssm_decode(q, k_cache, v_cache, kv_lens, tau=..., ...)      -> out [B,Hq,d] bf16
     ssm_decode_workspace_bytes(B, Hq, d, num_splits)
     ssm_strerror(code), ssm_last_error(), ssm_abi_version()
@@ -100,6 +101,9 @@ def lib():
     L.ssm_last_error.argtypes = []
     L.ssm_abi_version.restype = ctypes.c_int
     L.ssm_abi_version.argtypes = []
+    if L.ssm_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {L.ssm_abi_version()}, this binding expects {ABI_VERSION}: "
+                           "rebuild it with `python -m long_context_flash_amd.build`")
     _lib = L
     return L
 
@@ -118,6 +122,16 @@ def describe(t: Optional[torch.Tensor]) -> Tensor:
         d.shape[i] = t.shape[i]
         d.stride[i] = t.stride(i)
     return d
+
+
+def _on_device(device: torch.device, **tensors):
+    """Every tensor handed to the library must live on the GPU of the call (the kernels dereference the
+    pointers on that device); raise before any library call otherwise."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} is on {t.device}; the call runs on {device} and needs every tensor there")
 
 
 def _stream_handle(stream) -> Optional[int]:
@@ -140,7 +154,17 @@ class SkipStats:
     unit_gap: Optional[torch.Tensor] = None     # float32
     counters: Optional[torch.Tensor] = None     # int64 [4]: visited, skipped, qk tiles, pv tiles
 
+    def tensors(self) -> dict:
+        return {"skip_stats.tile_state": self.tile_state, "skip_stats.unit_gap": self.unit_gap,
+                "skip_stats.counters": self.counters}
+
     def c(self) -> SkipStatsC:
+        for t, dt, name in ((self.tile_state, torch.uint8, "tile_state"), (self.unit_gap, torch.float32, "unit_gap"),
+                            (self.counters, torch.int64, "counters")):
+            if t is not None and (t.dtype != dt or not t.is_contiguous()):
+                raise ValueError(f"skip_stats.{name} must be a contiguous {dt} tensor")
+        if self.counters is not None and self.counters.numel() < 4:
+            raise ValueError("skip_stats.counters needs 4 elements")
         s = SkipStatsC()
         if self.tile_state is not None:
             s.tile_state = self.tile_state.data_ptr()
@@ -169,6 +193,7 @@ def ssm_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
                 skip_stats: Optional[SkipStats] = None, stream=None, tile_q: int = 128, tile_k: int = 64,
                 scale: float = 0.0) -> torch.Tensor:
     """Skip Softmax prefill: q [B,S,Hq,d], k/v [B,S,Hkv,d] bf16 on the GPU -> out [B,S,Hq,d] bf16."""
+    _on_device(q.device, q=q, k=k, v=v, out=out, **(skip_stats.tensors() if skip_stats else {}))
     if out is None:
         out = torch.empty_like(q)
     qd, kd, vd, od = describe(q), describe(k), describe(v), describe(out)
@@ -187,6 +212,7 @@ def ssm_prefill_fp8qk(q: torch.Tensor, q_scale: float, k: torch.Tensor, k_scale:
                       scale: float = 0.0) -> torch.Tensor:
     """Skip Softmax prefill with 8-bit scores: q [B,S,Hq,d] and k [B,S,Hkv,d] torch.float8_e4m3fn codes (query =
     q_scale * code, key = k_scale * code), v [B,S,Hkv,d] bf16 on the GPU -> out [B,S,Hq,d] bf16."""
+    _on_device(q.device, q=q, k=k, v=v, out=out, **(skip_stats.tensors() if skip_stats else {}))
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     qd, kd, vd, od = describe(q), describe(k), describe(v), describe(out)
@@ -222,6 +248,8 @@ def ssm_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     q_start[b+1]-1, the last of its kv_lens[b] cached keys); k_cache/v_cache [pages,Hkv,64,d] bf16, or
     torch.float8_e4m3fn codes (key = k_scale * code, value = v_scale * code), with page_table int32
     [B,max_pages]; q_start int32 [B+1] and kv_lens int32 [B] on the GPU."""
+    _on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table, v_page_table=v_page_table,
+               q_start=q_start, kv_lens=kv_lens, out=out, **(skip_stats.tensors() if skip_stats else {}))
     if out is None:
         out = torch.empty_like(q)
     for name, t in (("q_start", q_start), ("kv_lens", kv_lens)):
@@ -252,6 +280,8 @@ def ssm_prefill_paged_fp8qk(q: torch.Tensor, q_scale: float, k_cache: torch.Tens
     """Chunked prefill with 8-bit queries over e4m3 pages: q [total_q,Hq,d] torch.float8_e4m3fn codes (query =
     q_scale * code), k_cache/v_cache [pages,Hkv,64,d] torch.float8_e4m3fn codes with k_scale / v_scale; the rest
     as ssm_prefill_paged.  out [total_q,Hq,d] bf16."""
+    _on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table, v_page_table=v_page_table,
+               q_start=q_start, kv_lens=kv_lens, out=out, **(skip_stats.tensors() if skip_stats else {}))
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     for name, t in (("q_start", q_start), ("kv_lens", kv_lens)):
@@ -295,6 +325,8 @@ def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
     sink_seed: splits after the first start their running maximum at the first key tile's row maxima.
     k_cache/v_cache may be torch.float8_e4m3fn tensors of codes; keys and values are then k_scale * code and
     v_scale * code."""
+    _on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, kv_lens=kv_lens, out=out, page_table=page_table,
+               v_page_table=v_page_table, workspace=workspace, **(skip_stats.tensors() if skip_stats else {}))
     if out is None:
         out = torch.empty_like(q)
     B, Hq, d = q.shape

@@ -407,3 +407,36 @@ int main(void) {
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert "q" in r.stdout
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    """The binding refuses tensors that are not on the call's GPU (the kernels would dereference host
+    addresses); checked on the host, so it runs without a GPU."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(1, 64, 4, 64, dtype=bf)
+    kv = torch.zeros(1, 64, 1, 64, dtype=bf)
+    with pytest.raises(ValueError, match="needs every tensor"):
+        ssm.ssm_prefill(q, kv, kv)
+    with pytest.raises(ValueError, match="needs every tensor"):
+        ssm.ssm_prefill_fp8qk(q.to(torch.float8_e4m3fn), 1.0, kv.to(torch.float8_e4m3fn), 1.0, kv)
+    pool = torch.zeros(4, 1, 64, 64, dtype=bf)
+    pt = torch.zeros(1, 4, dtype=torch.int32)
+    qs, kl = torch.tensor([0, 64], dtype=torch.int32), torch.tensor([256], dtype=torch.int32)
+    with pytest.raises(ValueError, match="needs every tensor"):
+        ssm.ssm_prefill_paged(q[0], pool, pool, pt, qs, kl, 64)
+    with pytest.raises(ValueError, match="needs every tensor"):
+        ssm.ssm_prefill_paged_fp8qk(q[0].to(torch.float8_e4m3fn), 1.0, pool.to(torch.float8_e4m3fn),
+                                    pool.to(torch.float8_e4m3fn), pt, qs, kl, 64, 1.0, 1.0)
+    with pytest.raises(ValueError, match="needs every tensor"):
+        ssm.ssm_decode(q[0, :1], pool, pool, kl, page_table=pt)
+
+
+def test_skip_stats_dtypes_are_checked():
+    import torch
+    with pytest.raises(ValueError, match="tile_state"):
+        ssm.SkipStats(tile_state=torch.zeros(4, dtype=torch.int32)).c()
+    with pytest.raises(ValueError, match="counters"):
+        ssm.SkipStats(counters=torch.zeros(3, dtype=torch.int64)).c()
+    with pytest.raises(ValueError, match="unit_gap"):
+        ssm.SkipStats(unit_gap=torch.zeros(4, 2, dtype=torch.float32)[:, 0]).c()
