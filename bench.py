@@ -243,6 +243,52 @@ def time_fp8_decode(ssm, torch, np, w, data, dq, kp, vp, pt, lens, dout, ws, dst
             "speedup_vs_bf16": None}
 
 
+def _timed(torch, np, fn, steps):
+    """mean ms of `steps` calls of fn between HIP events on the current stream, after one untimed call"""
+    fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
+def time_prefill_vs_dense(ssm, torch, np, w, q, k, v, out, skip_ms, sparsity, steps, dev):
+    """The same prefill launch at tau = -inf (no tile skipped: the dense kernel) against the timed skip launch:
+    the speedup skipping buys on this input, the quantity the Skip Softmax pages report (as context: 1.4x for
+    prefill of Llama 3.3 70B at 128K on GB200)."""
+    cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+    ms = _timed(torch, np, lambda: ssm.ssm_prefill(q, k, v, causal=True, tau=-math.inf, out=out,
+                                                   skip_stats=ssm.SkipStats(counters=cnt), tile_q=w.tile_q), steps)
+    c = cnt.cpu().numpy()
+    if int(c[1]) != 0:
+        raise RuntimeError("tau = -inf skipped tiles")
+    return {"dense_ms": round(ms, 3), "skip_ms": skip_ms, "skip_sparsity": sparsity,
+            "speedup_vs_dense": round(ms / skip_ms, 3), "pages_prefill_speedup": 1.4}
+
+
+def time_decode_tau_sweep(ssm, torch, np, w, dq, kp, vp, pt, lens, dout, ws, steps, dev):
+    """The decode at each calibrated tau of its workload (tau = -inf, written as null, is the dense kernel): time,
+    sparsity and the speedup over tau = -inf (as context: the pages project 1.36x for decode of Llama 3.3 70B)."""
+    rows = []
+    for tau in w.taus:
+        cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+        ms = _timed(torch, np, lambda: ssm.ssm_decode(dq, kp, vp, lens, tau=tau, out=dout, page_table=pt,
+                                                      num_splits=w.num_splits, workspace=ws,
+                                                      skip_stats=ssm.SkipStats(counters=cnt)), steps)
+        c = cnt.cpu().numpy()
+        # tau = -inf is written as null (JSON has no infinities)
+        rows.append({"tau": None if math.isinf(tau) else round(float(tau), 4), "ms": round(ms, 4),
+                     "sparsity": round(float(c[1]) / float(c[0]), 4)})
+    dense = rows[0]["ms"]
+    for r in rows:
+        r["speedup_vs_dense"] = round(dense / r["ms"], 3)
+    return {"sweep": rows, "pages_decode_speedup": 1.36}
+
+
 def recorded_fp8_mfma_ceiling():
     """Random-operand fp8 MFMA rate recorded in profiles/mfma_ceiling.json (None if absent)."""
     rec = _recorded("mfma_ceiling.json", "fp8")
@@ -589,6 +635,8 @@ def main():
         res["prefill_chunked_paged"] = time_chunked_prefill(ssm, torch, np, pw, pdata, tau_p, args.steps, dev)
         res["prefill_fp8_qk"] = time_fp8qk_prefill(ssm, torch, np, pw, q, k, v, pout, tau_p, res["prefill_ms"],
                                                    args.steps, dev)
+        res["prefill_vs_dense"] = time_prefill_vs_dense(ssm, torch, np, pw, q, k, v, pout, res["prefill_ms"],
+                                                        res["prefill_sparsity"], args.steps, dev)
     if run_decode:
         c = dcnt.cpu().numpy() / args.steps
         ssm.ssm_decode(dq, kp, vp, lens, tau=tau_d, out=dout, page_table=pt, num_splits=dw.num_splits,
@@ -632,6 +680,8 @@ def main():
         res["decode_fp8_kv"] = time_fp8_decode(ssm, torch, np, dw, ddata, dq, kp, vp, pt, lens, dout, ws, dstate, tau_d,
                                                args.steps, dev)
         res["decode_fp8_kv"]["speedup_vs_bf16"] = round(res["decode_ms"] / res["decode_fp8_kv"]["ms"], 3)
+        res["decode_tau_sweep"] = time_decode_tau_sweep(ssm, torch, np, dw, dq, kp, vp, pt, lens, dout, ws, args.steps,
+                                                        dev)
         read_ceiling = recorded_read_ceiling()
         if read_ceiling:
             for leg in ("decode_sink_seeded", "decode_fp8_kv"):
@@ -652,7 +702,7 @@ def main():
                 res["cpu_baseline_decode"] = cpu_baseline_decode(dw, ddata, tau_d, threads)
         elif run_decode:
             res["cpu_baseline"] = cpu_baseline_decode(dw, ddata, tau_d, threads)
-    print(json.dumps(res), flush=True)
+    print(json.dumps(res, allow_nan=False), flush=True)
 
 
 if __name__ == "__main__":
