@@ -27,6 +27,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 namespace {
 
 constexpr int kGrid = 512, kThreads = 256, kOps = 16;  // u32x4 operand registers per lane (8 A, 8 B)
+constexpr int kValuGrid = 2048;  // workgroups of the VALU timing loops (256 threads, one output word each)
 constexpr int kMfmaPerIter = 16;
 constexpr double kFlopPerMfma = 2.0 * 32 * 32 * 16;
 
@@ -102,6 +103,41 @@ __global__ __launch_bounds__(256) void valu_loop(float* __restrict__ out, int it
   out[blockIdx.x * 256 + threadIdx.x] = r;
 }
 
+// Softmax weights of 8 scores per lane per iteration, packed to bf16 pairs as the attention kernels pack P:
+// OP 0 = exponential weights 2^t (v_exp_f32, then a bf16 pack); OP 1 = power-of-two weights 2^round(t) built
+// in the bf16 exponent field (clamp at the smallest normal exponent, round to an integer, shift, pack), the
+// coarse logarithmic weights of the Rowmax-PoT idea, in the fewest full-rate instructions found.  Both share the scaling fma that produces t (a chain per
+// element, so nothing is loop-invariant) and one xor per pair that keeps the result live.
+template <int OP>
+__global__ __launch_bounds__(256) void weight_loop(uint32_t* __restrict__ out, int iters) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (float)(threadIdx.x + i) * 1e-6f - 1.0f;
+  uint32_t acc = 0;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float t0 = __builtin_fmaf(a[i], 0.999f, -0.001f), t1 = __builtin_fmaf(a[i + 1], 0.999f, -0.001f);
+      uint32_t w;
+      if constexpr (OP == 0) {
+        const bf16x2 v = {(__bf16)__builtin_amdgcn_exp2f(t0), (__bf16)__builtin_amdgcn_exp2f(t1)};
+        w = __builtin_bit_cast(uint32_t, v);
+      } else {
+        // k = t rounded to the nearest integer (ties to even) appears in the low mantissa bits of
+        // t + 1.5 * 2^23 (0x4B400000 + k); the bf16 bits of 2^k are (k + 127) << 7, clamped at k = -126
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_fmaxf(t0, -126.f) + 12582912.0f);
+        const uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_fmaxf(t1, -126.f) + 12582912.0f);
+        w = (((u0 << 7) + ((127u - 0x4B400000u) << 7)) & 0xffffu) | ((u1 << 23) + ((127u - 0x4B400000u) << 23));
+      }
+      acc ^= w;
+      a[i] = t0;
+      a[i + 1] = t1;
+    }
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 #define CHECK(x)                                                                        \
   do {                                                                                  \
     const hipError_t e_ = (x);                                                          \
@@ -137,10 +173,36 @@ double rate(const u32x4* src, float* out, int iters, bool f8 = false) {
             : waves * iters * kMfmaPerIter * kFlopPerMfma / (ms * 1e-3) / 1e12;
 }
 
+// weights per second per SIMD (one per lane and score) of weight_loop<OP>
+template <int OP>
+double weight_rate(uint32_t* out, int num_simds) {
+  const int grid = kValuGrid, iters = 4096;
+  hipLaunchKernelGGL(weight_loop<OP>, dim3(grid), dim3(256), 0, 0, out, 16);
+  CHECK(hipGetLastError());
+  CHECK(hipDeviceSynchronize());
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  float best = 1e30f;
+  for (int rep = 0; rep < 3; ++rep) {
+    CHECK(hipEventRecord(e0, 0));
+    hipLaunchKernelGGL(weight_loop<OP>, dim3(grid), dim3(256), 0, 0, out, iters);
+    CHECK(hipGetLastError());
+    CHECK(hipEventRecord(e1, 0));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    best = ms < best ? ms : best;
+  }
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return (double)grid * 256 * iters * 8 / num_simds / (best * 1e-3);
+}
+
 // wave instructions per second per SIMD of valu_loop<OP> (OP 1 counts the exponential and its add as two)
 template <int OP>
 double valu_rate(float* out, int num_simds) {
-  const int grid = 2048, iters = 4096;
+  const int grid = kValuGrid, iters = 4096;
   hipLaunchKernelGGL(valu_loop<OP>, dim3(grid), dim3(256), 0, 0, out, 16);
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
@@ -203,7 +265,8 @@ int main(int argc, char** argv) {
   CHECK(hipMalloc(&rnd, n * sizeof(u32x4)));
   CHECK(hipMalloc(&rnd8, n * sizeof(u32x4)));
   CHECK(hipMemcpy(rnd8, host8.data(), n * sizeof(u32x4), hipMemcpyHostToDevice));
-  CHECK(hipMalloc(&out, (size_t)kGrid * kThreads * sizeof(float)));
+  // one word per thread of the largest grid that writes it (the VALU loops' kValuGrid x 256)
+  CHECK(hipMalloc(&out, (size_t)(kGrid > kValuGrid ? kGrid : kValuGrid) * kThreads * sizeof(float)));
   CHECK(hipMemset(zero, 0, n * sizeof(u32x4)));
   CHECK(hipMemcpy(rnd, host.data(), n * sizeof(u32x4), hipMemcpyHostToDevice));
   double z = 0, r = 0, z8 = 0, r8 = 0;
@@ -220,13 +283,18 @@ int main(int argc, char** argv) {
   CHECK(hipGetDevice(&dev));
   CHECK(hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev));
   const double fma_rate = valu_rate<0>(out, num_cus * 4), pair_rate = valu_rate<1>(out, num_cus * 4) / 2.0;
+  uint32_t* out32 = reinterpret_cast<uint32_t*>(out);
+  const double exp_w = weight_rate<0>(out32, num_cus * 4), pot_w = weight_rate<1>(out32, num_cus * 4);
   std::printf("{\"instruction\": \"v_mfma_f32_32x32x16_bf16\", \"zero_operands_tflops\": %.1f, "
               "\"random_operands_tflops\": %.1f, \"published_peak_tflops\": 2500.0, \"workgroups\": %d, "
               "\"waves_per_simd\": 2, \"iterations\": %d, \"valu_fma_f32_per_us_per_simd\": %.1f, "
               "\"valu_exp_f32_plus_add_per_us_per_simd\": %.1f, \"exp_plus_add_in_fma_times\": %.2f, "
+              "\"weights\": {\"exp2_bf16_per_us_per_simd\": %.1f, \"pow2_bf16_per_us_per_simd\": %.1f, "
+              "\"pow2_time_over_exp2_time\": %.3f}, "
               "\"fp8\": {\"instruction\": \"v_mfma_f32_32x32x64_f8f6f4\", \"zero_operands_tflops\": %.1f, "
               "\"random_operands_tflops\": %.1f, \"published_peak_tflops\": 5000.0}}\n",
-              z, r, kGrid, iters, fma_rate * 1e-6, pair_rate * 1e-6, fma_rate / pair_rate, z8, r8);
+              z, r, kGrid, iters, fma_rate * 1e-6, pair_rate * 1e-6, fma_rate / pair_rate, exp_w * 1e-6, pot_w * 1e-6,
+              exp_w / pot_w, z8, r8);
   CHECK(hipFree(zero));
   CHECK(hipFree(rnd));
   CHECK(hipFree(rnd8));
