@@ -78,6 +78,18 @@ def test_prefill_128k_sampled():
     assert r["sparsity"] >= 0.45, "the calibrated workload skips about half of its tiles"
 
 
+def test_prefill_128k_dense_sampled():
+    """The same workload at tau = -inf (the dense launch the benchmark times for its speedup): no tile skipped,
+    sampled units against the oracle."""
+    w = synth.PREFILL_128K
+    data = synth.gen_prefill(w)
+    nqt = w.S // 128
+    units = np.array([0 * nqt + 0, 21 * nqt + 300, 63 * nqt + nqt - 1])
+    r = check_prefill(data, B=1, S=w.S, Hq=w.Hq, Hkv=w.Hkv, d=w.d, causal=True, tau=-math.inf, tile_q=128,
+                      units=units, where="128k dense")
+    assert r["sparsity"] == 0.0
+
+
 def test_batch3_causal_gqa2_odd_length():
     w = synth.replace(synth.PREFILL_16K, B=3, S=515, Hq=8, Hkv=4, d=64, seed=8)
     check_prefill(_data(w), B=3, S=515, Hq=8, Hkv=4, d=64, causal=True, tau=-LN1000, tile_q=64,
