@@ -50,6 +50,22 @@ def test_group_sizes_d64(G):
     check_decode(data, tau=-LN1000, num_splits=8, paged=False, where=f"d64 G={G}")
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_largest_group_and_split_count(paged):
+    """The largest supported configuration per unit: 16 query heads per KV head at d = 128 and 64 splits (the
+    upper bound of num_splits), kv_len from 1 to 9000 (from more splits than tiles to 2-3 tiles per split),
+    split-local and sink-seeded."""
+    w = _small(B=4, Hq=32, Hkv=2, d=128, seed=21)
+    lens = np.array([1, 700, 4097, 9000], np.int32)
+    data = synth.gen_decode(w, kv_lens=lens, contiguous=True, paged=True)
+    for seeded in (False, True):
+        for tau in (-LN1000, -1.0):  # -1: a split of 2-3 tiles skips too
+            r = check_decode(data, tau=tau, num_splits=64, paged=paged, sink_seed=seeded,
+                             where=f"G16 d128 P64 paged={paged} seeded={seeded} tau={tau}")
+            if tau == -1.0:
+                assert r["sparsity"] > 0.05, "the case must exercise the skip path"
+
+
 def test_decode_32k_full():
     """The 32K workload at full size, split-K (16) and the sequential definition (1 split)."""
     w = synth.DECODE_32K
