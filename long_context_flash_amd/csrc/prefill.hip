@@ -49,6 +49,8 @@
 // scale); S^T on v_mfma_f32_32x32x64_f8f6f4, twice the bf16 rate, for the QK^T that every visited tile
 // pays.  K tiles sit in LDS as 8-bit rows (D bytes); each lane reads 32 bytes of one key row per MFMA, and
 // Q and K use the same channel order (any order gives the same dot products).  V, P and P.V stay bf16.
+// Both together (the chunked prefill with 8-bit queries over fp8 pages): the K pages already sit in LDS as
+// the QK8 rows, so the scores take the QK8 reads and MFMA, and V takes the KV8 reads and conversions.
 //
 // Exponentials use a lazily moved reference maximum: P = 2^(S*c - m_ref*c) with
 // m_ref only raised when the true running maximum exceeds it by more than 8
