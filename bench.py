@@ -14,6 +14,12 @@ Prints ONE JSON line.  ``value`` is the prefill's dense-equivalent TFLOP/s
 KV GB/s is reported beside it.  ``roofline`` is the prefill kernel against the bf16 MFMA
 peak; ``roofline_decode`` is the decode path against HBM.  ``cpu_baseline`` is the fp64
 oracle timed on a bounded sample of the same prefill work on the host cores.
+
+After the timed steps (unless --main-only) the variants are timed on their own on the same inputs:
+the sink-seeded and fp8-cache decodes, the fp8-score prefill, the chunked prefill (last 8192 queries
+against a paged pool of all keys; bf16 pages, fp8 pages, 8-bit queries over fp8 pages), and the
+speedup skipping buys over the dense kernel (the prefill at tau = -inf, the decode over its
+calibrated tau sweep).
 """
 from __future__ import annotations
 
