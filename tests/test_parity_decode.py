@@ -124,3 +124,29 @@ def test_strided_query_and_output_match_contiguous():
     ssm.ssm_decode(qv, kc, vc, lens, tau=-LN1000, num_splits=8, out=ov)
     torch.cuda.synchronize()
     assert torch.equal(ov, ref), "strided q/out changed the result"
+
+
+def test_separate_value_page_table_matches_shared():
+    """V pages under their own page table (the pool permuted differently from K's) give the same bits as one
+    shared table: each cache is addressed through its own table."""
+    import torch
+    import long_context_flash_amd as ssm
+    w = _small()
+    data = synth.gen_decode(w, contiguous=False, paged=True)
+    dev = "cuda"
+    pt = data["page_table"]
+    sigma = np.random.default_rng(5).permutation(data["v_pool"].shape[0]).astype(np.int32)
+    v_pool2 = np.empty_like(data["v_pool"])
+    v_pool2[sigma] = data["v_pool"]                      # page p of the old pool is page sigma[p] of the new one
+    v_pt2 = np.where(pt >= 0, sigma[np.maximum(pt, 0)], pt).astype(np.int32)
+    q = ssm.bf16_from_bits(data["q"], dev)
+    kp, vp = ssm.bf16_from_bits(data["k_pool"], dev), ssm.bf16_from_bits(data["v_pool"], dev)
+    vp2 = ssm.bf16_from_bits(v_pool2, dev)
+    lens = torch.from_numpy(data["kv_lens"]).to(dev)
+    pt_d, v_pt2_d = torch.from_numpy(pt).to(dev), torch.from_numpy(v_pt2).to(dev)
+    for seeded in (False, True):
+        ref = ssm.ssm_decode(q, kp, vp, lens, tau=-4.0, page_table=pt_d, num_splits=8, sink_seed=seeded)
+        got = ssm.ssm_decode(q, kp, vp2, lens, tau=-4.0, page_table=pt_d, v_page_table=v_pt2_d, num_splits=8,
+                             sink_seed=seeded)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"separate V page table changed the output (seeded={seeded})"

@@ -209,3 +209,26 @@ def test_strided_views_match_contiguous(mode):
     assert (st_c == 2).any(), "no tile skipped: the case does not exercise the skip path"
     assert np.array_equal(st_s, st_c), "strided views changed the decisions"
     assert np.array_equal(out_s, out_c), "strided views changed the result"
+
+
+def test_separate_value_page_table_matches_shared():
+    """The chunked prefill with V pages under their own page table gives the same bits as one shared table."""
+    import long_context_flash_amd as ssm
+    import torch
+    w = synth.replace(SMALL, d=128)
+    cb = chunk_batch(w, [(129, 700), (300, 300), (63, 1000)], seed=11)
+    dev = "cuda"
+    pt = cb["page_table"]
+    sigma = np.random.default_rng(6).permutation(cb["v_pool"].shape[0]).astype(np.int32)
+    v_pool2 = np.empty_like(cb["v_pool"])
+    v_pool2[sigma] = cb["v_pool"]
+    v_pt2 = np.where(pt >= 0, sigma[np.maximum(pt, 0)], pt).astype(np.int32)
+    q = ssm.bf16_from_bits(cb["q"], dev)
+    kp, vp = ssm.bf16_from_bits(cb["k_pool"], dev), ssm.bf16_from_bits(cb["v_pool"], dev)
+    vp2 = ssm.bf16_from_bits(v_pool2, dev)
+    qs, kl = torch.from_numpy(cb["q_start"]).to(dev), torch.from_numpy(cb["kv_lens"]).to(dev)
+    pt_d, v_pt2_d = torch.from_numpy(pt).to(dev), torch.from_numpy(v_pt2).to(dev)
+    ref = ssm.ssm_prefill_paged(q, kp, vp, pt_d, qs, kl, cb["max_q"], tau=-LN1000)
+    got = ssm.ssm_prefill_paged(q, kp, vp2, pt_d, qs, kl, cb["max_q"], tau=-LN1000, v_page_table=v_pt2_d)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref), "separate V page table changed the output"
