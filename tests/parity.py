@@ -79,8 +79,9 @@ def unit_ids(B, Hq, nqt, units):
     return units // (Hq * nqt), (units // nqt) % Hq, units % nqt
 
 
-def run_prefill_gpu(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, device="cuda", fp8qk=None):
-    """fp8qk: the synth.fp8_qk() codes and scales of q and k (ssm_prefill_fp8qk), else the bf16 prefill."""
+def run_prefill_gpu(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, device="cuda", fp8qk=None, scale=0.0):
+    """fp8qk: the synth.fp8_qk() codes and scales of q and k (ssm_prefill_fp8qk), else the bf16 prefill.
+    scale: the logit scale (0: 1/sqrt(d))."""
     v = ssm.bf16_from_bits(data["v"], device)
     units, nkt = ssm.prefill_stats_shape(B, S, Hq, tile_q)
     stats = ssm.SkipStats.alloc(units, nkt, device, gaps=True)
@@ -91,7 +92,7 @@ def run_prefill_gpu(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, device="cuda
     else:
         q = ssm.bf16_from_bits(data["q"], device)
         k = ssm.bf16_from_bits(data["k"], device)
-        out = ssm.ssm_prefill(q, k, v, causal=causal, tau=tau, skip_stats=stats, tile_q=tile_q)
+        out = ssm.ssm_prefill(q, k, v, causal=causal, tau=tau, skip_stats=stats, tile_q=tile_q, scale=scale)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
             stats.counters.cpu().numpy())
@@ -150,15 +151,17 @@ def oracle_prefill_fp8qk(data, f8, *, B, S, Hq, Hkv, causal, tau, tile_q, units,
 
 
 def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, where="prefill", threads=None,
-                  fp8qk=None, strict=True):
+                  fp8qk=None, strict=True, scale=0.0):
     """Run the GPU prefill on the whole input and compare the listed units (all when None) with the oracle.
     fp8qk: the synth.fp8_qk() codes and scales of q and k; both sides then score the same 8-bit values, and the
     bars widen by what the fp8 MFMA's score error (fp8_score_error_bound) can move the outputs; strict then also
     asserts the plain bar (inputs whose score energy is spread over the channels meet it)."""
     log(f"{where}: GPU prefill B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} tau={tau} tile_q={tile_q} "
         f"fp8qk={fp8qk is not None}")
+    if fp8qk is not None and scale:
+        raise ValueError("the fp8-score bound assumes the default logit scale")
     out, st, gap, cnt = run_prefill_gpu(data, B=B, S=S, Hq=Hq, Hkv=Hkv, d=d, causal=causal, tau=tau, tile_q=tile_q,
-                                        fp8qk=fp8qk)
+                                        fp8qk=fp8qk, scale=scale)
     nqt = -(-S // tile_q)
     vis = int((st > 0).sum())
     skipped = int((st == 2).sum())
@@ -173,7 +176,7 @@ def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, wh
             return oracle_prefill_fp8qk(data, fp8qk, B=B, S=S, Hq=Hq, Hkv=Hkv, causal=causal, tau=tau, tile_q=tile_q,
                                         units=units, override=ov, threads=threads)
         return oracle.prefill(data["q"], data["k"], data["v"], causal=causal, tau=tau, tile_q=tile_q, tile_k=64,
-                              units=units, override=ov, threads=threads)
+                              scale=scale, units=units, override=ov, threads=threads)
 
     ref = run_oracle()
     slack = ref.get("score_err")
@@ -213,7 +216,7 @@ def fp8_device(codes, device):
     return torch.from_numpy(codes).to(device).view(torch.float8_e4m3fn)
 
 
-def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda", sink_seed=False, fp8=None):
+def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda", sink_seed=False, fp8=None, scale=0.0):
     """fp8: the synth.fp8_kv() copies of the K/V (the GPU then reads the codes with their scales)."""
     q = ssm.bf16_from_bits(data["q"], device)
     lens = torch.from_numpy(data["kv_lens"]).to(device)
@@ -233,7 +236,7 @@ def run_decode_gpu(data, *, tau, num_splits, paged, device="cuda", sink_seed=Fal
         Hkv, max_tiles = kc.shape[1], -(-kc.shape[2] // 64)
     stats = ssm.SkipStats.alloc(B * Hkv, max_tiles, device, gaps=True)
     out = ssm.ssm_decode(q, kc, vc, lens, tau=tau, page_table=pt, num_splits=num_splits, skip_stats=stats,
-                         sink_seed=sink_seed, **scales)
+                         sink_seed=sink_seed, scale=scale, **scales)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
             stats.counters.cpu().numpy())
@@ -252,14 +255,14 @@ def contiguous_from_pages(pool, page_table, kv_lens, batches):
 
 
 def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", threads=None, sink_seed=False,
-                 fp8=None):
+                 fp8=None, scale=0.0):
     """GPU decode on the whole batch vs the oracle on the listed sequences (all when None).  fp8: the
     synth.fp8_kv() copies of the K/V; both sides then read the same codes and scales."""
     B, Hq, d = data["q"].shape
     log(f"{where}: GPU decode B={B} Hq={Hq} d={d} tau={tau} P={num_splits} paged={paged} sink_seed={sink_seed} "
         f"fp8={fp8 is not None}")
     out, st, gap, cnt = run_decode_gpu(data, tau=tau, num_splits=num_splits, paged=paged, sink_seed=sink_seed,
-                                       fp8=fp8)
+                                       fp8=fp8, scale=scale)
     vis = int((st > 0).sum())
     skipped = int((st == 2).sum())
     assert list(cnt) == [vis, skipped, vis, vis - skipped], f"{where}: counters {list(cnt)} vs tile_state"
@@ -279,7 +282,7 @@ def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", 
     scales = dict(k_scale=fp8["k_scale"], v_scale=fp8["v_scale"]) if fp8 is not None else {}
     log(f"{where}: oracle on {len(batches)} sequences")
     ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits,
-                        sink_seed=sink_seed, threads=threads, **scales)
+                        sink_seed=sink_seed, threads=threads, scale=scale, **scales)
     mt = ref["state"].shape[1]
     rows = (batches[:, None] * Hkv + np.arange(Hkv)[None]).ravel()
     st_g = st[rows][:, :mt]
@@ -289,7 +292,7 @@ def check_decode(data, *, tau, num_splits, paged, batches=None, where="decode", 
     if flips.any():
         ov = np.where(flips, np.where(st_g == 2, 1, 0), -1).astype(np.int8)
         ref = oracle.decode(data["q"][batches], kc, vc, lens[batches], tau=tau, num_splits=num_splits,
-                            override=ov, sink_seed=sink_seed, threads=threads, **scales)
+                            override=ov, sink_seed=sink_seed, threads=threads, scale=scale, **scales)
     got = out[batches].reshape(ref["out"].shape)
     max_abs, rel = errors(got, ref["out"])
     sparsity = skipped / max(vis, 1)

@@ -120,3 +120,14 @@ def test_strided_views_match_contiguous():
     ssm.ssm_prefill(qv, kv, vv, causal=True, tau=-LN1000, out=out)
     torch.cuda.synchronize()
     assert torch.equal(out, ref), "strided views changed the result"
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+def test_custom_logit_scale(scale):
+    """A logit scale other than 1/sqrt(d) (opts.scale) on both sides: the gaps, the decisions and the outputs
+    follow it (0.05 flattens the scores, 0.3 sharpens them)."""
+    w = synth.replace(synth.PREFILL_16K, S=700, Hq=8, Hkv=2, d=128, rank=8, seed=31)
+    r = check_prefill(_data(w), B=1, S=700, Hq=8, Hkv=2, d=128, causal=True, tau=-math.log(100.0), tile_q=128,
+                      scale=scale, where=f"prefill scale={scale}")
+    if scale == 0.3:
+        assert r["sparsity"] > 0
