@@ -51,7 +51,11 @@ enum { SSM_BF16 = 0, SSM_FP32 = 1, SSM_FP8_E4M3 = 2 /* OCP 8-bit float, 4 expone
 /* Strided tensor view.  stride[] is in elements; the last dimension must be
  * contiguous (stride 1).  data must be 16-byte aligned and every other stride
  * a multiple of 16 bytes (8 bf16 or 16 fp8 elements), so rows can be moved in
- * 16-byte pieces. */
+ * 16-byte pieces.  An empty view (some extent 0) may have data == NULL.
+ * A call with nothing to compute (prefill B, S or Hq 0; decode B or Hq 0;
+ * chunked prefill batch 0 or max_q_len 0) checks its descriptors and returns
+ * SSM_OK without launching; an empty decode needs no workspace, and an empty
+ * batch needs no kv_lens, q_start or page tables. */
 typedef struct {
   void* data;
   int32_t dtype;    /* SSM_BF16, SSM_FP32 or SSM_FP8_E4M3 (where an entry point accepts it) */

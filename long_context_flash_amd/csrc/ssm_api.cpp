@@ -25,10 +25,13 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+// An empty tensor (some extent 0) may carry a NULL data pointer: nothing is read or written through it.
 int check_tensor(const ssm_tensor* t, const char* name, int ndim, int dtype) {
   if (!t) return fail(SSM_EINVAL, "%s: NULL descriptor", name);
-  if (!t->data) return fail(SSM_EINVAL, "%s: NULL data pointer", name);
   if (t->ndim != ndim) return fail(SSM_EINVAL, "%s: expected %d dims, got %d", name, ndim, (int)t->ndim);
+  bool empty = false;
+  for (int i = 0; i < ndim; ++i) empty = empty || t->shape[i] == 0;
+  if (!t->data && !empty) return fail(SSM_EINVAL, "%s: NULL data pointer", name);
   if (t->dtype != dtype)
     return fail(SSM_EUNSUPPORTED, "%s: dtype %d not supported here (%s required)", name, (int)t->dtype,
                 dtype == SSM_BF16 ? "bf16" : "fp8 e4m3");
@@ -40,7 +43,8 @@ int check_tensor(const ssm_tensor* t, const char* name, int ndim, int dtype) {
     if (t->stride[i] < 0 || t->stride[i] % gran != 0)
       return fail(SSM_EUNSUPPORTED, "%s: stride[%d]=%lld must be a non-negative multiple of %d elements", name, i,
                   (long long)t->stride[i], gran);
-  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0) return fail(SSM_EUNSUPPORTED, "%s: data must be 16-byte aligned", name);
+  if (!empty && reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+    return fail(SSM_EUNSUPPORTED, "%s: data must be 16-byte aligned", name);
   return SSM_OK;
 }
 
@@ -210,11 +214,12 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
                const ssm_opts* opts) {
   int rc;
   if ((rc = check_tensor(q, "q", 3, SSM_BF16)) || (rc = check_tensor(out, "out", 3, SSM_BF16))) return rc;
-  if (!kv_lens) return fail(SSM_EINVAL, "kv_lens: NULL");
   if ((rc = check_tau(tau))) return rc;
   const int64_t B = q->shape[0], Hq = q->shape[1], d = q->shape[2];
   for (int i = 0; i < 3; ++i)
     if (out->shape[i] != q->shape[i]) return fail(SSM_EINVAL, "out shape mismatch in dim %d", i);
+  if (B == 0 || Hq == 0) return SSM_OK;  // nothing to compute (the caches, kv_lens and workspace may be empty)
+  if (!kv_lens) return fail(SSM_EINVAL, "kv_lens: NULL");
   int kcap, vcap;
   int64_t krows, vrows, hk, hv;
   if ((rc = check_cache(k_cache, "k_cache", B, d, &kcap, &krows, &hk)) ||
@@ -300,9 +305,10 @@ static int prefill_paged_impl(const ssm_tensor* q, const ssm_kv_cache* k_cache, 
   if ((rc = check_tensor(q, "q", 3, qk8 ? SSM_FP8_E4M3 : SSM_BF16)) || (rc = check_tensor(out, "out", 3, SSM_BF16)))
     return rc;
   if (qk8 && !(q_scale > 0.f && std::isfinite(q_scale))) return fail(SSM_EINVAL, "q_scale must be finite and > 0");
-  if (!q_start || !kv_lens) return fail(SSM_EINVAL, "q_start and kv_lens must be device arrays");
   if ((rc = check_tau(tau))) return rc;
   if (batch < 0 || max_q_len < 0) return fail(SSM_EINVAL, "batch and max_q_len must be >= 0");
+  if (batch == 0) return SSM_OK;  // nothing to compute (kv_lens and the page tables may be empty)
+  if (!q_start || !kv_lens) return fail(SSM_EINVAL, "q_start and kv_lens must be device arrays");
   const int64_t total_q = q->shape[0], Hq = q->shape[1], d = q->shape[2];
   for (int i = 0; i < 3; ++i)
     if (out->shape[i] != q->shape[i]) return fail(SSM_EINVAL, "out shape mismatch in dim %d", i);

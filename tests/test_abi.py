@@ -440,3 +440,24 @@ def test_skip_stats_dtypes_are_checked():
         ssm.SkipStats(counters=torch.zeros(3, dtype=torch.int64)).c()
     with pytest.raises(ValueError, match="unit_gap"):
         ssm.SkipStats(unit_gap=torch.zeros(4, 2, dtype=torch.float32)[:, 0]).c()
+
+
+def test_empty_problems_are_no_ops_with_null_data(lib):
+    """Empty views may carry NULL data (torch's empty tensors do); a call with nothing to compute returns
+    SSM_OK without a launch (no GPU needed), and an empty decode needs no workspace or kv_lens."""
+    opts = ssm.Opts(0.0, 0, 0, 0, None, 0, 0)
+    q, k, v, o = desc([1, 0, 8, 128], data=None), desc([1, 0, 2, 128], data=None), \
+        desc([1, 0, 2, 128], data=None), desc([1, 0, 8, 128], data=None)
+    rc = lib.ssm_prefill(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, 1, -6.9, ctypes.byref(o), None, None,
+                         ctypes.byref(opts))
+    assert rc == ssm.SSM_OK, ssm.ssm_last_error()
+    qd, od = desc([0, 8, 128], data=None), desc([0, 8, 128], data=None)
+    kc = cache([0, 2, 64, 128])
+    rc = lib.ssm_decode(ctypes.byref(qd), ctypes.byref(kc), ctypes.byref(kc), None, -6.9, ctypes.byref(od), None,
+                        None, ctypes.byref(opts))
+    assert rc == ssm.SSM_OK, ssm.ssm_last_error()
+    # a non-empty view still needs its data
+    q = desc([1, 4, 8, 128], data=None)
+    rc = lib.ssm_prefill(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 4, 1, -6.9, ctypes.byref(o), None, None,
+                         ctypes.byref(opts))
+    assert rc == ssm.SSM_EINVAL

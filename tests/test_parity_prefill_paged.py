@@ -232,3 +232,31 @@ def test_separate_value_page_table_matches_shared():
     got = ssm.ssm_prefill_paged(q, kp, vp2, pt_d, qs, kl, cb["max_q"], tau=-LN1000, v_page_table=v_pt2_d)
     torch.cuda.synchronize()
     assert torch.equal(got, ref), "separate V page table changed the output"
+
+
+def test_empty_inputs_are_no_ops():
+    """Empty torch tensors (NULL data) through every entry point: nothing launched, no error, outputs untouched."""
+    import long_context_flash_amd as ssm
+    import torch
+    dev = "cuda"
+    bf, f8 = torch.bfloat16, torch.float8_e4m3fn
+    q = torch.empty(1, 0, 8, 128, dtype=bf, device=dev)
+    kv = torch.empty(1, 0, 2, 128, dtype=bf, device=dev)
+    assert ssm.ssm_prefill(q, kv, kv).shape == (1, 0, 8, 128)
+    assert ssm.ssm_prefill_fp8qk(q.to(f8), 1.0, kv.to(f8), 1.0, kv).shape == (1, 0, 8, 128)
+    pool = torch.zeros(4, 2, 64, 128, dtype=bf, device=dev)
+    lens0 = torch.empty(0, dtype=torch.int32, device=dev)
+    out = ssm.ssm_decode(torch.empty(0, 8, 128, dtype=bf, device=dev), pool, pool, lens0,
+                         page_table=torch.empty(0, 4, dtype=torch.int32, device=dev))
+    assert out.shape == (0, 8, 128)
+    # a batch of chunks with no queries at all, and an empty batch
+    pt = torch.zeros(2, 4, dtype=torch.int32, device=dev)
+    qs = torch.zeros(3, dtype=torch.int32, device=dev)
+    kl = torch.full((2,), 100, dtype=torch.int32, device=dev)
+    q0 = torch.empty(0, 8, 128, dtype=bf, device=dev)
+    assert ssm.ssm_prefill_paged(q0, pool, pool, pt, qs, kl, 0).shape == (0, 8, 128)
+    assert ssm.ssm_prefill_paged_fp8qk(q0.to(f8), 1.0, pool.to(f8), pool.to(f8), pt, qs, kl, 0, 1.0, 1.0).shape == \
+        (0, 8, 128)
+    assert ssm.ssm_prefill_paged(q0, pool, pool, torch.empty(0, 4, dtype=torch.int32, device=dev),
+                                 torch.zeros(1, dtype=torch.int32, device=dev), lens0, 0).shape == (0, 8, 128)
+    torch.cuda.synchronize()
