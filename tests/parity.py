@@ -368,7 +368,7 @@ def seq_kv_fp8(cb, f8, b):
     return res
 
 
-def run_prefill_paged_gpu(cb, *, Hq, causal, tau, tile_q, device="cuda", fp8=None, fp8q=None):
+def run_prefill_paged_gpu(cb, *, Hq, causal, tau, tile_q, device="cuda", fp8=None, fp8q=None, scale=0.0):
     """fp8: the fp8_pools() of cb (the GPU then reads the e4m3 pools with their scales); fp8q: the
     fp8_q_packed() of cb as well (ssm_prefill_paged_fp8qk: 8-bit queries scored on the fp8 MFMA)."""
     if fp8q is not None and fp8 is None:
@@ -389,17 +389,17 @@ def run_prefill_paged_gpu(cb, *, Hq, causal, tau, tile_q, device="cuda", fp8=Non
     stats = ssm.SkipStats.alloc(B * Hq * nqt, pt.shape[1], device, gaps=True)
     if fp8q is not None:
         out = ssm.ssm_prefill_paged_fp8qk(q, fp8q["q_scale"], kc, vc, pt, qs, kl, cb["max_q"], causal=causal,
-                                          tau=tau, skip_stats=stats, tile_q=tile_q, **scales)
+                                          tau=tau, skip_stats=stats, tile_q=tile_q, scale=scale, **scales)
     else:
         out = ssm.ssm_prefill_paged(q, kc, vc, pt, qs, kl, cb["max_q"], causal=causal, tau=tau, skip_stats=stats,
-                                    tile_q=tile_q, **scales)
+                                    tile_q=tile_q, scale=scale, **scales)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), stats.tile_state.cpu().numpy(), stats.unit_gap.cpu().numpy(),
             stats.counters.cpu().numpy())
 
 
 def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads=None, sample=None, fp8=None,
-                        fp8q=None, strict=True):
+                        fp8q=None, strict=True, scale=0.0):
     """GPU chunked prefill on the whole ragged batch vs the oracle on each sequence (all its units, or the
     (h, q_tile) pairs listed in sample[b]).  fp8: the fp8_pools() of cb; the oracle then reads the
     dequantised pools (every e4m3 value is exact in bf16, so the plain bar applies).  fp8q: the
@@ -410,7 +410,10 @@ def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads
     B = len(seqs)
     log(f"{where}: GPU chunked prefill seqs={seqs} Hq={Hq} causal={causal} tau={tau} tile_q={tile_q} "
         f"fp8={fp8 is not None} fp8q={fp8q is not None}")
-    out, st, gap, cnt = run_prefill_paged_gpu(cb, Hq=Hq, causal=causal, tau=tau, tile_q=tile_q, fp8=fp8, fp8q=fp8q)
+    if fp8q is not None and scale:
+        raise ValueError("the fp8-score bound assumes the default logit scale")
+    out, st, gap, cnt = run_prefill_paged_gpu(cb, Hq=Hq, causal=causal, tau=tau, tile_q=tile_q, fp8=fp8, fp8q=fp8q,
+                                              scale=scale)
     vis, skipped = int((st > 0).sum()), int((st == 2).sum())
     assert list(cnt) == [vis, skipped, vis, vis - skipped], f"{where}: counters {list(cnt)} vs tile_state"
     nqt_max = -(-cb["max_q"] // tile_q)
@@ -441,7 +444,7 @@ def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads
         else:
             kb, vb = dat["k"], dat["v"]
         ref = oracle.prefill(qb, kb, vb, causal=causal, tau=tau, tile_q=tile_q, tile_k=64, units=ounits,
-                             threads=threads)
+                             threads=threads, scale=scale)
         hs = np.arange(Hq).repeat(nqt) if sample is None else hq[:, 0]
         qts = np.tile(np.arange(nqt), Hq) if sample is None else hq[:, 1]
         slack = vmax = None
@@ -459,7 +462,7 @@ def check_prefill_paged(cb, *, Hq, causal, tau, tile_q, where="chunked", threads
         if flips.any():
             ov = np.where(flips, np.where(st_g == 2, 1, 0), -1).astype(np.int8)
             ref = oracle.prefill(qb, kb, vb, causal=causal, tau=tau, tile_q=tile_q, tile_k=64, units=ounits,
-                                 override=ov, threads=threads)
+                                 override=ov, threads=threads, scale=scale)
         got = np.zeros_like(ref["out"])
         q0 = cb["q_start"][b]
         pairs = [(h, qt) for h in range(Hq) for qt in range(nqt)] if sample is None else [tuple(x) for x in hq]

@@ -154,9 +154,13 @@ def test_separate_value_page_table_matches_shared():
 
 @pytest.mark.parametrize("scale", [0.05, 0.3])
 def test_custom_logit_scale(scale):
-    """A logit scale other than 1/sqrt(d) on both sides, contiguous and paged, split-local and seeded."""
+    """A logit scale other than 1/sqrt(d) on both sides, contiguous and paged, split-local and seeded, and over
+    an fp8 cache."""
     data = synth.gen_decode(_small(seed=32), contiguous=True, paged=True)
     for paged in (False, True):
         for seeded in (False, True):
             check_decode(data, tau=-4.0, num_splits=8, paged=paged, sink_seed=seeded, scale=scale,
                          where=f"decode scale={scale} paged={paged} seeded={seeded}")
+    # over an fp8 cache the key scale multiplies the logit scale
+    check_decode(data, tau=-4.0, num_splits=8, paged=True, scale=scale, fp8=synth.fp8_kv(data),
+                 where=f"decode scale={scale} fp8")

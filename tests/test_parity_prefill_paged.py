@@ -260,3 +260,13 @@ def test_empty_inputs_are_no_ops():
     assert ssm.ssm_prefill_paged(q0, pool, pool, torch.empty(0, 4, dtype=torch.int32, device=dev),
                                  torch.zeros(1, dtype=torch.int32, device=dev), lens0, 0).shape == (0, 8, 128)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+def test_custom_logit_scale(scale):
+    """A logit scale other than 1/sqrt(d) (opts.scale) through the chunked prefill, bf16 and fp8 pages."""
+    w = synth.replace(SMALL, d=128)
+    cb = chunk_batch(w, [(129, 700), (300, 300), (63, 1000)], seed=12)
+    for f8 in (None, fp8_pools(cb)):
+        check_prefill_paged(cb, Hq=w.Hq, causal=True, tau=-math.log(100.0), tile_q=128, fp8=f8, scale=scale,
+                            where=f"chunked scale={scale} fp8={f8 is not None}")
