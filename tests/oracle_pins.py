@@ -573,9 +573,55 @@ def pin_worked_example_sink_seed(lib=None):
     assert list(r["gamma"][0]) == [math.inf, 5.0, -2.0, -10.0], "W6 gaps against the seed"
 
 
+def _bf16_bits_and_values(x):
+    """torch's round-to-nearest-even bf16 of x: (uint16 bit patterns, their values as float64 via torch)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16), t.to(torch.float64).numpy()
+
+
+def pin_input_widening(lib=None):
+    """The oracle's bf16 and fp32 inputs are the values they encode: on bf16 bit patterns it must give exactly
+    (bit for bit: outputs, unit gaps, masks) what it gives on torch's float64 decoding of the same bf16 values,
+    and on fp32 arrays exactly what it gives on numpy's float64 widening of them.  Both prefill and decode, with
+    planted tiles so that some tiles are skipped and the masks are compared too."""
+    q, k, v = prefill_inputs(21, 1, 300, 4, 2, 64, planted=2)
+    for causal in (True, False):
+        ref = None
+        for variant in ("bf16", "fp32"):
+            if variant == "bf16":
+                (qb, qd), (kb, kd), (vb, vd) = (_bf16_bits_and_values(x) for x in (q, k, v))
+                a = oracle.prefill(qb, kb, vb, causal=causal, tau=-LN1000, tile_q=64, lib=lib)
+                b = oracle.prefill(qd, kd, vd, causal=causal, tau=-LN1000, tile_q=64, lib=lib)
+            else:
+                q32, k32, v32 = (x.astype(np.float32) for x in (q, k, v))
+                a = oracle.prefill(q32, k32, v32, causal=causal, tau=-LN1000, tile_q=64, lib=lib)
+                b = oracle.prefill(*(x.astype(np.float64) for x in (q32, k32, v32)), causal=causal, tau=-LN1000,
+                                   tile_q=64, lib=lib)
+            for key in ("out", "gamma", "state"):
+                assert np.array_equal(a[key], b[key], equal_nan=True), f"prefill {variant} widening differs in {key}"
+            assert (a["state"] == oracle.SKIPPED).any(), "the case must skip some tiles"
+            ref = a["out"] if ref is None else ref
+        # bf16 rounding moves the output by far less than the output itself
+        assert np.abs(ref - a["out"]).max() < 0.05
+    qd_, kd_, vd_, lens = decode_planted(22, B=2, Hq=8, Hkv=2, d=64, smax=1024)
+    for variant in ("bf16", "fp32"):
+        if variant == "bf16":
+            (qb, qd), (kb, kd), (vb, vd) = (_bf16_bits_and_values(x) for x in (qd_, kd_, vd_))
+            a = oracle.decode(qb, kb, vb, lens, tau=-LN1000, num_splits=4, lib=lib)
+            b = oracle.decode(qd, kd, vd, lens, tau=-LN1000, num_splits=4, lib=lib)
+        else:
+            x32 = [x.astype(np.float32) for x in (qd_, kd_, vd_)]
+            a = oracle.decode(*x32, lens, tau=-LN1000, num_splits=4, lib=lib)
+            b = oracle.decode(*(x.astype(np.float64) for x in x32), lens, tau=-LN1000, num_splits=4, lib=lib)
+        for key in ("out", "gamma", "state"):
+            assert np.array_equal(a[key], b[key], equal_nan=True), f"decode {variant} widening differs in {key}"
+        assert (a["state"] == oracle.SKIPPED).any(), "the decode case must skip some tiles"
+
+
 ALL_PINS = [pin_dense_prefill, pin_dense_decode, pin_longdouble_bruteforce, pin_forms_agree, pin_mask_invariants,
             pin_uniform_scores, pin_dropped_mass, pin_split_invariance, pin_output_given_mask, pin_worked_examples,
-            pin_sink_seed, pin_worked_example_sink_seed, pin_fp8_kv, pin_chunked_prefill, pin_worked_example_chunk]
+            pin_sink_seed, pin_worked_example_sink_seed, pin_fp8_kv, pin_chunked_prefill, pin_worked_example_chunk,
+            pin_input_widening]
 
 
 def run_all(lib=None):

@@ -49,6 +49,13 @@ MUTANTS = [
      "const double mul = src == u->k ? u->v_mul : u->v_mul;", 1),
     ("combine_equal_weights", "double w = exp(ls[(int64_t)s * nr + r] - big);", "double w = ls[(int64_t)s * nr + r] > -INFINITY ? 1.0 : 0.0;", 1),
     ("tile_max_includes_next_key", "j < (t + 1) * T && j < nk", "j <= (t + 1) * T && j < nk", 1),
+    ("bf16_shift_15", "[i] << 16;", "[i] << 15;", 1),
+    ("bf16_low_half_of_word", "uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;",
+     "uint32_t bits = (uint32_t)((const uint16_t*)base)[i];", 1),
+    ("f32_truncated_to_bf16", "if (dt == ORACLE_F32) return (double)((const float*)base)[i];",
+     "if (dt == ORACLE_F32) { uint32_t u; memcpy(&u, (const float*)base + i, 4); u &= 0xffff0000u; float f; "
+     "memcpy(&f, &u, 4); return (double)f; }", 1),
+    ("dtype_codes_swapped", "if (dt == ORACLE_F32) return", "if (dt == ORACLE_BF16) return", 1),
     ("split_size_floor", "const int tps = (nt + P - 1) / P;", "const int tps = nt / P > 0 ? nt / P : 1;", 1),
 ]
 
