@@ -145,6 +145,25 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+# standalone measurement programs of this benchmark (not part of the library): the MFMA rate this GPU sustains
+# with zero and random operands, and the HBM streaming-read rate in the decode's load shapes
+CEILING_PROGRAMS = ("mfma_ceiling", "read_ceiling")
+CEILING_DIR = os.path.join(ROOT, "_build", "ceilings")
+
+
+def build_ceiling_programs():
+    """Compile mfma_ceiling.hip and read_ceiling.hip (next to this file) into _build/ceilings/."""
+    from long_context_flash_amd.build import HIPCC_FLAGS, hipcc
+    os.makedirs(CEILING_DIR, exist_ok=True)
+    for name in CEILING_PROGRAMS:
+        exe = os.path.join(CEILING_DIR, name)
+        r = subprocess.run([hipcc(), *HIPCC_FLAGS, os.path.join(ROOT, name + ".hip"), "-o", exe + ".tmp"],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {name}.hip:\n{r.stdout}\n{r.stderr}")
+        os.replace(exe + ".tmp", exe)
+
+
 def prefill_flops(w, visited, kept):
     dense = 4.0 * w.B * w.Hq * w.d * (w.S * (w.S + 1) / 2 if w.causal else w.S * w.S)
     per_tile = 2.0 * w.tile_q * w.tile_k * w.d
@@ -447,55 +466,271 @@ def time_chunked_prefill(ssm, torch, np, w, data, tau, steps, dev):
     return res
 
 
-def cpu_baseline_prefill(w, data, threads, n_units=256):
-    """Time the fp64 oracle on a bounded sample of prefill units; dense-equivalent TFLOP/s."""
-    import numpy as np
-    import oracle
+def leg_decode_32k(ssm, torch, np, steps, dev, threads, cpu=True):
+    """decode_b8_kv32k (batch 8, 64/8 heads, d 128, contiguous 32K caches, tau = -ln 1000) with 16 split-local
+    scans, one scan, and 16 sink-seeded scans: GPU time, sparsity and HBM rate of each, beside the oracle's time
+    on all 8 sequences of the same input and the parity of the timed output."""
+    import synth
+    w = synth.DECODE_32K
+    tau = w.taus[0]
+    data = synth.gen_decode(w, threads=threads)
+    dq = ssm.bf16_from_bits(data["q"], dev)
+    kc, vc = ssm.bf16_from_bits(data["k_cache"], dev), ssm.bf16_from_bits(data["v_cache"], dev)
+    lens = torch.from_numpy(data["kv_lens"]).to(dev)
+    out = torch.empty_like(dq)
+    max_tiles = -(-kc.shape[2] // 64)
+    state = torch.zeros(w.B * w.Hkv, max_tiles, dtype=torch.uint8, device=dev)
+    rows = []
+    for name, P, seeded in (("split_local_p16", 16, False), ("one_scan_p1", 1, False), ("sink_seeded_p16", 16, True)):
+        ws = ssm.decode_workspace(w.B, w.Hq, w.d, P, dev)
+        cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+        run = lambda st: ssm.ssm_decode(dq, kc, vc, lens, tau=tau, out=out, num_splits=P, workspace=ws,
+                                        skip_stats=st, sink_seed=seeded)
+        ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps)
+        got = out.float().cpu().numpy()
+        c = cnt.cpu().numpy() / (steps + 1)
+        state.zero_()
+        run(ssm.SkipStats(tile_state=state))
+        st = state.cpu().numpy()
+        if not (int((st != 0).sum()) == c[0] and int((st == 2).sum()) == c[1]):
+            raise RuntimeError(f"decode 32K {name}: tile states disagree with the timed counters")
+        kb, vk, va, small = decode_bytes(w, data["kv_lens"], st, P)
+        nt = -(-data["kv_lens"] // 64)
+        seed_bytes = 0.0
+        if seeded:
+            for n in (int(x) for x in nt if x > 0):
+                tps = -(-n // P)
+                seed_bytes += (-(-n // tps) - 1) * w.Hkv * 64 * w.d * 2
+        t = ms / 1e3
+        tot = kb + vk + small + seed_bytes
+        row = {"variant": name, "num_splits": P, "sink_seed": seeded, "ms": round(ms, 4),
+               "sparsity": round(float(c[1]) / float(c[0]), 4), "kv_gbps": round((kb + vk) / t / 1e9, 1),
+               "total_gbps": round(tot / t / 1e9, 1), "hbm_frac": round(tot / t / 1e9 / HBM_PEAK_GBPS, 4)}
+        if cpu:
+            base, par = cpu_baseline_decode(np, w, data, tau, threads, P, got, st, sink_seed=seeded)
+            row["oracle_kv_gbps"] = round(base["value"], 3)
+            row["oracle_seconds"] = base["seconds"]
+            row["gpu_over_oracle"] = round(row["kv_gbps"] / base["value"], 1)
+            row["parity"] = par
+        rows.append(row)
+        del ws
+    del kc, vc
+    return {"workload": f"{w.name} (contiguous, kv_len {w.kv_len}, tau -ln 1000)", "tau": tau,
+            "oracle_threads": threads, "variants": rows}
+
+
+def leg_prefill_16k(ssm, torch, np, steps, dev, threads, cpu=True, n_units=64):
+    """prefill_s16k (batch 1, 64/8 heads, d 128, S 16384 causal) at tau = -inf, -ln 100 and -ln 1000: GPU time,
+    sparsity, dense-equivalent and executed TFLOP/s and the MFMA roofline fraction at each tau, beside the
+    oracle's time on n_units sampled units of the same input and the parity of the timed output there."""
+    import synth
+    w = synth.PREFILL_16K
+    data = synth.gen_prefill(w, threads=threads)
+    q, k, v = (ssm.bf16_from_bits(data[x], dev) for x in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    units_n, nkt = ssm.prefill_stats_shape(w.B, w.S, w.Hq, w.tile_q)
+    state = torch.zeros(units_n, nkt, dtype=torch.uint8, device=dev)
+    units, heads, qts = prefill_sample_units(np, w, n_units)
+    rows = []
+    for tau in w.taus:
+        cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+        run = lambda st: ssm.ssm_prefill(q, k, v, causal=True, tau=tau, out=out, skip_stats=st, tile_q=w.tile_q)
+        ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps)
+        got = gather_prefill_rows(torch, np, out, w, heads, qts)
+        c = cnt.cpu().numpy() / (steps + 1)
+        state.zero_()
+        run(ssm.SkipStats(tile_state=state))
+        st = state.cpu().numpy()
+        if not (int((st != 0).sum()) == c[0] and int((st == 2).sum()) == c[1]):
+            raise RuntimeError("prefill 16K: tile states disagree with the timed counters")
+        visited, skipped = float(c[0]), float(c[1])
+        dense, executed = prefill_flops(w, visited, visited - skipped)
+        t = ms / 1e3
+        row = {"tau": None if math.isinf(tau) else round(tau, 4), "ms": round(ms, 4),
+               "sparsity": round(skipped / visited, 4), "dense_tflops": round(dense / t / 1e12, 2),
+               "executed_tflops": round(executed / t / 1e12, 2),
+               "mfma_frac": round(executed / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        if cpu:
+            base, par = cpu_baseline_prefill(np, w, data, tau, threads, units, got, st[units])
+            row["oracle_dense_tflops"] = round(base["value"], 5)
+            row["oracle_seconds"] = base["seconds"]
+            row["gpu_over_oracle"] = round(row["dense_tflops"] / base["value"], 1)
+            row["parity"] = par
+        rows.append(row)
+    del q, k, v, out, state
+    return {"workload": f"{w.name} (causal, GEN-A rel_frac {w.rel_frac})", "oracle_units": n_units,
+            "oracle_threads": threads, "taus": rows}
+
+
+PARITY_MAX_ABS, PARITY_REL_L2, PARITY_BAND = 1e-2, 3e-3, 1e-3
+
+
+def host_info(threads):
+    """The host the CPU legs ran on: logical CPUs (nproc), those this process may use, the CPU model, and the
+    threads the oracle was given."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model, "threads": threads,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def oracle_threads():
+    """Threads for the oracle: the CPU share this process is given (OMP_NUM_THREADS where the launcher sets
+    it, else every CPU the process may run on)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return max(1, min(usable, share) if share > 0 else usable)
+
+
+def parity_fields(np, got, ref_out, st_gpu, st_ref, gamma_ref, tau):
+    """The timed launch against the oracle on the same units: output max-abs and relative L2 error, and the skip
+    decisions compared on every visited tile whose oracle unit gap lies at least PARITY_BAND from tau (closer
+    tiles may go either way; ref_out must then be the oracle re-run with the GPU's decisions there)."""
+    got = np.asarray(got, np.float64)
+    ref_out = np.asarray(ref_out, np.float64)
+    diff = got - ref_out
+    den = float(np.linalg.norm(ref_out.ravel()))
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    rel = float(np.linalg.norm(diff.ravel()) / den) if den > 0 else 0.0
+    vis = st_ref > 0
+    if math.isinf(tau):
+        amb = np.zeros(st_ref.shape, bool)
+    else:
+        with np.errstate(invalid="ignore"):
+            amb = vis & (np.abs(gamma_ref - tau) < PARITY_BAND)
+    off = vis & ~amb
+    agree = int((off & (st_gpu == st_ref)).sum())
+    return {"max_abs": float("%.4g" % max_abs), "rel_l2": float("%.4g" % rel),
+            "mask_tiles_off_band": int(off.sum()), "mask_agree_off_band": agree,
+            "ambiguous_tiles": int(amb.sum()), "ambiguous_flips": int((amb & (st_gpu != st_ref)).sum()),
+            "unvisited_agree": bool(((st_gpu == 0) == (st_ref == 0)).all()),
+            "pass": bool(max_abs <= PARITY_MAX_ABS and rel <= PARITY_REL_L2 and agree == int(off.sum()))}
+
+
+def flip_override(np, st_gpu, st_ref, gamma_ref, tau):
+    """Oracle mask override that takes the GPU's decision on ambiguous tiles where the two differ (else None)."""
+    if math.isinf(tau):
+        return None
+    with np.errstate(invalid="ignore"):
+        flips = (st_ref > 0) & (np.abs(gamma_ref - tau) < PARITY_BAND) & (st_gpu != st_ref)
+    if not flips.any():
+        return None
+    return np.where(flips, np.where(st_gpu == 2, 1, 0), -1).astype(np.int8)
+
+
+def prefill_sample_units(np, w, n_units):
+    """n_units prefill units (q-tiles spread evenly over the sequence, heads rotating), as unit ids and (h, qt)."""
     nqt = -(-w.S // w.tile_q)
     qts = np.linspace(0, nqt - 1, n_units).round().astype(np.int64)
     heads = (np.arange(n_units) * 11) % w.Hq
-    units = heads * nqt + qts
+    return heads * nqt + qts, heads, qts
+
+
+def gather_prefill_rows(torch, np, out, w, heads, qts):
+    """[n, tile_q, d] float64 rows of a [1, S, Hq, d] output for units (h, qt) (rows past S are 0)."""
+    rows = []
+    for h, qt in zip(heads.tolist(), qts.tolist()):
+        r0, r1 = qt * w.tile_q, min(w.S, (qt + 1) * w.tile_q)
+        x = torch.zeros(w.tile_q, w.d, dtype=torch.float32, device=out.device)
+        x[:r1 - r0] = out[0, r0:r1, h].float()
+        rows.append(x)
+    return torch.stack(rows).cpu().numpy().astype(np.float64)
+
+
+def cpu_baseline_prefill(np, w, data, tau, threads, units, got, st_gpu):
+    """Time the fp64 oracle on a bounded sample of prefill units (dense-equivalent TFLOP/s on the host) and
+    compare it with the timed launch's outputs and decisions on those units."""
+    import oracle
+    nqt = -(-w.S // w.tile_q)
+    qts = units % nqt
     rows_keys = 0.0
     for qt in qts:  # dense-equivalent work of these units: sum over rows of visible keys
         r0, r1 = qt * w.tile_q, min(w.S, (qt + 1) * w.tile_q)
-        rows_keys += sum(i + 1 for i in range(r0, r1))
+        rows_keys += (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2 if w.causal else (r1 - r0) * w.S
     flops = 4.0 * w.d * rows_keys
     t0 = time.perf_counter()
-    oracle.prefill(data["q"], data["k"], data["v"], causal=True, tau=w.taus[0], tile_q=w.tile_q, tile_k=w.tile_k,
-                   units=units, threads=threads)
+    ref = oracle.prefill(data["q"], data["k"], data["v"], causal=w.causal, tau=tau, tile_q=w.tile_q,
+                         tile_k=w.tile_k, units=units, threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_units} prefill units (q-tiles spread evenly over 0..{nqt - 1}, heads rotating) of the "
-                      f"128K prefill, {flops / 1e9:.1f} dense-equiv GFLOP in {dt:.1f} s",
-            "seconds": dt}
+    ov = flip_override(np, st_gpu, ref["state"], ref["gamma"], tau)
+    ref_out = ref["out"] if ov is None else oracle.prefill(
+        data["q"], data["k"], data["v"], causal=w.causal, tau=tau, tile_q=w.tile_q, tile_k=w.tile_k, units=units,
+        override=ov, threads=threads)["out"]
+    return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+             "sample": f"{len(units)} prefill units (q-tiles spread evenly over 0..{nqt - 1}, heads rotating) of "
+                       f"{w.name}, {flops / 1e9:.1f} dense-equiv GFLOP in {dt:.1f} s",
+             "seconds": round(dt, 3)},
+            parity_fields(np, got, ref_out, st_gpu, ref["state"], ref["gamma"], tau))
 
 
-def cpu_baseline_decode(w, data, tau, threads, chunk=4):
-    """The oracle on every sequence of the decode workload (timed per chunk of sequences, gathered from the
-    page pool into contiguous caches outside the timed region)."""
-    import numpy as np
+def paged_to_contiguous(np, w, data, b):
+    """Sequences b of a paged gen_decode() input as contiguous [len(b), Hkv, smax, d] caches (layout only)."""
+    lens = data["kv_lens"]
+    nt = -(-lens[b] // 64)
+    smax = int(max(nt.max(), 1)) * 64
+    kc = np.zeros((len(b), w.Hkv, smax, w.d), np.uint16)
+    vc = np.zeros_like(kc)
+    for i, bb in enumerate(b):
+        pages = data["page_table"][bb, :nt[i]]
+        kc[i, :, :nt[i] * 64] = data["k_pool"][pages].transpose(1, 0, 2, 3).reshape(w.Hkv, -1, w.d)
+        vc[i, :, :nt[i] * 64] = data["v_pool"][pages].transpose(1, 0, 2, 3).reshape(w.Hkv, -1, w.d)
+    return kc, vc
+
+
+def cpu_baseline_decode(np, w, data, tau, threads, num_splits, got, st_gpu, sink_seed=False, chunk=4):
+    """The oracle on every sequence of a decode workload (KV GB/s on the host, timed per chunk of sequences;
+    paged inputs are gathered into contiguous caches outside the timed region), compared with the timed
+    launch's outputs got [B, Hq, d] and tile states st_gpu [B*Hkv, max_tiles]."""
     import oracle
     lens = data["kv_lens"]
-    dt = 0.0
-    kv = 0.0
+    G = w.Hq // w.Hkv
+    dt = kv = 0.0
+    outs, refs, sg, sr, gr = [], [], [], [], []
     for c0 in range(0, w.B, chunk):
         b = np.arange(c0, min(w.B, c0 + chunk))
-        nt = -(-lens[b] // 64)
-        smax = int(nt.max()) * 64
-        kc = np.zeros((len(b), w.Hkv, smax, w.d), np.uint16)
-        vc = np.zeros_like(kc)
-        for i, bb in enumerate(b):
-            pages = data["page_table"][bb, :nt[i]]
-            kc[i, :, :nt[i] * 64] = data["k_pool"][pages].transpose(1, 0, 2, 3).reshape(w.Hkv, -1, w.d)
-            vc[i, :, :nt[i] * 64] = data["v_pool"][pages].transpose(1, 0, 2, 3).reshape(w.Hkv, -1, w.d)
+        if "k_pool" in data:
+            kc, vc = paged_to_contiguous(np, w, data, b)
+        else:
+            kc, vc = data["k_cache"][b], data["v_cache"][b]
         t0 = time.perf_counter()
-        r = oracle.decode(data["q"][b], kc, vc, lens[b], tau=tau, num_splits=w.num_splits, threads=threads)
+        r = oracle.decode(data["q"][b], kc, vc, lens[b], tau=tau, num_splits=num_splits, sink_seed=sink_seed,
+                          threads=threads)
         dt += time.perf_counter() - t0
         kept = r["state"] == 1
         kv += float(lens[b].astype(np.int64).sum()) * w.Hkv * w.d * 2 + float(kept.sum()) * 64 * w.d * 2
-    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"all {w.B} decode sequences (every KV group), {chunk} sequences per oracle call",
-            "seconds": dt}
+        maxt = r["state"].shape[1]
+        stg = st_gpu[c0 * w.Hkv:(c0 + len(b)) * w.Hkv]
+        if stg[:, maxt:].any():
+            raise RuntimeError("decode: tiles past the sequences marked visited")
+        stg = stg[:, :maxt]
+        ov = flip_override(np, stg, r["state"], r["gamma"], tau)
+        ro = r["out"] if ov is None else oracle.decode(data["q"][b], kc, vc, lens[b], tau=tau,
+                                                       num_splits=num_splits, sink_seed=sink_seed, override=ov,
+                                                       threads=threads)["out"]
+        outs.append(got[b].reshape(len(b) * w.Hkv, G, w.d))
+        refs.append(ro)
+        sg.append(stg.ravel())
+        sr.append(r["state"].ravel())
+        gr.append(r["gamma"].ravel())
+    par = parity_fields(np, np.concatenate(outs), np.concatenate(refs), np.concatenate(sg), np.concatenate(sr),
+                        np.concatenate(gr), tau)
+    return ({"value": kv / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+             "sample": f"all {w.B} sequences of {w.name} (every KV group), {chunk} sequences per oracle call",
+             "seconds": round(dt, 3)}, par)
 
 
 def main():
@@ -523,10 +758,10 @@ def main():
         summarize_traffic(*args.summarize_traffic, args.traffic_command)
         return
     if args.mfma_ceiling or args.read_ceiling:
-        exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_flash_amd",
-                           "mfma_ceiling" if args.mfma_ceiling else "read_ceiling")
+        exe = os.path.join(CEILING_DIR, "mfma_ceiling" if args.mfma_ceiling else "read_ceiling")
         if not os.path.exists(exe):
-            sys.exit(f"{exe} is missing: build with `python -m long_context_flash_amd.build`")
+            sys.exit(f"{exe} is missing: build it with `python -c 'import bench; bench.build_ceiling_programs()'` "
+                     "(__graft_entry__.build() does)")
         sys.exit(subprocess.run([exe]).returncode)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (each GPU would run the same "
@@ -541,7 +776,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    threads = synth.default_threads()
+    threads = synth.default_threads()   # input generation
+    cpu_threads = oracle_threads()      # the oracle legs: this process's CPU share
     run_prefill = args.only in (None, "prefill")
     run_decode = args.only in (None, "decode")
 
@@ -605,6 +841,23 @@ def main():
     d_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
     step_ms = wall * 1e3 / args.steps
     log(f"prefill ms {['%.2f' % x for x in p_ms]}  decode ms {['%.3f' % x for x in d_ms]}  wall/step {step_ms:.2f}")
+    # the timed launches' outputs (before the later legs reuse the output buffers), for the parity check of the
+    # CPU-baseline legs; and the prefill's per-tile decisions from one more, untimed call on the same inputs
+    if run_prefill:
+        p_units, p_heads, p_qts = prefill_sample_units(np, pw, 256)
+        p_got = gather_prefill_rows(torch, np, pout, pw, p_heads, p_qts)
+        n_units, nkt = ssm.prefill_stats_shape(pw.B, pw.S, pw.Hq, pw.tile_q)
+        pstate = torch.zeros(n_units, nkt, dtype=torch.uint8, device=dev)
+        ssm.ssm_prefill(q, k, v, causal=True, tau=tau_p, out=torch.empty_like(pout),
+                        skip_stats=ssm.SkipStats(tile_state=pstate), tile_q=pw.tile_q)
+        pst_all = pstate.cpu().numpy()
+        c_t = pcnt.cpu().numpy() / args.steps
+        if not (int((pst_all != 0).sum()) == c_t[0] and int((pst_all == 2).sum()) == c_t[1]):
+            raise RuntimeError("prefill tile states disagree with the timed counters")
+        p_st = pst_all[p_units]
+        del pstate, pst_all
+    if run_decode:
+        d_got = dout.float().cpu().numpy()
 
     res = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(step_ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -648,6 +901,7 @@ def main():
         ssm.ssm_decode(dq, kp, vp, lens, tau=tau_d, out=dout, page_table=pt, num_splits=dw.num_splits,
                        workspace=ws, skip_stats=ssm.SkipStats(tile_state=dstate))
         state = dstate.cpu().numpy()
+        dstate_timed = state
         if not (int((state != 0).sum()) == c[0] and int((state == 2).sum()) == c[1]):
             raise RuntimeError(f"decode tile states {int((state != 0).sum())}/{int((state == 2).sum())} disagree "
                                f"with the timed counters {c[0]}/{c[1]}")
@@ -688,6 +942,12 @@ def main():
         res["decode_fp8_kv"]["speedup_vs_bf16"] = round(res["decode_ms"] / res["decode_fp8_kv"]["ms"], 3)
         res["decode_tau_sweep"] = time_decode_tau_sweep(ssm, torch, np, dw, dq, kp, vp, pt, lens, dout, ws, args.steps,
                                                         dev)
+        log("decode 32K legs")
+        res["decode_32k"] = leg_decode_32k(ssm, torch, np, args.steps, dev, cpu_threads, cpu=not args.no_cpu_baseline)
+    if run_prefill and not args.main_only:
+        log("prefill 16K legs")
+        res["prefill_16k"] = leg_prefill_16k(ssm, torch, np, args.steps, dev, cpu_threads,
+                                             cpu=not args.no_cpu_baseline)
         read_ceiling = recorded_read_ceiling()
         if read_ceiling:
             for leg in ("decode_sink_seeded", "decode_fp8_kv"):
@@ -701,13 +961,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu_baseline:
+        host = host_info(cpu_threads)
         if run_prefill:
             log("cpu baseline: oracle on sampled prefill units")
-            res["cpu_baseline"] = cpu_baseline_prefill(pw, pdata, threads)
-            if run_decode:
-                res["cpu_baseline_decode"] = cpu_baseline_decode(dw, ddata, tau_d, threads)
-        elif run_decode:
-            res["cpu_baseline"] = cpu_baseline_decode(dw, ddata, tau_d, threads)
+            base, par = cpu_baseline_prefill(np, pw, pdata, tau_p, cpu_threads, p_units, p_got, p_st)
+            base["host"] = host
+            res["cpu_baseline"] = base
+            res["parity"] = {"prefill": par}
+        if run_decode:
+            log("cpu baseline: oracle on every decode sequence")
+            base, par = cpu_baseline_decode(np, dw, ddata, tau_d, cpu_threads, dw.num_splits, d_got,
+                                            dstate_timed)
+            base["host"] = host
+            res["cpu_baseline" if not run_prefill else "cpu_baseline_decode"] = base
+            res.setdefault("parity", {})["decode"] = par
+        res["parity"]["bar"] = {"max_abs": PARITY_MAX_ABS, "rel_l2": PARITY_REL_L2, "mask_band": PARITY_BAND,
+                                "what": "the timed launches' outputs and skip decisions against the fp64 oracle "
+                                        "on the cpu_baseline samples"}
     print(json.dumps(res, allow_nan=False), flush=True)
 
 

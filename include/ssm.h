@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 
 enum {
   SSM_OK = 0,
@@ -121,7 +121,10 @@ typedef struct {
  * exact softmax over the kept keys. */
 #define SSM_DECODE_SINK_SEED 1
 
-/* Causal or full prefill (self-attention, S_q = S_k = seqlen).
+/* Causal or full prefill (self-attention, S_q = S_k = seqlen): the context phase of the recap of
+ * "Accelerating Long-Context Inference with Skip Softmax in NVIDIA TensorRT-LLM" (Detailed Analysis: a key
+ * block whose local maximum trails the running maximum by more than tau is skipped whole; Skip Softmax
+ * Mechanism) and of the news item (Benefits and Implementation: the prefill phase).
  *   q   [B, S, Hq, d]  bf16    k, v [B, S, Hkv, d] bf16    out [B, S, Hq, d] bf16
  *   d in {64, 128}; Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv).
  *   causal != 0: query i attends to keys j <= i (top-left aligned).
@@ -143,7 +146,9 @@ int ssm_prefill_fp8qk(const ssm_tensor* q, float q_scale, const ssm_tensor* k, f
                       int32_t seqlen, int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats,
                       void* stream, const ssm_opts* opts);
 
-/* Single-token GQA decode with split-K and a log-sum-exp combine.
+/* Single-token GQA decode with split-K and a log-sum-exp combine: the generation phase of the same rule (recap,
+ * Key Points and Detailed Analysis; news item, Benefits and Implementation: in decode the saving is the memory
+ * traffic of the skipped blocks, so a skipped tile's V rows are never read).
  *   q [B, Hq, d] bf16; out [B, Hq, d] bf16; K/V caches bf16 or fp8 e4m3 (see ssm_kv_cache: an fp8
  *   cache is read at half the bytes and each code is converted exactly to bf16 for the MFMAs); kv_lens device int32 [B], each in [0, Smax or
  *   max_pages*page_size]; query b attends to keys j < kv_lens[b].  kv_len 0 gives 0.
@@ -158,7 +163,9 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
                const ssm_opts* opts);
 
 /* Chunked prefill against a paged KV cache (a serving context phase: new tokens attend to the cached
- * context and to each other).  A ragged batch of `batch` sequences:
+ * context and to each other); the skip rule of ssm_prefill (recap, Detailed Analysis and Skip Softmax
+ * Mechanism) applied to the context phase the news item's Benefits and Implementation names, over the
+ * decode's paged cache.  A ragged batch of `batch` sequences:
  *   q, out [total_q, Hq, d] bf16: sequence b's n_b = q_start[b+1] - q_start[b] query rows are rows
  *     q_start[b] .. q_start[b+1]-1 (q_start: device int32 [batch+1], 0 <= n_b <= max_q_len);
  *   k_cache, v_cache: paged pools [pages, Hkv, 64, d] with page tables of equal length (see ssm_kv_cache),
@@ -187,8 +194,9 @@ int ssm_prefill_paged_fp8qk(const ssm_tensor* q, float q_scale, const ssm_kv_cac
                             int32_t max_q_len, int32_t causal, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats,
                             void* stream, const ssm_opts* opts);
 
-/* Bytes of device workspace ssm_decode needs (fp32 partial outputs and
- * log-sum-exps per (b, query head, split)).  0 for invalid arguments. */
+/* Bytes of device workspace ssm_decode needs: fp32 partial outputs and log-sum-exps per (b, query head,
+ * split), and for batches up to 8192 the longest-first dispatch order of the sequences (int32 per sequence,
+ * written by the call).  0 for invalid arguments. */
 size_t ssm_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int32_t num_splits);
 
 const char* ssm_strerror(int code);   /* static text for a return code */

@@ -60,7 +60,7 @@ class Opts(ctypes.Structure):
                 ("decode_flags", ctypes.c_int32)]
 
 
-ABI_VERSION = 6               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 7               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
 DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
 
 

@@ -49,7 +49,6 @@ namespace ssm {
 constexpr int kDecTK = 64;
 constexpr int kDecWaves = 4;
 constexpr int kDecMaxG = 16;
-constexpr int kDecSortMax = 1024;  // batches up to this size are dispatched longest sequence first
 
 // Buffer resource over the valid rows of key tile t of (b, g) in a pool of ES-byte elements: rows past
 // kv_len, and every row of a tile whose page id is outside the pool, read as zero.
@@ -84,9 +83,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   __shared__ float cl[kDecWaves][kDecMaxG];
   __shared__ __attribute__((aligned(16))) float cacc[kDecWaves][kDecMaxG][D];
 
-  __shared__ int lens_lds[kDecSortMax];
   __shared__ unsigned cnt_lds[kDecWaves][2];
-  __shared__ int b_lds;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform: the tile index, its page id and its buffer resource then live in scalar registers
@@ -99,25 +96,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   const int G = a.G;
   auto clamp_len = [&](int l) { return l < 0 ? 0 : (l > kv_cap ? kv_cap : l); };
 
-  // Longest sequences first: workgroups are dispatched in index order, so the rank-th longest
-  // sequence (ties by index) takes the rank-th group of Hkv * P workgroups and the short ones
-  // fill the tail.  Batches larger than kDecSortMax keep the plain order.
-  int b = rank;
-  if (a.B <= kDecSortMax) {
-    for (int i = tid; i < a.B; i += 256) lens_lds[i] = clamp_len(a.kv_lens[i]);
-    __syncthreads();
-    for (int c = tid; c < a.B; c += 256) {
-      const int lc = lens_lds[c];
-      int r = 0;
-      for (int j = 0; j < a.B; ++j) {
-        const int lj = lens_lds[j];
-        r += lj > lc || (lj == lc && j < c);
-      }
-      if (r == rank) b_lds = c;
-    }
-    __syncthreads();
-    b = __builtin_amdgcn_readfirstlane(b_lds);
-  }
+  // Longest sequences first: workgroups are dispatched in index order, so the rank-th longest sequence
+  // (decode_order_kernel's order; plain order for batches above kDecSortMax) takes the rank-th group of
+  // Hkv * P workgroups and the short ones fill the tail.
+  const int b = a.order ? __builtin_amdgcn_readfirstlane(load_uniform_i32(a.order, rank)) : rank;
   const int bg = b * a.Hkv + g;
   const int len = clamp_len(__builtin_amdgcn_readfirstlane(a.kv_lens[b]));
   const int nt = (len + kDecTK - 1) / kDecTK;
@@ -201,8 +183,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if constexpr (ES == 2) vreg[st][e] = buffer_load_16(r, vvo[st][e >> 2] + (e & 3) * vrow);
-        else vraw[st][e] = buffer_load_8(r, vvo[st][e >> 2] + (e & 3) * vrow);
+        // lanes whose channels lie past D (D = 64) read outside the resource, i.e. zeros
+        const uint32_t off = v_ch_ok ? vvo[st][e >> 2] + (e & 3) * vrow : 0xffffffffu;
+        if constexpr (ES == 2) vreg[st][e] = buffer_load_16(r, off);
+        else vraw[st][e] = buffer_load_8(r, off);
       }
   };
 
@@ -400,6 +384,27 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   }
 }
 
+// order[r] = the sequence with the r-th longest kv_len (ties by index), lengths clamped to [0, kv_cap]: the
+// dispatch order of decode_split_kernel.  One thread per sequence counts the sequences that precede it; every
+// workgroup stages all B lengths in LDS (B <= kDecSortMax).
+__global__ __launch_bounds__(256) void decode_order_kernel(const int32_t* kv_lens, int B, int kv_cap, int32_t* order) {
+  __shared__ int lens[kDecSortMax];
+  for (int i = threadIdx.x; i < B; i += 256) {
+    const int l = kv_lens[i];
+    lens[i] = l < 0 ? 0 : (l > kv_cap ? kv_cap : l);
+  }
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= B) return;
+  const int lc = lens[c];
+  int r = 0;
+  for (int j = 0; j < B; ++j) {
+    const int lj = lens[j];
+    r += lj > lc || (lj == lc && j < c);
+  }
+  order[r] = c;
+}
+
 // out[b, h, :] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M); 0 when every split is empty.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
@@ -427,6 +432,11 @@ hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hkv * a.num_splits);
   const unsigned cgrid = (unsigned)((int64_t)a.B * a.Hq);
   if (grid == 0) return hipSuccess;
+  if (a.order) {
+    if (a.B > kDecSortMax) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(decode_order_kernel, dim3((a.B + 255) / 256), dim3(256), 0, stream, a.kv_lens, a.B, kv_cap,
+                       a.order);
+  }
   const dim3 blk(256);
   if (d == 128 && !a.kv_fp8)
     hipLaunchKernelGGL((decode_split_kernel<128, 2>), dim3(grid), blk, 0, stream, a, kv_cap, k_pool_pages, v_pool_pages);

@@ -85,12 +85,25 @@ const char* ssm_strerror(int code) {
 
 const char* ssm_last_error(void) { return g_last_error; }
 
+namespace {
+// decode workspace layout: partial outputs [B, Hq, P, d] fp32 | partial LSEs [B, Hq, P] fp32 | dispatch order [B]
+// int32 (batches up to kDecSortMax), each part starting on a 256-byte boundary
+struct DecodeWs {
+  size_t lse_off, order_off, bytes;
+};
+DecodeWs decode_ws_layout(size_t B, size_t Hq, size_t d, size_t P) {
+  const size_t rows = B * Hq * P;
+  DecodeWs w;
+  w.lse_off = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+  w.order_off = (w.lse_off + rows * sizeof(float) + 255) & ~(size_t)255;
+  w.bytes = w.order_off + (B <= (size_t)ssm::kDecSortMax ? B * sizeof(int32_t) : 0);
+  return w;
+}
+}  // namespace
+
 size_t ssm_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int32_t num_splits) {
   if (B < 0 || Hq < 0 || d <= 0 || num_splits <= 0) return 0;
-  const size_t rows = (size_t)B * (size_t)Hq * (size_t)num_splits;
-  const size_t o_bytes = rows * (size_t)d * sizeof(float);
-  const size_t lse_off = (o_bytes + 255) & ~(size_t)255;
-  return lse_off + rows * sizeof(float);
+  return decode_ws_layout((size_t)B, (size_t)Hq, (size_t)d, (size_t)num_splits).bytes;
 }
 
 // qk8: q and k hold e4m3 codes with dequantisation factors q_scale, k_scale (ssm_prefill_fp8qk)
@@ -283,9 +296,10 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
   a.scale_log2 = lscale * 1.4426950408889634f;
   a.tau_raw = std::isinf(tau) ? tau : tau / lscale;
   char* ws_base = static_cast<char*>(opts->workspace);
-  const size_t rows = (size_t)B * Hq * P;
+  const DecodeWs lay = decode_ws_layout((size_t)B, (size_t)Hq, (size_t)d, (size_t)P);
   a.part_o = reinterpret_cast<float*>(ws_base);
-  a.part_lse = reinterpret_cast<float*>(ws_base + ((rows * d * sizeof(float) + 255) & ~(size_t)255));
+  a.part_lse = reinterpret_cast<float*>(ws_base + lay.lse_off);
+  a.order = B <= ssm::kDecSortMax ? reinterpret_cast<int32_t*>(ws_base + lay.order_off) : nullptr;
   a.o = static_cast<uint16_t*>(out->data);
   a.o_sb = out->stride[0]; a.o_sh = out->stride[1];
   if (skip_stats) {

@@ -59,6 +59,7 @@ struct DecodeArgs {
   float scale, scale_log2, tau_raw;  // scale: logit scale per raw q.k product (softmax scale x key scale)
   float* part_o;             // workspace [B, Hq, P, d] fp32
   float* part_lse;           // workspace [B, Hq, P] fp32 (base-2 log-sum-exp of raw-scaled logits)
+  int32_t* order;            // workspace [B]: dispatch order, longest sequence first (NULL: plain order)
   uint16_t* o;               // [B, Hq, d]
   int64_t o_sb, o_sh;
   uint8_t* tile_state;
@@ -69,6 +70,8 @@ struct DecodeArgs {
 // mode 0: bf16; 1: e4m3 q/k scores (contiguous only); 2: e4m3 K/V pages (chunked only); 3: e4m3 queries
 // scored against e4m3 K pages, e4m3 V pages (chunked only)
 hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, int mode, hipStream_t stream);
+constexpr int kDecSortMax = 8192;  // batches up to this size are dispatched longest sequence first
+
 hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
                               hipStream_t stream);
 
