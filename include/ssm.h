@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 7
+#define SSM_ABI_VERSION 8
 
 enum {
   SSM_OK = 0,
@@ -161,6 +161,21 @@ int ssm_prefill_fp8qk(const ssm_tensor* q, float q_scale, const ssm_tensor* k, f
 int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
                const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
                const ssm_opts* opts);
+
+/* ssm_decode without a caller workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same arguments, semantics, outputs and
+ * errors as ssm_decode, except that opts->workspace and opts->workspace_bytes are ignored: the workspace is a
+ * statically sized array in each GPU's memory (32 MiB, held by every GPU the library runs on until the process
+ * ends), whose device address the first call on a device looks up.  The call allocates nothing.
+ *   - Returns SSM_EWORKSPACE when ssm_decode_workspace_bytes(B, Hq, d, num_splits) exceeds 32 MiB (e.g. batch
+ *     32, 64 query heads, d 128 needs 16.9 MB at 16 splits), and SSM_EINVAL when `stream` belongs to a device
+ *     other than the current one; nothing is launched then.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents (nothing in it needs
+ *     clearing: each call writes every byte it reads).  Calls that overlap in time on one GPU (different
+ *     streams, or host threads) race on it: serialise them, e.g. on one stream. */
+int ssm_decode_noalloc(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+                       const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+                       const ssm_opts* opts);
 
 /* Chunked prefill against a paged KV cache (a serving context phase: new tokens attend to the cached
  * context and to each other); the skip rule of ssm_prefill (recap, Detailed Analysis and Skip Softmax

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     ssm_prefill_paged(q, k_cache, v_cache, page_table, ...)     -> out [total_q,Hq,d] bf16
     ssm_prefill_paged_fp8qk(q8, q_scale, k_cache8, v_cache8, ...) -> out (fp8 e4m3 queries over fp8 pages)
     ssm_decode(q, k_cache, v_cache, kv_lens, tau=..., ...)      -> out [B,Hq,d] bf16
+    ssm_decode_noalloc(q, k_cache, v_cache, kv_lens, out=..., ...) -> out (workspace: the library's static scratch)
     ssm_decode_workspace_bytes(B, Hq, d, num_splits)
     ssm_strerror(code), ssm_last_error(), ssm_abi_version()
 """
@@ -29,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EWORKSPACE, SSM_EHIP = range(5)
 SSM_BF16, SSM_FP32, SSM_FP8_E4M3 = 0, 1, 2
-EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_prefill_fp8qk", "ssm_decode", "ssm_prefill_paged", "ssm_prefill_paged_fp8qk",
+EXPORTED_SYMBOLS = ("ssm_prefill", "ssm_prefill_fp8qk", "ssm_decode", "ssm_decode_noalloc", "ssm_prefill_paged", "ssm_prefill_paged_fp8qk",
                     "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error", "ssm_abi_version")
 
 
@@ -60,7 +61,7 @@ class Opts(ctypes.Structure):
                 ("decode_flags", ctypes.c_int32)]
 
 
-ABI_VERSION = 7               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 8               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
 DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
 
 
@@ -85,6 +86,9 @@ def lib():
     L.ssm_decode.restype = ctypes.c_int
     L.ssm_decode.argtypes = [P(Tensor), P(KvCache), P(KvCache), ctypes.c_void_p, ctypes.c_float, P(Tensor),
                              P(SkipStatsC), ctypes.c_void_p, P(Opts)]
+    L.ssm_decode_noalloc.restype = ctypes.c_int
+    L.ssm_decode_noalloc.argtypes = [P(Tensor), P(KvCache), P(KvCache), ctypes.c_void_p, ctypes.c_float, P(Tensor),
+                                     P(SkipStatsC), ctypes.c_void_p, P(Opts)]
     L.ssm_prefill_paged.restype = ctypes.c_int
     L.ssm_prefill_paged.argtypes = [P(Tensor), P(KvCache), P(KvCache), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P(Tensor), P(SkipStatsC),
@@ -325,12 +329,30 @@ def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
     sink_seed: splits after the first start their running maximum at the first key tile's row maxima.
     k_cache/v_cache may be torch.float8_e4m3fn tensors of codes; keys and values are then k_scale * code and
     v_scale * code."""
+    return _decode(q, k_cache, v_cache, kv_lens, tau, out, page_table, v_page_table, num_splits, workspace, skip_stats,
+                   stream, scale, sink_seed, k_scale, v_scale, noalloc=False)
+
+
+def ssm_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_lens: torch.Tensor,
+                       tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
+                       page_table: Optional[torch.Tensor] = None, v_page_table: Optional[torch.Tensor] = None,
+                       num_splits: int = 16, skip_stats: Optional[SkipStats] = None, stream=None, scale: float = 0.0,
+                       sink_seed: bool = False, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """ssm_decode whose workspace is the library's static per-GPU scratch array (ssm_decode_noalloc): the C call
+    allocates nothing.  Pass ``out`` to keep this wrapper from allocating it.  Calls that overlap on one GPU race
+    on the shared scratch."""
+    return _decode(q, k_cache, v_cache, kv_lens, tau, out, page_table, v_page_table, num_splits, None, skip_stats,
+                   stream, scale, sink_seed, k_scale, v_scale, noalloc=True)
+
+
+def _decode(q, k_cache, v_cache, kv_lens, tau, out, page_table, v_page_table, num_splits, workspace, skip_stats,
+            stream, scale, sink_seed, k_scale, v_scale, noalloc):
     _on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, kv_lens=kv_lens, out=out, page_table=page_table,
                v_page_table=v_page_table, workspace=workspace, **(skip_stats.tensors() if skip_stats else {}))
     if out is None:
         out = torch.empty_like(q)
     B, Hq, d = q.shape
-    if workspace is None:
+    if workspace is None and not noalloc:
         workspace = decode_workspace(B, Hq, d, num_splits, q.device)
     vpt = page_table if v_page_table is None else v_page_table
 
@@ -350,12 +372,12 @@ def ssm_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv
         raise ValueError("kv_lens must be a contiguous int32 tensor")
     kc, vc = cache(k_cache, page_table, k_scale), cache(v_cache, vpt, v_scale)
     qd, od = describe(q), describe(out)
-    opts = Opts(float(scale), 0, 64, int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                DECODE_SINK_SEED if sink_seed else 0)
+    ws_ptr, ws_bytes = (None, 0) if noalloc else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    opts = Opts(float(scale), 0, 64, int(num_splits), ws_ptr, ws_bytes, DECODE_SINK_SEED if sink_seed else 0)
     st = skip_stats.c() if skip_stats is not None else None
-    rc = lib().ssm_decode(ctypes.byref(qd), ctypes.byref(kc), ctypes.byref(vc), kv_lens.data_ptr(), float(tau),
-                          ctypes.byref(od), ctypes.byref(st) if st else None, _stream_handle(stream),
-                          ctypes.byref(opts))
+    fn = lib().ssm_decode_noalloc if noalloc else lib().ssm_decode
+    rc = fn(ctypes.byref(qd), ctypes.byref(kc), ctypes.byref(vc), kv_lens.data_ptr(), float(tau), ctypes.byref(od),
+            ctypes.byref(st) if st else None, _stream_handle(stream), ctypes.byref(opts))
     _check(rc)
     return out
 
@@ -378,6 +400,6 @@ def bf16_from_bits(a, device=None) -> torch.Tensor:
     return t.to(device) if device is not None else t
 
 
-__all__ = ["ssm_prefill", "ssm_prefill_fp8qk", "ssm_prefill_paged_fp8qk", "ssm_decode", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
+__all__ = ["ssm_prefill", "ssm_prefill_fp8qk", "ssm_prefill_paged_fp8qk", "ssm_decode", "ssm_decode_noalloc", "ssm_prefill_paged", "ssm_decode_workspace_bytes", "ssm_strerror", "ssm_last_error",
            "ssm_abi_version", "SkipStats", "SsmError", "prefill_stats_shape", "decode_workspace", "bf16_from_bits",
            "lib", "describe", "LIB_PATH", "EXPORTED_SYMBOLS"]

@@ -41,6 +41,8 @@
 // maximum at key tile 0's per-query maxima instead of -inf; each wave scores
 // tile 0 once before its scan.  The combined output stays the exact softmax
 // over the kept keys; the seed only changes which tiles are skipped.
+#include <mutex>
+
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -425,6 +427,36 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const float r = wsum > 0.f ? o / wsum : 0.f;
   const __bf16 x = (__bf16)r;
   a.o[(int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ch] = __builtin_bit_cast(uint16_t, x);
+}
+
+// The decode workspace of ssm_decode_noalloc: one statically sized array in each GPU's memory, held until the
+// process ends.  Host code never uses the array's name as an address: its device address is taken once per
+// device with that device current (hipGetSymbolAddress) and kept here.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (stream) {  // the kernels run on the stream's device: it must be the current one, whose array is used
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != dev) return hipErrorInvalidDevice;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *ptr = ptrs[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_pages, int64_t v_pool_pages,

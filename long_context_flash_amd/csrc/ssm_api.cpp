@@ -222,9 +222,10 @@ static int check_cache(const ssm_kv_cache* c, const char* name, int64_t B, int64
   return SSM_OK;
 }
 
-int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
-               const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
-               const ssm_opts* opts) {
+// noalloc: the workspace is this GPU's static scratch array (ssm_decode_noalloc) instead of opts->workspace
+static int decode_impl(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+                       const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+                       const ssm_opts* opts, bool noalloc) {
   int rc;
   if ((rc = check_tensor(q, "q", 3, SSM_BF16)) || (rc = check_tensor(out, "out", 3, SSM_BF16))) return rc;
   if ((rc = check_tau(tau))) return rc;
@@ -267,10 +268,23 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
       return fail(SSM_EINVAL, "unit_gap needs %lld elements", (long long)need);
   }
   const size_t ws = ssm_decode_workspace_bytes((int)B, (int)Hq, (int)d, P);
-  if (!opts || !opts->workspace) return fail(SSM_EWORKSPACE, "decode needs opts->workspace of %zu bytes", ws);
-  if (opts->workspace_bytes < ws) return fail(SSM_EWORKSPACE, "workspace has %zu bytes, needs %zu", opts->workspace_bytes, ws);
-  if (reinterpret_cast<uintptr_t>(opts->workspace) % 256 != 0) return fail(SSM_EINVAL, "workspace must be 256-byte aligned");
-  if (B == 0 || Hq == 0) return SSM_OK;
+  void* ws_ptr = nullptr;
+  if (noalloc) {
+    if (ws > ssm::kDecodeScratchBytes)
+      return fail(SSM_EWORKSPACE, "this decode needs %zu bytes of workspace; the static scratch of "
+                  "ssm_decode_noalloc holds %zu (use ssm_decode with a caller workspace)", ws, ssm::kDecodeScratchBytes);
+    const hipError_t e = ssm::decode_scratch(static_cast<hipStream_t>(stream), &ws_ptr);
+    if (e == hipErrorInvalidDevice)
+      return fail(SSM_EINVAL, "ssm_decode_noalloc: the stream's device must be the current device");
+    if (e != hipSuccess) return fail(SSM_EHIP, "device scratch lookup failed: %s", hipGetErrorString(e));
+  } else {
+    if (!opts || !opts->workspace) return fail(SSM_EWORKSPACE, "decode needs opts->workspace of %zu bytes", ws);
+    if (opts->workspace_bytes < ws)
+      return fail(SSM_EWORKSPACE, "workspace has %zu bytes, needs %zu", opts->workspace_bytes, ws);
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 256 != 0)
+      return fail(SSM_EINVAL, "workspace must be 256-byte aligned");
+    ws_ptr = opts->workspace;
+  }
 
   ssm::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
@@ -295,7 +309,7 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
   a.scale = lscale;
   a.scale_log2 = lscale * 1.4426950408889634f;
   a.tau_raw = std::isinf(tau) ? tau : tau / lscale;
-  char* ws_base = static_cast<char*>(opts->workspace);
+  char* ws_base = static_cast<char*>(ws_ptr);
   const DecodeWs lay = decode_ws_layout((size_t)B, (size_t)Hq, (size_t)d, (size_t)P);
   a.part_o = reinterpret_cast<float*>(ws_base);
   a.part_lse = reinterpret_cast<float*>(ws_base + lay.lse_off);
@@ -308,6 +322,18 @@ int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_ca
     a.counters = skip_stats->counters;
   }
   return launch_status(ssm::launch_decode_impl(a, (int)d, kv_cap, krows, vrows, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_decode(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+               const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+               const ssm_opts* opts) {
+  return decode_impl(q, k_cache, v_cache, kv_lens, tau, out, skip_stats, stream, opts, false);
+}
+
+int ssm_decode_noalloc(const ssm_tensor* q, const ssm_kv_cache* k_cache, const ssm_kv_cache* v_cache,
+                       const int32_t* kv_lens, float tau, ssm_tensor* out, ssm_skip_stats* skip_stats, void* stream,
+                       const ssm_opts* opts) {
+  return decode_impl(q, k_cache, v_cache, kv_lens, tau, out, skip_stats, stream, opts, true);
 }
 
 // qk8: q holds e4m3 codes with dequantisation factor q_scale and the caches must be e4m3 (ssm_prefill_paged_fp8qk)

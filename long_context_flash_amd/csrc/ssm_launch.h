@@ -71,6 +71,12 @@ struct DecodeArgs {
 // scored against e4m3 K pages, e4m3 V pages (chunked only)
 hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, int mode, hipStream_t stream);
 constexpr int kDecSortMax = 8192;  // batches up to this size are dispatched longest sequence first
+// size of the static device array that serves as ssm_decode_noalloc's workspace (one per GPU)
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+
+// the current device's address of that array (the first call on a device looks it up); hipErrorInvalidDevice when
+// `stream` belongs to another device
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
 
 hipError_t launch_decode_impl(const DecodeArgs& a, int d, int kv_cap, int64_t k_pool_rows, int64_t v_pool_rows,
                               hipStream_t stream);

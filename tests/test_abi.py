@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 7
+    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 8
     for code in range(5):
         assert ssm.ssm_strerror(code)
     assert "unknown" in ssm.ssm_strerror(99)
@@ -203,6 +203,22 @@ def call_decode(lib, q=None, kc=None, vc=None, lens=FAKE, tau=-6.9, o=None, opts
         opts = ssm.Opts(0.0, 0, 0, 16, 256 * 1024, 1 << 30)
     return lib.ssm_decode(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(vc), lens, tau, ctypes.byref(o), None,
                           None, ctypes.byref(opts) if opts else None)
+
+
+def test_decode_noalloc_rejects_before_any_device_call(lib):
+    """ssm_decode_noalloc validates like ssm_decode, then rejects a request whose workspace exceeds its 32 MiB static
+    scratch with SSM_EWORKSPACE (no HIP call, nothing launched: this runs without a GPU)."""
+    B, Hq, d, P = 64, 64, 128, 64
+    assert ssm.ssm_decode_workspace_bytes(B, Hq, d, P) > 32 << 20
+    q, o = desc([B, Hq, d]), desc([B, Hq, d])
+    kc, vc = cache([B, 8, 1024, d]), cache([B, 8, 1024, d])
+    opts = ssm.Opts(0.0, 0, 0, P, None, 0, 0)
+    call = lambda tau, op: lib.ssm_decode_noalloc(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(vc), FAKE, tau,
+                                                  ctypes.byref(o), None, None, ctypes.byref(op) if op else None)
+    assert call(-6.9, opts) == ssm.SSM_EWORKSPACE
+    assert "static scratch" in ssm.ssm_last_error()
+    assert call(1.0, opts) == ssm.SSM_EINVAL          # tau > 0: the same checks as ssm_decode come first
+    assert call(-6.9, ssm.Opts(0.0, 0, 0, 65, None, 0, 0)) == ssm.SSM_EUNSUPPORTED
 
 
 @pytest.mark.parametrize("case,code", [
