@@ -40,11 +40,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "long_context_flash_amd", "csrc")
-KERNEL_SOURCES = {"prefill": ["prefill.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"],
+KERNEL_SOURCES = {"prefill": ["prefill_pp.hip", "prefill.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"],
                   "decode": ["decode.hip", "ssm_device.h", "ssm_launch.h", "ssm_api.cpp"]}
 COPY_PROBE_BYTES = 1 << 30
 # the step's kernels as the profiler names them (d = 128, tile_q = 128, plain prefill, bf16 cache)
-PREFILL_KERNEL = "prefill_kernel<128, 128, false, 0>"
+PREFILL_KERNEL = "prefill_pp_kernel"
 DECODE_SPLIT_KERNEL = "decode_split_kernel<128, 2>"
 DECODE_COMBINE_KERNEL = "decode_combine_kernel<128>"
 

@@ -13,7 +13,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssm.so")
-SOURCES = ["prefill.hip", "decode.hip", "ssm_api.cpp"]
+SOURCES = ["prefill.hip", "prefill_pp.hip", "decode.hip", "ssm_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 vector ops (v_pk_*_f32).
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

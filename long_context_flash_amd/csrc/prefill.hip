@@ -572,6 +572,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked,
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hq * a.nqt);
   if (grid == 0) return hipSuccess;
   if (chunked ? mode == 1 : (mode == 2 || mode == 3)) return hipErrorInvalidValue;
+  if (!chunked && mode == 0 && d == 128 && tile_q == 128 && a.G % 2 == 0) return launch_prefill_pp(a, stream);
   const dim3 blk(tile_q * 2);
 #define SSM_PREFILL_LAUNCH(D, TQ)                                                                                \
   if (d == D && tile_q == TQ) {                                                                                  \
