@@ -47,6 +47,7 @@ COPY_PROBE_BYTES = 1 << 30
 PREFILL_KERNEL = "prefill_pp_kernel"
 DECODE_SPLIT_KERNEL = "decode_split_kernel<128, 2>"
 DECODE_COMBINE_KERNEL = "decode_combine_kernel<128>"
+DECODE_ORDER_KERNEL = "decode_order_kernel"
 
 
 def sources_sha(path_kind):
@@ -118,8 +119,9 @@ def summarize_traffic(fetch_dir, write_dir, command):
            "prefill": {"kernels": PREFILL_KERNEL,
                        "bytes_per_launch": launch_bytes(lambda n: PREFILL_KERNEL in n),
                        "source_sha256": sources_sha("prefill")},
-           "decode": {"kernels": "decode_split_kernel + decode_combine_kernel",
-                      "bytes_per_launch": launch_bytes(lambda n: DECODE_SPLIT_KERNEL in n or DECODE_COMBINE_KERNEL in n),
+           "decode": {"kernels": "decode_order_kernel + decode_split_kernel + decode_combine_kernel",
+                      "bytes_per_launch": launch_bytes(lambda n: DECODE_SPLIT_KERNEL in n or DECODE_COMBINE_KERNEL in n
+                                                       or DECODE_ORDER_KERNEL in n),
                       "source_sha256": sources_sha("decode")}}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
@@ -134,7 +136,7 @@ def summarize_traffic(fetch_dir, write_dir, command):
         fk = sum(fetch[n]) / len(fetch[n])
         wk = sum(write.get(n, [0])) / max(len(write.get(n, [0])), 1)
         lines.append(f"| `{n[:90]}` | {len(fetch[n])} | {fk:.0f} | {wk:.0f} | {(fk * f_fac + wk * w_fac) * 1024:.4g} |")
-    lines += ["", f"Per launch: prefill {rec['prefill']['bytes_per_launch']:.4g} B; decode (split + combine) "
+    lines += ["", f"Per launch: prefill {rec['prefill']['bytes_per_launch']:.4g} B; decode (order + split + combine) "
               f"{rec['decode']['bytes_per_launch']:.4g} B."]
     with open(os.path.join(ROOT, "profiles", "hbm_traffic__prefill_s128k__decode_b32_kv128k_paged.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -921,7 +923,7 @@ def main():
                                   "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                   "frac": round((kb + vk + small) / t / 1e9 / HBM_PEAK_GBPS, 4),
                                   "traffic": recorded_traffic("decode"),
-                                  "kernel": f"{DECODE_SPLIT_KERNEL} + {DECODE_COMBINE_KERNEL}",
+                                  "kernel": f"{DECODE_ORDER_KERNEL} + {DECODE_SPLIT_KERNEL} + {DECODE_COMBINE_KERNEL}",
                                   "per_launch_bytes": kb + vk + small}
         read_ceiling = recorded_read_ceiling()
         if read_ceiling:
@@ -942,16 +944,16 @@ def main():
         res["decode_fp8_kv"]["speedup_vs_bf16"] = round(res["decode_ms"] / res["decode_fp8_kv"]["ms"], 3)
         res["decode_tau_sweep"] = time_decode_tau_sweep(ssm, torch, np, dw, dq, kp, vp, pt, lens, dout, ws, args.steps,
                                                         dev)
+        read_ceiling = recorded_read_ceiling()
+        if read_ceiling:
+            for leg in ("decode_sink_seeded", "decode_fp8_kv"):
+                res[leg]["read_ceiling_frac"] = round(res[leg]["total_gbps"] / read_ceiling, 4)
         log("decode 32K legs")
         res["decode_32k"] = leg_decode_32k(ssm, torch, np, args.steps, dev, cpu_threads, cpu=not args.no_cpu_baseline)
     if run_prefill and not args.main_only:
         log("prefill 16K legs")
         res["prefill_16k"] = leg_prefill_16k(ssm, torch, np, args.steps, dev, cpu_threads,
                                              cpu=not args.no_cpu_baseline)
-        read_ceiling = recorded_read_ceiling()
-        if read_ceiling:
-            for leg in ("decode_sink_seeded", "decode_fp8_kv"):
-                res[leg]["read_ceiling_frac"] = round(res[leg]["total_gbps"] / read_ceiling, 4)
     res["config"] = cfg
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
