@@ -37,7 +37,7 @@ class _PrefillShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_double), ("tau", ctypes.c_double),
-                ("S_k", ctypes.c_int32)]
+                ("S_k", ctypes.c_int32), ("weights", ctypes.c_int32)]
 
 
 class _DecodeShape(ctypes.Structure):
@@ -91,9 +91,11 @@ def default_threads() -> int:
 
 
 def prefill(q, k, v, *, causal=True, tau=-math.log(1000.0), tile_q=128, tile_k=64, scale=0.0,
-            units=None, override=None, form="closed", threads=None, lib=None) -> dict:
+            units=None, override=None, form="closed", weights="exp", threads=None, lib=None) -> dict:
     """Skip Softmax prefill on q [B,S,Hq,d], k/v [B,S_k,Hkv,d] with S_k >= S (S_k > S: chunked prefill, the
     queries being the last S of the S_k positions; causal masking is then bottom-right aligned).
+    weights: "exp" (softmax) or "rowmax_pot" (a kept key's weight is 2^(rint(log2(e) l) - rint(log2(e) mu)),
+    mu the row maximum over the kept keys).
 
     Returns dict: out [n,tile_q,d], lse [n,tile_q], state/gamma [n,ceil(S_k/tile_k)], dropped [n,tile_q],
     for the listed units (unit = (b*Hq + h)*ceil(S/tile_q) + qt) or all units in that order."""
@@ -110,7 +112,10 @@ def prefill(q, k, v, *, causal=True, tau=-math.log(1000.0), tile_q=128, tile_k=6
         ov = np.ascontiguousarray(override, dtype=np.int8).reshape(n, nkt)
     res = {"out": np.empty((n, tile_q, d)), "lse": np.empty((n, tile_q)), "state": np.empty((n, nkt), np.uint8),
            "gamma": np.empty((n, nkt)), "dropped": np.empty((n, tile_q))}
-    shape = _PrefillShape(B, S, Hq, Hkv, d, tile_q, tile_k, int(bool(causal)), float(scale), float(tau), Sk)
+    if weights not in ("exp", "rowmax_pot"):
+        raise ValueError("weights must be 'exp' or 'rowmax_pot'")
+    shape = _PrefillShape(B, S, Hq, Hkv, d, tile_q, tile_k, int(bool(causal)), float(scale), float(tau), Sk,
+                          1 if weights == "rowmax_pot" else 0)
     rc = (lib or load()).oracle_prefill(ctypes.byref(shape), _p(q), _p(k), _p(v), _dtype_code(q, k, v),
                                         _p(units_arr), n, _p(ov), 1 if form == "scan" else 0,
                                         _p(res["out"]), _p(res["lse"]), _p(res["state"]), _p(res["gamma"]),

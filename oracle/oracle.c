@@ -59,6 +59,17 @@
  *      tau <= 0, a skipped tile never holds a new maximum, so the scan's
  *      running maximum equals step 5's prefix maximum and both forms produce
  *      the same mask.
+ *  Rowmax-PoT weights (prefill option; "Approximating Softmax in Pretrained
+ *  LLMs: Model Sensitivity and Kernel Acceleration", AI Summary and Abstract:
+ *  the exponential is replaced by powers of two, a coarse logarithmic weight
+ *  representation anchored at each row maximum).  READING: the base-2 log
+ *  weight log2(e) * l of a kept key is rounded to the nearest integer k (ties
+ *  to even) and its weight is 2^(k - K), K the rounded log weight of the row
+ *  maximum over the kept keys (whose weight is therefore exactly 1).  Step 8
+ *  then uses these weights in place of e^(l - mu); steps 1-7 (which tiles are
+ *  skipped) are unchanged.  In the scan form the reference is the rounded log
+ *  weight of the running maximum, so it moves by whole powers of two and both
+ *  forms compute the same weights.
  */
 #include "oracle.h"
 
@@ -88,6 +99,9 @@ static double widen(const void* base, int dt, int64_t i) {
   return (double)f;
 }
 
+/* Rowmax-PoT: the rounded base-2 log weight of a logit (see the header). */
+static double pot_exponent(double logit) { return nearbyint(logit * 1.4426950408889634074); }
+
 /* ------------------------------------------------------------ one unit */
 typedef struct {
   int nr, d, tile_k, ntiles, nkeys;
@@ -103,6 +117,7 @@ typedef struct {
   int seed_scans;           /* scans after the first start from the first tile's row maxima */
   double scale, tau;
   const int8_t* override;   /* [ntiles] or NULL */
+  int pot;                  /* 1: Rowmax-PoT weights in place of the exponentials */
 } unit_t;
 
 typedef struct {
@@ -196,8 +211,9 @@ static int unit_closed(const unit_t* u, unit_out* o) {
     if (m > -INFINITY)
       for (int j = 0; j < nk; ++j) {
         if (Lr[j] == -INFINITY) continue;
-        if (!skip[j / T]) z += exp(Lr[j] - m);
-        else dz += exp(Lr[j] - m);
+        const double w = u->pot ? ldexp(1.0, (int)(pot_exponent(Lr[j]) - pot_exponent(m))) : exp(Lr[j] - m);
+        if (!skip[j / T]) z += w;
+        else dz += w;
       }
     Z[r] = z;
     lost[r] = dz;
@@ -209,13 +225,14 @@ static int unit_closed(const unit_t* u, unit_out* o) {
     for (int r = 0; r < nr; ++r) {
       double l = L[(int64_t)r * nk + j];
       if (l == -INFINITY || !o->out) continue;
-      double w = exp(l - mu[r]) / Z[r];
+      double w = (u->pot ? ldexp(1.0, (int)(pot_exponent(l) - pot_exponent(mu[r]))) : exp(l - mu[r])) / Z[r];
       for (int c = 0; c < d; ++c) o->out[(int64_t)r * d + c] += w * row[c];
     }
   }
   for (int r = 0; r < nr; ++r) {
     int empty = mu[r] == -INFINITY;
-    if (o->lse) o->lse[r] = empty ? -INFINITY : mu[r] + log(Z[r]);
+    /* log of the sum of the kept weights before normalisation (PoT: of the 2^k) */
+    if (o->lse) o->lse[r] = empty ? -INFINITY : (u->pot ? pot_exponent(mu[r]) * 0.6931471805599453094 : mu[r]) + log(Z[r]);
     if (o->dropped) o->dropped[r] = empty ? 0.0 : lost[r] / Z[r];
   }
 done:
@@ -236,8 +253,9 @@ static int unit_scan(const unit_t* u, unit_out* o) {
   double* Mt = (double*)malloc(sizeof(double) * (size_t)nr);
   double* row = (double*)malloc(sizeof(double) * (size_t)d);
   double* seed = (double*)malloc(sizeof(double) * (size_t)nr);
+  double* kref = (double*)malloc(sizeof(double) * (size_t)nr);  /* PoT: rounded log weight of the running max */
   int rc = 0;
-  if (!m || !l || !a || !os || !ls || !lt || !Mt || !row || !seed) { rc = 2; goto done; }
+  if (!m || !l || !a || !os || !ls || !lt || !Mt || !row || !seed || !kref) { rc = 2; goto done; }
   /* sink seeding: the row maxima of the unit's first tile, from its own logits */
   for (int r = 0; r < nr; ++r) seed[r] = -INFINITY;
   if (u->seed_scans)
@@ -250,7 +268,7 @@ static int unit_scan(const unit_t* u, unit_out* o) {
       }
     }
   for (int s = 0; s < ns; ++s) {
-    for (int r = 0; r < nr; ++r) { m[r] = -INFINITY; l[r] = 0; }
+    for (int r = 0; r < nr; ++r) { m[r] = -INFINITY; l[r] = 0; kref[r] = -INFINITY; }
     memset(a, 0, sizeof(double) * (size_t)nr * d);
     for (int t = u->scan_first[s]; t < u->scan_first[s + 1]; ++t) {
       const int j0 = t * T, j1 = (t + 1) * T < nk ? (t + 1) * T : nk;
@@ -284,7 +302,14 @@ static int unit_scan(const unit_t* u, unit_out* o) {
       for (int r = 0; r < nr; ++r) {
         if (Mt[r] == -INFINITY) continue;
         double mn = Mt[r] > m[r] ? Mt[r] : m[r];
-        double c = exp(m[r] - mn);
+        double c;
+        if (u->pot) {  /* the reference moves by whole powers of two */
+          const double kn = pot_exponent(mn);
+          c = kref[r] == -INFINITY ? 0.0 : ldexp(1.0, (int)(kref[r] - kn));
+          kref[r] = kn;
+        } else {
+          c = exp(m[r] - mn);
+        }
         l[r] *= c;
         for (int e = 0; e < d; ++e) a[(int64_t)r * d + e] *= c;
         m[r] = mn;
@@ -294,7 +319,7 @@ static int unit_scan(const unit_t* u, unit_out* o) {
         for (int r = 0; r < nr; ++r) {
           double x = lt[(int64_t)r * T + (j - j0)];
           if (x == -INFINITY) continue;
-          double p = exp(x - m[r]);
+          double p = u->pot ? ldexp(1.0, (int)(pot_exponent(x) - kref[r])) : exp(x - m[r]);
           l[r] += p;
           for (int e = 0; e < d; ++e) a[(int64_t)r * d + e] += p * row[e];
         }
@@ -304,7 +329,7 @@ static int unit_scan(const unit_t* u, unit_out* o) {
       double* osr = os + ((int64_t)s * nr + r) * d;
       if (l[r] > 0) {
         for (int e = 0; e < d; ++e) osr[e] = a[(int64_t)r * d + e] / l[r];
-        ls[(int64_t)s * nr + r] = m[r] + log(l[r]);
+        ls[(int64_t)s * nr + r] = (u->pot ? kref[r] * 0.6931471805599453094 : m[r]) + log(l[r]);
       } else {
         for (int e = 0; e < d; ++e) osr[e] = 0;
         ls[(int64_t)s * nr + r] = -INFINITY;
@@ -331,7 +356,7 @@ static int unit_scan(const unit_t* u, unit_out* o) {
     if (o->dropped) o->dropped[r] = NAN;
   }
 done:
-  free(m); free(l); free(a); free(os); free(ls); free(lt); free(Mt); free(row); free(seed);
+  free(m); free(l); free(a); free(os); free(ls); free(lt); free(Mt); free(row); free(seed); free(kref);
   return rc;
 }
 
@@ -424,6 +449,7 @@ static int prefill_one(void* vctx, int64_t n) {
   u.nscans = 1; u.scan_first = scan_first;
   u.scale = P->scale; u.tau = s->tau;
   u.override = P->override ? P->override + n * P->nkt : NULL;
+  u.pot = s->weights == ORACLE_WEIGHTS_ROWMAX_POT;
   unit_out o;
   o.out = P->out ? P->out + n * Tq * d : NULL;
   o.lse = P->lse ? P->lse + n * Tq : NULL;
@@ -448,7 +474,7 @@ int oracle_prefill(const oracle_prefill_shape* s, const void* q, const void* k, 
                    double* out, double* lse, uint8_t* state, double* gamma, double* dropped, int threads) {
   if (!s || !q || !k || !v || s->B < 1 || s->S < 1 || s->Hq < 1 || s->Hkv < 1 || s->d < 1 ||
       s->Hq % s->Hkv || s->tile_q < 1 || s->tile_k < 1 || !valid_tau(s->tau) || in_dtype < 0 || in_dtype > 2 ||
-      (s->S_k != 0 && s->S_k < s->S))
+      (s->S_k != 0 && s->S_k < s->S) || (s->weights != ORACLE_WEIGHTS_EXP && s->weights != ORACLE_WEIGHTS_ROWMAX_POT))
     return 1;
   prefill_job P;
   memset(&P, 0, sizeof P);

@@ -24,6 +24,7 @@ extern "C" {
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2, ORACLE_FP8E4M3 = 3 };
 enum { ORACLE_CLOSED_FORM = 0, ORACLE_SCAN_FORM = 1 };
 enum { ORACLE_TILE_UNVISITED = 0, ORACLE_TILE_EXECUTED = 1, ORACLE_TILE_SKIPPED = 2 };
+enum { ORACLE_WEIGHTS_EXP = 0, ORACLE_WEIGHTS_ROWMAX_POT = 1 };
 
 typedef struct {
   int32_t B, S, Hq, Hkv, d;   /* q [B,S,Hq,d]; k, v [B,S,Hkv,d]; contiguous */
@@ -34,6 +35,9 @@ typedef struct {
   int32_t S_k;                /* chunked prefill: keys per sequence (k, v are [B,S_k,Hkv,d]); the S
                                  queries are the last S of S_k positions, so query i sees keys
                                  j <= S_k - S + i (bottom-right causal).  0 means S_k = S. */
+  int32_t weights;            /* ORACLE_WEIGHTS_EXP, or ORACLE_WEIGHTS_ROWMAX_POT: a kept key's weight is
+                                 2^(rint(log2(e) l) - rint(log2(e) mu)), mu the row maximum over the kept
+                                 keys; lse is then the log of the sum of the 2^rint(log2(e) l) */
 } oracle_prefill_shape;
 
 /* Prefill units are u = (b*Hq + h)*ceil(S/tile_q) + qt.  units == NULL means all

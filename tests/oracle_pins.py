@@ -618,10 +618,97 @@ def pin_input_widening(lib=None):
         assert (a["state"] == oracle.SKIPPED).any(), "the decode case must skip some tiles"
 
 
+def _integer_logit_inputs(seed, S=200, Hq=4, Hkv=2, d=16, delta=0.0):
+    """Integer-valued q, k (entries in -2..2) so that with the logit scale ln 2 the base-2 log weights
+    log2(e) * ln2 * q.k are the integers q.k; with delta > 0 an extra channel (q: 1, k: uniform in
+    (-delta, delta)) moves each of them off its integer by less than delta."""
+    r = rng(seed)
+    q = r.integers(-2, 3, (1, S, Hq, d)).astype(np.float64)
+    k = r.integers(-2, 3, (1, S, Hkv, d)).astype(np.float64)
+    v = r.standard_normal((1, S, Hkv, d))
+    if delta:
+        q = np.concatenate([q, np.ones((1, S, Hq, 1))], -1)
+        k = np.concatenate([k, r.uniform(-delta, delta, (1, S, Hkv, 1))], -1)
+        v = np.concatenate([v, np.zeros((1, S, Hkv, 1))], -1)
+    return q, k, v
+
+
+def pin_rowmax_pot(lib=None):
+    """Rowmax-PoT weights ("Approximating Softmax in Pretrained LLMs", Abstract: powers of two anchored at the
+    row maximum; the oracle's reading: 2^(rint(log2(e) l) - rint(log2(e) mu))):
+      * logits whose base-2 log weights are integers (scale ln 2, integer q.k) have exact power-of-two weights,
+        so the PoT output equals SDPA float64 at that scale (causal and not, tau = -inf), and equals the exact
+        softmax of the oracle at a finite tau with identical masks;
+      * moving every such log weight by less than 0.45 (one extra channel) leaves the PoT weights unchanged:
+        the PoT output equals SDPA on the unmoved integer logits while the exact softmax moves;
+      * both forms agree."""
+    ln2 = math.log(2.0)
+    for causal in (True, False):
+        q, k, v = _integer_logit_inputs(31)
+        got = oracle.prefill(q, k, v, causal=causal, tau=-math.inf, tile_q=64, scale=ln2, weights="rowmax_pot",
+                             lib=lib)
+        ref = sdpa_prefill(q, k, v, causal, scale=ln2)
+        err = np.abs(unit_rows(got["out"], 1, 200, 4, 64) - ref).max()
+        assert err < 1e-12, f"integer log weights: PoT differs from softmax by {err}"
+        a = oracle.prefill(q, k, v, causal=causal, tau=-2.0, tile_q=64, scale=ln2, weights="rowmax_pot", lib=lib)
+        b = oracle.prefill(q, k, v, causal=causal, tau=-2.0, tile_q=64, scale=ln2, lib=lib)
+        assert np.array_equal(a["state"], b["state"]) and (a["state"] == oracle.SKIPPED).any()
+        assert np.abs(a["out"] - b["out"]).max() < 1e-12
+        qp, kp, vp = _integer_logit_inputs(31, delta=0.45)
+        got = oracle.prefill(qp, kp, vp, causal=causal, tau=-math.inf, tile_q=64, scale=ln2, weights="rowmax_pot",
+                             lib=lib)
+        err = np.abs(unit_rows(got["out"], 1, 200, 4, 64)[..., :16] - ref).max()
+        assert err < 1e-12, f"log weights moved by < 0.45: PoT output moved by {err}"
+        exact = oracle.prefill(qp, kp, vp, causal=causal, tau=-math.inf, tile_q=64, scale=ln2, lib=lib)
+        assert np.abs(unit_rows(exact["out"], 1, 200, 4, 64)[..., :16] - ref).max() > 1e-3
+        for form_in in ((q, k, v, -2.0), (qp, kp, vp, -math.inf)):
+            x, y, z, tau = form_in
+            c = oracle.prefill(x, y, z, causal=causal, tau=tau, tile_q=64, scale=ln2, weights="rowmax_pot", lib=lib)
+            sc = oracle.prefill(x, y, z, causal=causal, tau=tau, tile_q=64, scale=ln2, weights="rowmax_pot",
+                                form="scan", lib=lib)
+            assert np.array_equal(c["state"], sc["state"]) and np.abs(c["out"] - sc["out"]).max() < 1e-12
+
+
+def pin_worked_example_rowmax_pot(lib=None):
+    """W8 (hand-derived): logit scale ln 2, one query (1, 0) per row, three keys whose base-2 log weights are 0,
+    -1.3, -2.6 (keys (0, 0), (-1.3, 0), (-2.6, 0)), values (1, 0), (0, 1), (4, 4), non-causal: the PoT weights
+    are 1, 2^-1, 2^-3 (nearest integers 0, -1, -3), so o = ((1, 0) + (0, 1/2) + (1/2, 1/2)) / (13/8)
+    = (12/13, 8/13).  W9: 64 keys at log weight 0 with values (j, 1), then 64 keys at -12.4 with values
+    (1000, -1): at tau = -ln 1000 the second tile is skipped (gap -12.4 ln2 = -8.6 < tau) and o = (31.5, 1); at
+    tau = -inf it is kept with weights 2^-12 each: o = (sum_j j + 64 * 1000 / 4096, 64 - 64 / 4096)
+    / (64 + 64 / 4096)."""
+    ln2 = math.log(2.0)
+    q = np.zeros((1, 3, 1, 2)); q[..., 0] = 1.0
+    k = np.array([[0.0, 0.0], [-1.3, 0.0], [-2.6, 0.0]]).reshape(1, 3, 1, 2)
+    v = np.array([[1.0, 0.0], [0.0, 1.0], [4.0, 4.0]]).reshape(1, 3, 1, 2)
+    for form in ("closed", "scan"):
+        r = oracle.prefill(q, k, v, causal=False, tau=-math.inf, tile_q=64, scale=ln2, weights="rowmax_pot",
+                           form=form, lib=lib)
+        got = unit_rows(r["out"], 1, 3, 1, 64)[0, :, 0]
+        assert np.abs(got - np.array([12 / 13, 8 / 13])).max() < 1e-14, f"W8 {form}: {got}"
+    S = 128
+    q = np.zeros((1, S, 1, 2)); q[..., 0] = 1.0
+    k = np.zeros((1, S, 1, 2)); k[0, 64:, 0, 0] = -12.4
+    v = np.zeros((1, S, 1, 2))
+    v[0, :64, 0, 0] = np.arange(64); v[0, :64, 0, 1] = 1.0
+    v[0, 64:, 0, 0] = 1000.0; v[0, 64:, 0, 1] = -1.0
+    w = 2.0 ** -12
+    for form in ("closed", "scan"):
+        r = oracle.prefill(q, k, v, causal=False, tau=-LN1000, tile_q=64, scale=ln2, weights="rowmax_pot",
+                           form=form, lib=lib)
+        got = unit_rows(r["out"], 1, S, 1, 64)[0, :, 0]
+        assert np.abs(got - np.array([31.5, 1.0])).max() < 1e-12 and (r["state"][:, 1] == oracle.SKIPPED).all()
+        r = oracle.prefill(q, k, v, causal=False, tau=-math.inf, tile_q=64, scale=ln2, weights="rowmax_pot",
+                           form=form, lib=lib)
+        got = unit_rows(r["out"], 1, S, 1, 64)[0, :, 0]
+        want = np.array([2016 + 64 * 1000 * w, 64 - 64 * w]) / (64 + 64 * w)
+        assert np.abs(got - want).max() < 1e-12, f"W9 {form}: {got[0]} vs {want}"
+
+
 ALL_PINS = [pin_dense_prefill, pin_dense_decode, pin_longdouble_bruteforce, pin_forms_agree, pin_mask_invariants,
             pin_uniform_scores, pin_dropped_mass, pin_split_invariance, pin_output_given_mask, pin_worked_examples,
             pin_sink_seed, pin_worked_example_sink_seed, pin_fp8_kv, pin_chunked_prefill, pin_worked_example_chunk,
-            pin_input_widening]
+            pin_input_widening, pin_rowmax_pot, pin_worked_example_rowmax_pot]
 
 
 def run_all(lib=None):

@@ -56,6 +56,14 @@ MUTANTS = [
      "if (dt == ORACLE_F32) { uint32_t u; memcpy(&u, (const float*)base + i, 4); u &= 0xffff0000u; float f; "
      "memcpy(&f, &u, 4); return (double)f; }", 1),
     ("dtype_codes_swapped", "if (dt == ORACLE_F32) return", "if (dt == ORACLE_BF16) return", 1),
+    ("pot_floor_not_nearest", "return nearbyint(logit * 1.4426950408889634074);",
+     "return floor(logit * 1.4426950408889634074);", 1),
+    ("pot_natural_log_units", "return nearbyint(logit * 1.4426950408889634074);", "return nearbyint(logit);", 1),
+    ("pot_difference_rounded", "ldexp(1.0, (int)(pot_exponent(l) - pot_exponent(mu[r])))",
+     "ldexp(1.0, (int)pot_exponent(l - mu[r]))", 1),
+    ("pot_ignored_in_scan_form", "double p = u->pot ? ldexp(1.0, (int)(pot_exponent(x) - kref[r])) : exp(x - m[r]);",
+     "double p = exp(x - m[r]);", 1),
+    ("pot_flag_dropped", "u.pot = s->weights == ORACLE_WEIGHTS_ROWMAX_POT;", "u.pot = 0;", 1),
     ("split_size_floor", "const int tps = (nt + P - 1) / P;", "const int tps = nt / P > 0 ? nt / P : 1;", 1),
 ]
 
