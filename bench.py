@@ -565,6 +565,7 @@ def leg_prefill_16k(ssm, torch, np, steps, dev, threads, cpu=True, n_units=64):
 
 
 PARITY_MAX_ABS, PARITY_REL_L2, PARITY_BAND = 1e-2, 3e-3, 1e-3
+PARITY_BF16_OUT, PARITY_ACC_ABS = 2.0 ** -8, 2e-3  # where |o| > 2.05: bf16 output rounding + accumulated error
 
 
 def host_info(threads):
@@ -608,6 +609,7 @@ def parity_fields(np, got, ref_out, st_gpu, st_ref, gamma_ref, tau):
     den = float(np.linalg.norm(ref_out.ravel()))
     max_abs = float(np.abs(diff).max()) if diff.size else 0.0
     rel = float(np.linalg.norm(diff.ravel()) / den) if den > 0 else 0.0
+    within = bool((np.abs(diff) <= np.maximum(PARITY_MAX_ABS, PARITY_BF16_OUT * np.abs(ref_out) + PARITY_ACC_ABS)).all())
     vis = st_ref > 0
     if math.isinf(tau):
         amb = np.zeros(st_ref.shape, bool)
@@ -620,7 +622,7 @@ def parity_fields(np, got, ref_out, st_gpu, st_ref, gamma_ref, tau):
             "mask_tiles_off_band": int(off.sum()), "mask_agree_off_band": agree,
             "ambiguous_tiles": int(amb.sum()), "ambiguous_flips": int((amb & (st_gpu != st_ref)).sum()),
             "unvisited_agree": bool(((st_gpu == 0) == (st_ref == 0)).all()),
-            "pass": bool(max_abs <= PARITY_MAX_ABS and rel <= PARITY_REL_L2 and agree == int(off.sum()))}
+            "pass": bool(within and rel <= PARITY_REL_L2 and agree == int(off.sum()))}
 
 
 def flip_override(np, st_gpu, st_ref, gamma_ref, tau):
@@ -977,7 +979,8 @@ def main():
             base["host"] = host
             res["cpu_baseline" if not run_prefill else "cpu_baseline_decode"] = base
             res.setdefault("parity", {})["decode"] = par
-        res["parity"]["bar"] = {"max_abs": PARITY_MAX_ABS, "rel_l2": PARITY_REL_L2, "mask_band": PARITY_BAND,
+        res["parity"]["bar"] = {"max_abs": PARITY_MAX_ABS, "max_abs_large_o": "2^-8 |o| + 2e-3 where larger",
+                                "rel_l2": PARITY_REL_L2, "mask_band": PARITY_BAND,
                                 "what": "the timed launches' outputs and skip decisions against the fp64 oracle "
                                         "on the cpu_baseline samples"}
     print(json.dumps(res, allow_nan=False), flush=True)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 8
+#define SSM_ABI_VERSION 9
 
 enum {
   SSM_OK = 0,
@@ -108,7 +108,21 @@ typedef struct {
   void* workspace;         /* decode: device buffer of >= ssm_decode_workspace_bytes() bytes */
   size_t workspace_bytes;
   int32_t decode_flags;    /* decode: 0 or SSM_DECODE_SINK_SEED; other bits are SSM_EINVAL */
+  int32_t weights;         /* SSM_WEIGHTS_EXP (0) or SSM_WEIGHTS_ROWMAX_POT: ssm_prefill and ssm_prefill_fp8qk;
+                              the other entry points return SSM_EUNSUPPORTED for anything but 0; other
+                              values are SSM_EINVAL */
 } ssm_opts;
+
+/* Softmax weights of the prefill ("Approximating Softmax in Pretrained LLMs: Model Sensitivity and Kernel
+ * Acceleration", AI Summary and Abstract: Rowmax-PoT replaces the exponential by powers of two, a coarse
+ * logarithmic weight anchored at each row maximum).  With SSM_WEIGHTS_ROWMAX_POT a kept key's weight is
+ * 2^(rint(log2(e) * l) - rint(log2(e) * mu)) for its logit l and the row maximum mu over the kept keys (ties
+ * to even), so the weights are exact powers of two and no exponential is evaluated; the output is
+ * sum_j w_j v_j / sum_j w_j over the kept keys.  Which tiles are skipped does not change.  The rounding is
+ * decided on the fp32 logits, so a logit within a few fp32 ulps of a half-integer base-2 log weight may round
+ * either way. */
+#define SSM_WEIGHTS_EXP 0
+#define SSM_WEIGHTS_ROWMAX_POT 1
 
 /* Sink-seeded split-K decode.  By default every split-K chunk is an independent
  * scan whose running maximum starts at -inf, so the first tile of every chunk

@@ -58,11 +58,12 @@ class SkipStatsC(ctypes.Structure):
 class Opts(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_float), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("decode_flags", ctypes.c_int32)]
+                ("decode_flags", ctypes.c_int32), ("weights", ctypes.c_int32)]
 
 
-ABI_VERSION = 8               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 9               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
 DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
+WEIGHTS = {"exp": 0, "rowmax_pot": 1}  # SSM_WEIGHTS_EXP, SSM_WEIGHTS_ROWMAX_POT
 
 
 _lib = None
@@ -187,6 +188,12 @@ class SkipStats:
                          counters=torch.zeros(4, dtype=torch.int64, device=device))
 
 
+def _weights_code(weights: str) -> int:
+    if weights not in WEIGHTS:
+        raise ValueError(f"weights must be one of {sorted(WEIGHTS)}")
+    return WEIGHTS[weights]
+
+
 def prefill_stats_shape(B, S, Hq, tile_q=128, tile_k=64):
     """(units, tiles) of the prefill statistics: unit = (b*Hq + h)*ceil(S/tile_q) + q_tile."""
     return B * Hq * (-(-S // tile_q)), -(-S // tile_k)
@@ -195,13 +202,14 @@ def prefill_stats_shape(B, S, Hq, tile_q=128, tile_k=64):
 def ssm_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
                 tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
                 skip_stats: Optional[SkipStats] = None, stream=None, tile_q: int = 128, tile_k: int = 64,
-                scale: float = 0.0) -> torch.Tensor:
-    """Skip Softmax prefill: q [B,S,Hq,d], k/v [B,S,Hkv,d] bf16 on the GPU -> out [B,S,Hq,d] bf16."""
+                scale: float = 0.0, weights: str = "exp") -> torch.Tensor:
+    """Skip Softmax prefill: q [B,S,Hq,d], k/v [B,S,Hkv,d] bf16 on the GPU -> out [B,S,Hq,d] bf16.
+    weights: "exp" (softmax) or "rowmax_pot" (power-of-two weights anchored at the row maximum)."""
     _on_device(q.device, q=q, k=k, v=v, out=out, **(skip_stats.tensors() if skip_stats else {}))
     if out is None:
         out = torch.empty_like(q)
     qd, kd, vd, od = describe(q), describe(k), describe(v), describe(out)
-    opts = Opts(float(scale), int(tile_q), int(tile_k), 0, None, 0)
+    opts = Opts(float(scale), int(tile_q), int(tile_k), 0, None, 0, 0, _weights_code(weights))
     st = skip_stats.c() if skip_stats is not None else None
     rc = lib().ssm_prefill(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), int(q.shape[1]) if q.dim() == 4 else 0,
                            int(bool(causal)), float(tau), ctypes.byref(od), ctypes.byref(st) if st else None,
@@ -213,14 +221,14 @@ def ssm_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
 def ssm_prefill_fp8qk(q: torch.Tensor, q_scale: float, k: torch.Tensor, k_scale: float, v: torch.Tensor,
                       causal: bool = True, tau: float = -math.log(1000.0), out: Optional[torch.Tensor] = None,
                       skip_stats: Optional[SkipStats] = None, stream=None, tile_q: int = 128, tile_k: int = 64,
-                      scale: float = 0.0) -> torch.Tensor:
+                      scale: float = 0.0, weights: str = "exp") -> torch.Tensor:
     """Skip Softmax prefill with 8-bit scores: q [B,S,Hq,d] and k [B,S,Hkv,d] torch.float8_e4m3fn codes (query =
     q_scale * code, key = k_scale * code), v [B,S,Hkv,d] bf16 on the GPU -> out [B,S,Hq,d] bf16."""
     _on_device(q.device, q=q, k=k, v=v, out=out, **(skip_stats.tensors() if skip_stats else {}))
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     qd, kd, vd, od = describe(q), describe(k), describe(v), describe(out)
-    opts = Opts(float(scale), int(tile_q), int(tile_k), 0, None, 0)
+    opts = Opts(float(scale), int(tile_q), int(tile_k), 0, None, 0, 0, _weights_code(weights))
     st = skip_stats.c() if skip_stats is not None else None
     rc = lib().ssm_prefill_fp8qk(ctypes.byref(qd), float(q_scale), ctypes.byref(kd), float(k_scale), ctypes.byref(vd),
                                  int(q.shape[1]) if q.dim() == 4 else 0, int(bool(causal)), float(tau),

@@ -112,7 +112,9 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // ragged rows of q/o, K/V read through a page table (see PrefillArgs).  MODE 0: bf16; 1 (QK8): q and k hold
 // e4m3 codes, QK^T on the fp8 MFMA; 2 (KV8, chunked only): the K/V pages hold e4m3 codes; 3 (chunked only):
 // both, i.e. e4m3 queries scored on the fp8 MFMA against e4m3 key pages, V pages converted as in 2.
-template <int D, int TQ, bool CHUNKED, int MODE>
+// POT: Rowmax-PoT weights 2^(rint(c2*S) - kref) in place of the exponentials, kref an integer reference moved
+// like m_ref (the output and row sums are invariant to its choice, and the rescale is an exact power of two).
+template <int D, int TQ, bool CHUNKED, int MODE, bool POT>
 __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   constexpr bool QK8 = MODE == 1 || MODE == 3, KV8 = MODE == 2 || MODE == 3;
   static_assert(!(CHUNKED && QK8 && !KV8), "8-bit scores over bf16 pages are not implemented");
@@ -372,9 +374,9 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   // exponential pair n/2 (n even, P^T operand order) of the scores s
   auto exp_pair = [&](const f32x16 (&s)[2], uint32_t (&pk)[4][4], int n, float eo) {
     const int st = n >> 3, e = n & 7;  // 16-key step, position inside it
-    const float p0 = exp2_fast(fmaf(s[st >> 1][8 * (st & 1) + e], c2, -eo));
-    const float p1 = exp2_fast(fmaf(s[st >> 1][8 * (st & 1) + e + 1], c2, -eo));
-    pk[st][e >> 1] = pack_bf16x2(p0, p1);
+    const float s0 = s[st >> 1][8 * (st & 1) + e], s1 = s[st >> 1][8 * (st & 1) + e + 1];
+    if constexpr (POT) pk[st][e >> 1] = pot_pack_bf16x2(s0, s1, c2, eo);
+    else pk[st][e >> 1] = pack_bf16x2(exp2_fast(fmaf(s0, c2, -eo)), exp2_fast(fmaf(s1, c2, -eo)));
     l_part = dot2_bf16_sum(pk[st][e >> 1], l_part);
   };
   // keep the exponentials where they are issued (next to the MFMAs they overlap) instead of letting
@@ -494,12 +496,23 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
         ++n_exec;
         // advance the true max; move the reference max only when it trails by > 8
         m_true = fmaxf(m_true, mx);
-        const bool move = (m_true - m_ref) * c2 > kRefSlack;  // also true while m_ref = -inf and m_true finite
-        alpha = move ? exp2_fast((m_ref - m_true) * c2) : 1.f;  // 0 when m_ref = -inf
-        resc = wave_ballot(move) != 0;
-        l_part *= alpha;
-        m_ref = move ? m_true : m_ref;
-        moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+        if constexpr (POT) {
+          // m_ref: the integer reference in base-2 log-weight units
+          const float kn = rintf(m_true * c2);     // -inf while the row has no valid key
+          const bool move = kn - m_ref > kRefSlack;  // also true while m_ref = -inf and kn finite
+          alpha = move ? (m_ref == neg_inf() ? 0.f : ldexpf(1.f, (int)(m_ref - kn))) : 1.f;  // exact
+          resc = wave_ballot(move) != 0;
+          l_part *= alpha;
+          m_ref = move ? kn : m_ref;
+          moff = m_ref == neg_inf() ? 0.f : m_ref;
+        } else {
+          const bool move = (m_true - m_ref) * c2 > kRefSlack;  // also true while m_ref = -inf and m_true finite
+          alpha = move ? exp2_fast((m_ref - m_true) * c2) : 1.f;  // 0 when m_ref = -inf
+          resc = wave_ballot(move) != 0;
+          l_part *= alpha;
+          m_ref = move ? m_true : m_ref;
+          moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+        }
       }
     } else {
       // past the last tile: only the pending P.V; its V tile was loaded in the previous iteration
@@ -572,16 +585,19 @@ hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked,
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hq * a.nqt);
   if (grid == 0) return hipSuccess;
   if (chunked ? mode == 1 : (mode == 2 || mode == 3)) return hipErrorInvalidValue;
+  if (chunked && a.pot) return hipErrorInvalidValue;
   if (!chunked && mode == 0 && d == 128 && tile_q == 128 && a.G % 2 == 0) return launch_prefill_pp(a, stream);
   const dim3 blk(tile_q * 2);
-#define SSM_PREFILL_LAUNCH(D, TQ)                                                                                \
-  if (d == D && tile_q == TQ) {                                                                                  \
-    if (chunked && mode == 2) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 2>), dim3(grid), blk, 0, stream, a); \
-    else if (chunked && mode == 3) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 3>), dim3(grid), blk, 0, stream, a); \
-    else if (chunked) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 0>), dim3(grid), blk, 0, stream, a);       \
-    else if (mode == 1) hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 1>), dim3(grid), blk, 0, stream, a);    \
-    else hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 0>), dim3(grid), blk, 0, stream, a);                   \
-    return hipGetLastError();                                                                                    \
+#define SSM_PREFILL_LAUNCH(D, TQ)                                                                                   \
+  if (d == D && tile_q == TQ) {                                                                                     \
+    if (chunked && mode == 2) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 2, false>), dim3(grid), blk, 0, stream, a); \
+    else if (chunked && mode == 3) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 3, false>), dim3(grid), blk, 0, stream, a); \
+    else if (chunked) hipLaunchKernelGGL((prefill_kernel<D, TQ, true, 0, false>), dim3(grid), blk, 0, stream, a);  \
+    else if (mode == 1 && a.pot) hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 1, true>), dim3(grid), blk, 0, stream, a); \
+    else if (mode == 1) hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 1, false>), dim3(grid), blk, 0, stream, a); \
+    else if (a.pot) hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 0, true>), dim3(grid), blk, 0, stream, a);    \
+    else hipLaunchKernelGGL((prefill_kernel<D, TQ, false, 0, false>), dim3(grid), blk, 0, stream, a);              \
+    return hipGetLastError();                                                                                       \
   }
   SSM_PREFILL_LAUNCH(128, 128)
   SSM_PREFILL_LAUNCH(128, 64)

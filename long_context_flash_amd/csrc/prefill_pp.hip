@@ -93,6 +93,9 @@ __device__ __forceinline__ void pp_map_unit(int bid, const PrefillArgs& a, int& 
 
 }  // namespace
 
+// POT: Rowmax-PoT weights 2^(rint(c2*S) - kref) in place of the exponentials (kref an integer reference that
+// trails the rounded row maximum by at most kRefSlackPP; the output and row sums are invariant to its choice).
+template <bool POT>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t k0[kTKpp * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t k1[kTKpp * kD];
@@ -202,7 +205,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) acc[cb] = f32x16{};
   float m_run = neg_inf();  // max of the row's scores over the tiles voted on so far (the skip rule's m_{i-1})
-  float m_ref = neg_inf();  // reference max of the exponentials (trails the true max by at most 8/c2)
+  float m_ref = neg_inf();  // reference max of the exponentials (trails the true max by at most 8/c2); POT: the
+                            // integer reference in base-2 log-weight units (trails rint(c2*max) by at most 8)
   float l_part = 0.f;       // this lane's half of the softmax denominator (summed in prefill_kernel's order, so the
                             // two kernels give the same bits)
   int n_exec = 0;
@@ -309,19 +313,29 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         ++n_exec;
         // m_run includes tile tp (updated at its vote) and no later tile; move the reference max only when it
         // trails by more than the slack
-        const bool move = (m_run - m_ref) * c2 > kRefSlackPP;  // also true while m_ref = -inf and m_run finite
-        const float alpha = move ? exp2_fast((m_ref - m_run) * c2) : 1.f;  // 0 when m_ref = -inf
-        pv_resc = wave_ballot(move) != 0;
+        float alpha, moff;
+        if constexpr (POT) {
+          const float kn = rintf(m_run * c2);        // -inf while the row has no valid key
+          const bool move = kn - m_ref > kRefSlackPP;  // also true while m_ref = -inf and kn finite
+          alpha = move ? (m_ref == neg_inf() ? 0.f : ldexpf(1.f, (int)(m_ref - kn))) : 1.f;  // exact
+          pv_resc = wave_ballot(move) != 0;
+          m_ref = move ? kn : m_ref;
+          moff = m_ref == neg_inf() ? 0.f : m_ref;
+        } else {
+          const bool move = (m_run - m_ref) * c2 > kRefSlackPP;  // also true while m_ref = -inf and m_run finite
+          alpha = move ? exp2_fast((m_ref - m_run) * c2) : 1.f;  // 0 when m_ref = -inf
+          pv_resc = wave_ballot(move) != 0;
+          m_ref = move ? m_run : m_ref;
+          moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+        }
         pv_alpha = alpha;
         l_part *= alpha;
-        m_ref = move ? m_run : m_ref;
-        const float moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
 #pragma unroll
         for (int n = 0; n < 32; n += 2) {
           const int stp = n >> 3, e = n & 7;  // 16-key step, position inside it (P^T operand order)
-          const float p0 = exp2_fast(fmaf(sprev[stp >> 1][8 * (stp & 1) + e], c2, -moff));
-          const float p1 = exp2_fast(fmaf(sprev[stp >> 1][8 * (stp & 1) + e + 1], c2, -moff));
-          pk[stp][e >> 1] = pack_bf16x2(p0, p1);
+          const float s0 = sprev[stp >> 1][8 * (stp & 1) + e], s1 = sprev[stp >> 1][8 * (stp & 1) + e + 1];
+          if constexpr (POT) pk[stp][e >> 1] = pot_pack_bf16x2(s0, s1, c2, moff);
+          else pk[stp][e >> 1] = pack_bf16x2(exp2_fast(fmaf(s0, c2, -moff)), exp2_fast(fmaf(s1, c2, -moff)));
           l_part = dot2_bf16_sum(pk[stp][e >> 1], l_part);
         }
         pv_pending = true;
@@ -444,7 +458,8 @@ hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * (a.Hq / 2) * a.nqt);
   if (grid == 0) return hipSuccess;
   if (a.G % 2 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_pp_kernel, dim3(grid), dim3(512), 0, stream, a);
+  if (a.pot) hipLaunchKernelGGL(prefill_pp_kernel<true>, dim3(grid), dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL(prefill_pp_kernel<false>, dim3(grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

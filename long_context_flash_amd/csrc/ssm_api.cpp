@@ -136,6 +136,9 @@ static int prefill_impl(const ssm_tensor* q, const ssm_tensor* k, const ssm_tens
   if (tile_k != 64) return fail(SSM_EUNSUPPORTED, "tile_k %d not supported (64)", tile_k);
   float scale;
   if ((rc = resolve_scale(opts, (int)d, &scale))) return rc;
+  const int32_t weights = opts ? opts->weights : SSM_WEIGHTS_EXP;
+  if (weights != SSM_WEIGHTS_EXP && weights != SSM_WEIGHTS_ROWMAX_POT)
+    return fail(SSM_EINVAL, "unknown weights %d", (int)weights);
   if (B > INT32_MAX || S > (1 << 30) || Hq > 65536) return fail(SSM_EUNSUPPORTED, "problem too large");
   const int64_t nqt = (S + tile_q - 1) / tile_q, nkt = (S + tile_k - 1) / tile_k;
   const int64_t units = B * Hq * nqt;
@@ -177,6 +180,7 @@ static int prefill_impl(const ssm_tensor* q, const ssm_tensor* k, const ssm_tens
   a.scale_log2 = lscale * 1.4426950408889634f;
   a.tau_raw = std::isinf(tau) ? tau : tau / lscale;
   a.v_scale = 1.f;
+  a.pot = weights == SSM_WEIGHTS_ROWMAX_POT;
   if (skip_stats) {
     a.tile_state = skip_stats->tile_state;
     a.unit_gap = skip_stats->unit_gap;
@@ -255,6 +259,8 @@ static int decode_impl(const ssm_tensor* q, const ssm_kv_cache* k_cache, const s
   if (P < 1 || P > 64) return fail(SSM_EUNSUPPORTED, "num_splits %d not supported (1..64)", P);
   const int32_t flags = opts ? opts->decode_flags : 0;
   if (flags & ~SSM_DECODE_SINK_SEED) return fail(SSM_EINVAL, "unknown decode_flags bits 0x%x", (unsigned)flags);
+  if (opts && opts->weights != SSM_WEIGHTS_EXP)
+    return fail(SSM_EUNSUPPORTED, "the decode takes only exponential weights (weights = 0)");
   float scale;
   if ((rc = resolve_scale(opts, (int)d, &scale))) return rc;
   if (B > 65535 || Hq > 65536 || B * Hkv * P > INT32_MAX) return fail(SSM_EUNSUPPORTED, "problem too large");
@@ -374,6 +380,8 @@ static int prefill_paged_impl(const ssm_tensor* q, const ssm_kv_cache* k_cache, 
   if (tile_k != 64) return fail(SSM_EUNSUPPORTED, "tile_k %d not supported (64)", tile_k);
   float scale;
   if ((rc = resolve_scale(opts, (int)d, &scale))) return rc;
+  if (opts && opts->weights != SSM_WEIGHTS_EXP)
+    return fail(SSM_EUNSUPPORTED, "the chunked prefill takes only exponential weights (weights = 0)");
   if (total_q > INT32_MAX || max_q_len > (1 << 30) || Hq > 65536) return fail(SSM_EUNSUPPORTED, "problem too large");
   const int64_t nqt = ((int64_t)max_q_len + tile_q - 1) / tile_q, nkt = k_cache->max_pages;
   const int64_t units = (int64_t)batch * Hq * nqt;

@@ -22,6 +22,7 @@ struct PrefillArgs {
   float scale_log2;          // scale * log2(e)
   float tau_raw;             // tau / scale: threshold on raw q.k gaps; -inf never skips
   float v_scale;             // e4m3 V pages (mode 2): value = v_scale * code
+  int32_t pot;               // 1: Rowmax-PoT weights (non-chunked prefill only), 0: exponentials
   uint8_t* tile_state;       // nullable [units, nkt]
   float* unit_gap;           // nullable [units, nkt]
   unsigned long long* counters;  // nullable [4]

@@ -294,6 +294,22 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return (x >> 16).astype(np.uint16)
 
 
-__all__ = ["quantize_fp8_e4m3", "fp8_kv", "fp8_qk", "FP8_E4M3_MAX", "PrefillWorkload", "DecodeWorkload", "WORKLOADS", "TINY_PREFILL", "DECODE_32K", "PREFILL_16K",
+def gen_integer_qk(seed: int, B: int, S: int, Hq: int, Hkv: int, d: int, *, lo: int = -2, hi: int = 2,
+                   offset: float = 0.0) -> dict:
+    """Queries and keys with integer entries in [lo, hi] (exact in bf16, so every dot product is an exact small
+    integer), values standard normal, all as bf16 bits.  offset > 0: the last channel of every query is 1 and
+    that of every key uniform in (-offset, offset) (rounded to bf16), so each dot product lies within offset
+    (plus bf16 rounding) of an integer."""
+    r = np.random.default_rng(seed)
+    q = r.integers(lo, hi + 1, (B, S, Hq, d)).astype(np.float32)
+    k = r.integers(lo, hi + 1, (B, S, Hkv, d)).astype(np.float32)
+    if offset:
+        q[..., -1] = 1.0
+        k[..., -1] = r.uniform(-offset, offset, (B, S, Hkv)).astype(np.float32)
+    v = r.standard_normal((B, S, Hkv, d)).astype(np.float32)
+    return {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v)}
+
+
+__all__ = ["gen_integer_qk", "quantize_fp8_e4m3", "fp8_kv", "fp8_qk", "FP8_E4M3_MAX", "PrefillWorkload", "DecodeWorkload", "WORKLOADS", "TINY_PREFILL", "DECODE_32K", "PREFILL_16K",
            "PREFILL_128K", "DECODE_128K", "gen_prefill", "gen_decode", "kv_lens_for", "bf16_bits_to_f32",
            "f32_to_bf16_bits", "build", "default_threads", "replace"]

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 8
+    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 9
     for code in range(5):
         assert ssm.ssm_strerror(code)
     assert "unknown" in ssm.ssm_strerror(99)
@@ -171,6 +171,35 @@ def test_prefill_fp8qk_rejects(lib, case, code):
     rc = call_prefill_fp8qk(lib, **kw)
     assert rc == code, (rc, ssm.ssm_last_error())
     assert ssm.ssm_last_error()
+
+
+def _weights_opts(w):
+    o = ssm.Opts(0.0, 0, 0, 0, None, 0, 0)
+    o.weights = w
+    return o
+
+
+def test_weights_option_is_validated(lib):
+    """ssm_opts.weights: unknown values are SSM_EINVAL for both prefills; Rowmax-PoT weights are SSM_EUNSUPPORTED for
+    the decode and the chunked prefills (no device call: these run without a GPU)."""
+    assert ssm.WEIGHTS == {"exp": ssm_h_define("SSM_WEIGHTS_EXP"), "rowmax_pot": ssm_h_define("SSM_WEIGHTS_ROWMAX_POT")}
+    for w in (2, -1):
+        assert call_prefill(lib, opts=_weights_opts(w)) == ssm.SSM_EINVAL
+        assert "weights" in ssm.ssm_last_error()
+        assert call_prefill_fp8qk(lib, opts=_weights_opts(w)) == ssm.SSM_EINVAL
+    pot = ssm.WEIGHTS["rowmax_pot"]
+    dec = ssm.Opts(0.0, 0, 0, 16, 256 * 1024, 1 << 30)
+    dec.weights = pot
+    assert call_decode(lib, opts=dec) == ssm.SSM_EUNSUPPORTED and "weights" in ssm.ssm_last_error()
+    assert call_prefill_paged(lib, opts=_weights_opts(pot)) == ssm.SSM_EUNSUPPORTED
+    assert "weights" in ssm.ssm_last_error()
+    with pytest.raises(ValueError):
+        ssm._weights_code("softmax")
+
+
+def ssm_h_define(name):
+    m = re.search(rf"#define {name} (\d+)", open(os.path.join(ROOT, "include", "ssm.h")).read())
+    return int(m.group(1))
 
 
 def test_prefill_stats_too_small(lib):
