@@ -297,6 +297,44 @@ def time_prefill_vs_dense(ssm, torch, np, w, q, k, v, out, skip_ms, sparsity, st
             "speedup_vs_dense": round(ms / skip_ms, 3), "pages_prefill_speedup": 1.4}
 
 
+def time_pot_prefill(ssm, torch, np, w, q, k, v, out, tau, exp_ms, exp_dense_ms, steps, dev):
+    """Rowmax-PoT weights ("Approximating Softmax in Pretrained LLMs", Abstract: powers of two anchored at the row
+    maximum in place of the exponentials) on the same input: the launch at tau and at tau = -inf (every tile's
+    weights computed) against the exponential-weight launches, and how far the output moves from the
+    exponential one (max abs and relative L2 over the whole output; the page reports the effect as a perplexity
+    change, which needs a trained model)."""
+    cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+    run = lambda t: ssm.ssm_prefill(q, k, v, causal=True, tau=t, out=out, skip_stats=ssm.SkipStats(counters=cnt),
+                                    tile_q=w.tile_q, weights="rowmax_pot")
+    ms = _timed(torch, np, lambda: run(tau), steps)
+    c = cnt.cpu().numpy() / (steps + 1)
+    cnt.zero_()
+    dense_ms = _timed(torch, np, lambda: run(-math.inf), steps)
+    if int(cnt[1]) != 0:
+        raise RuntimeError("tau = -inf skipped tiles")
+    out_e = torch.empty_like(out)
+    ssm.ssm_prefill(q, k, v, causal=True, tau=tau, out=out_e, tile_q=w.tile_q)
+    run(tau)
+    torch.cuda.synchronize()
+    mx, dd, ee = 0.0, 0.0, 0.0
+    for i in range(0, w.S, 8192):
+        e = out_e[:, i:i + 8192].float()
+        dlt = out[:, i:i + 8192].float() - e
+        mx = max(mx, float(dlt.abs().max()))
+        dd += float((dlt * dlt).sum())
+        ee += float((e * e).sum())
+    del out_e
+    visited, skipped = float(c[0]), float(c[1])
+    dense, executed = prefill_flops(w, visited, visited - skipped)
+    return {"workload": f"{w.name}, weights 2^(rint(log2e*l) - rint(log2e*rowmax))", "ms": round(ms, 3),
+            "dense_tflops": round(dense / (ms / 1e3) / 1e12, 2),
+            "executed_tflops": round(executed / (ms / 1e3) / 1e12, 2), "sparsity": round(skipped / visited, 4),
+            "speedup_vs_exp": round(exp_ms / ms, 3), "no_skip_ms": round(dense_ms, 3),
+            "no_skip_speedup_vs_exp": round(exp_dense_ms / dense_ms, 3),
+            "vs_exp_output": {"max_abs": float("%.4g" % mx), "rel_l2": float("%.4g" % math.sqrt(dd / max(ee, 1e-300)))},
+            "pages_speedup": {"causal_8k_fp8": 1.124, "noncausal_8k_fp8": 1.258, "hardware": "B200"}}
+
+
 def time_decode_tau_sweep(ssm, torch, np, w, dq, kp, vp, pt, lens, dout, ws, steps, dev):
     """The decode at each calibrated tau of its workload (tau = -inf, written as null, is the dense kernel): time,
     sparsity and the speedup over tau = -inf (as context: the pages project 1.36x for decode of Llama 3.3 70B)."""
@@ -900,6 +938,8 @@ def main():
                                                    args.steps, dev)
         res["prefill_vs_dense"] = time_prefill_vs_dense(ssm, torch, np, pw, q, k, v, pout, res["prefill_ms"],
                                                         res["prefill_sparsity"], args.steps, dev)
+        res["prefill_rowmax_pot"] = time_pot_prefill(ssm, torch, np, pw, q, k, v, pout, tau_p, res["prefill_ms"],
+                                                     res["prefill_vs_dense"]["dense_ms"], args.steps, dev)
     if run_decode:
         c = dcnt.cpu().numpy() / args.steps
         ssm.ssm_decode(dq, kp, vp, lens, tau=tau_d, out=dout, page_table=pt, num_splits=dw.num_splits,
