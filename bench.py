@@ -559,6 +559,65 @@ def leg_decode_32k(ssm, torch, np, steps, dev, threads, cpu=True):
             "oracle_threads": threads, "variants": rows}
 
 
+def leg_decode_b256(ssm, torch, np, steps, dev, threads, cpu=True, n_seq=8):
+    """decode_b256_kv16k_paged: 256 sequences (kv_len ~ U[8K, 16K], as many keys in all as the 128K decode) through
+    one ssm_decode call: the longest-first ordering kernel (one pass over the 256 lengths), the split kernel over
+    256 x 8 x 16 workgroups and the combine.  GPU time and HBM rate, and the parity of the timed outputs on
+    sampled sequences (the longest, the shortest and n_seq - 2 others) against the oracle."""
+    import synth
+    w = synth.DECODE_B256
+    tau = w.taus[0]
+    P = w.num_splits
+    data = synth.gen_decode(w, threads=threads)
+    dq = ssm.bf16_from_bits(data["q"], dev)
+    kp, vp = ssm.bf16_from_bits(data["k_pool"], dev), ssm.bf16_from_bits(data["v_pool"], dev)
+    pt = torch.from_numpy(data["page_table"]).to(dev)
+    lens = torch.from_numpy(data["kv_lens"]).to(dev)
+    out = torch.empty_like(dq)
+    ws = ssm.decode_workspace(w.B, w.Hq, w.d, P, dev)
+    cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+    run = lambda st: ssm.ssm_decode(dq, kp, vp, lens, tau=tau, out=out, page_table=pt, num_splits=P, workspace=ws,
+                                    skip_stats=st)
+    ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps)
+    got = out.float().cpu().numpy()
+    c = cnt.cpu().numpy() / (steps + 1)
+    state = torch.zeros(w.B * w.Hkv, pt.shape[1], dtype=torch.uint8, device=dev)
+    run(ssm.SkipStats(tile_state=state))
+    st = state.cpu().numpy()
+    if not (int((st != 0).sum()) == c[0] and int((st == 2).sum()) == c[1]):
+        raise RuntimeError("decode B=256: tile states disagree with the timed counters")
+    kb, vk, va, small = decode_bytes(w, data["kv_lens"], st, P)
+    t = ms / 1e3
+    tot = kb + vk + small
+    res = {"workload": f"{w.name} (B {w.B}, paged, kv_len U[{w.kv_len_lo}, {w.kv_len_hi}], P {P}, tau -ln 1000)",
+           "ms": round(ms, 4), "sparsity": round(float(c[1]) / float(c[0]), 4),
+           "kv_gbps": round((kb + vk) / t / 1e9, 1), "total_gbps": round(tot / t / 1e9, 1),
+           "hbm_frac": round(tot / t / 1e9 / HBM_PEAK_GBPS, 4)}
+    del kp, vp, ws
+    if cpu:
+        import oracle
+        L = data["kv_lens"]
+        order = np.argsort(-L, kind="stable")
+        rng = np.random.default_rng(256)
+        others = rng.choice(order[1:-1], n_seq - 2, replace=False)
+        pick = np.array([order[0], order[-1], *others], np.int64)
+        kc, vc = paged_to_contiguous(np, w, data, pick)
+        r = oracle.decode(data["q"][pick], kc, vc, L[pick], tau=tau, num_splits=P, threads=threads)
+        maxt = r["state"].shape[1]
+        rows = (pick[:, None] * w.Hkv + np.arange(w.Hkv)[None, :]).ravel()
+        stg = st[rows][:, :maxt]
+        if st[rows][:, maxt:].any():
+            raise RuntimeError("decode B=256: tiles past the sequences marked visited")
+        ov = flip_override(np, stg, r["state"], r["gamma"], tau)
+        ro = r["out"] if ov is None else oracle.decode(data["q"][pick], kc, vc, L[pick], tau=tau, num_splits=P,
+                                                       override=ov, threads=threads)["out"]
+        G = w.Hq // w.Hkv
+        res["parity"] = parity_fields(np, got[pick].reshape(len(pick) * w.Hkv, G, w.d), ro, stg.ravel(),
+                                      r["state"].ravel(), r["gamma"].ravel(), tau)
+        res["parity"]["sequences"] = [int(x) for x in pick]
+    return res
+
+
 def leg_prefill_16k(ssm, torch, np, steps, dev, threads, cpu=True, n_units=64):
     """prefill_s16k (batch 1, 64/8 heads, d 128, S 16384 causal) at tau = -inf, -ln 100 and -ln 1000: GPU time,
     sparsity, dense-equivalent and executed TFLOP/s and the MFMA roofline fraction at each tau, beside the
@@ -992,6 +1051,8 @@ def main():
                 res[leg]["read_ceiling_frac"] = round(res[leg]["total_gbps"] / read_ceiling, 4)
         log("decode 32K legs")
         res["decode_32k"] = leg_decode_32k(ssm, torch, np, args.steps, dev, cpu_threads, cpu=not args.no_cpu_baseline)
+        res["decode_b256"] = leg_decode_b256(ssm, torch, np, args.steps, dev, cpu_threads,
+                                             cpu=not args.no_cpu_baseline)
     if run_prefill and not args.main_only:
         log("prefill 16K legs")
         res["prefill_16k"] = leg_prefill_16k(ssm, torch, np, args.steps, dev, cpu_threads,

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 9
+#define SSM_ABI_VERSION 10
 
 enum {
   SSM_OK = 0,
@@ -224,8 +224,9 @@ int ssm_prefill_paged_fp8qk(const ssm_tensor* q, float q_scale, const ssm_kv_cac
                             void* stream, const ssm_opts* opts);
 
 /* Bytes of device workspace ssm_decode needs: fp32 partial outputs and log-sum-exps per (b, query head,
- * split), and for batches up to 8192 the longest-first dispatch order of the sequences (int32 per sequence,
- * written by the call).  0 for invalid arguments. */
+ * split), for batches up to 8192 the longest-first dispatch order of the sequences (int32 per sequence,
+ * written by the call), and two uint32 skip counts per (b, head, split) (used when skip counters are asked
+ * for).  0 for invalid arguments. */
 size_t ssm_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int32_t num_splits);
 
 const char* ssm_strerror(int code);   /* static text for a return code */

@@ -61,7 +61,7 @@ class Opts(ctypes.Structure):
                 ("decode_flags", ctypes.c_int32), ("weights", ctypes.c_int32)]
 
 
-ABI_VERSION = 9               # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
+ABI_VERSION = 10              # the layout above and the entry points match SSM_ABI_VERSION of include/ssm.h
 DECODE_SINK_SEED = 1          # SSM_DECODE_SINK_SEED
 WEIGHTS = {"exp": 0, "rowmax_pot": 1}  # SSM_WEIGHTS_EXP, SSM_WEIGHTS_ROWMAX_POT
 

@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
 
   const int64_t part_row = ((int64_t)b * a.Hq + g * G) * P + split;  // + q*P for query q of the group
   if (s_begin >= s_end) {  // empty split: lse = -inf, o = 0
+    if (a.counters && tid == 0) *reinterpret_cast<u32x2*>(a.wg_cnt + ((int64_t)bg * P + split) * 2) = u32x2{0u, 0u};
     for (int i = tid; i < G * D; i += 256) {
       const int q = i / D, c = i - q * D;
       a.part_o[(part_row + (int64_t)q * P) * D + c] = 0.f;
@@ -161,16 +162,21 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   // A operand of the QK^T MFMAs, key block kb, k-step ks: bf16 as loaded, or fp8 codes converted at use
   u32x4 kreg[4][KS];       // bf16: one k-step per register
   u32x4 kraw[4][KS / 2];   // fp8: k-steps 2j and 2j+1 in register j (bytes 0-7 and 8-15)
+  auto k_rsrc = [&](int t) {
+    return decode_tile_rsrc<ES>(a.k, a.k_pages, a.k_max_pages, k_pool_pages, a.k_sb, a.k_sh, a.k_ss, b, g, t, len, D);
+  };
+  // key block kb of a K tile (16 key rows) into its operand registers
+  auto load_k_block = [&](rsrc_t r, int kb) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (ES == 2) kreg[kb][ks] = buffer_load_16(r, kvo[kb] + ks * 64);
+      else if (ks % 2 == 0) kraw[kb][ks / 2] = buffer_load_16(r, kvo[kb] + ks * 32);
+    }
+  };
   auto load_k = [&](int t) {
-    const rsrc_t r = decode_tile_rsrc<ES>(a.k, a.k_pages, a.k_max_pages, k_pool_pages, a.k_sb, a.k_sh, a.k_ss, b, g,
-                                          t, len, D);
+    const rsrc_t r = k_rsrc(t);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (ES == 2) kreg[kb][ks] = buffer_load_16(r, kvo[kb] + ks * 64);
-        else if (ks % 2 == 0) kraw[kb][ks / 2] = buffer_load_16(r, kvo[kb] + ks * 32);
-      }
+    for (int kb = 0; kb < 4; ++kb) load_k_block(r, kb);
   };
   auto k_operand = [&](int kb, int ks) {
     if constexpr (ES == 2) return as_bf16x8(kreg[kb][ks]);
@@ -178,17 +184,23 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   };
   u32x4 vreg[2][8];  // 8 key rows x 8 channels per st (bf16), converted from vraw for an fp8 cache
   u32x2 vraw[2][8];
-  auto load_v = [&](int t) {
-    const rsrc_t r = decode_tile_rsrc<ES>(a.v, a.v_pages, a.v_max_pages, v_pool_pages, a.v_sb, a.v_sh, a.v_ss, b, g,
-                                          t, len, D);
+  // V rows of tile t if `real`, else 16 loads from an empty resource (zeros, no memory traffic): the loop issues
+  // the same loads on every path, so the compiler's wait counts stay exact and never drain the next K tile.
+  // Each V row is read whole and once, with the non-temporal policy: its lines do not displace the K tile's,
+  // which every 64-byte K load leaves half-read in L2 for the next instruction (8% faster at half the tiles
+  // kept, 10% with every tile kept; the same policy on the K loads makes the decode slower).
+  auto load_v = [&](int t, bool real) {
+    const rsrc_t r = real ? decode_tile_rsrc<ES>(a.v, a.v_pages, a.v_max_pages, v_pool_pages, a.v_sb, a.v_sh,
+                                                 a.v_ss, b, g, t, len, D)
+                          : make_rsrc(a.v, 0u);
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // lanes whose channels lie past D (D = 64) read outside the resource, i.e. zeros
         const uint32_t off = v_ch_ok ? vvo[st][e >> 2] + (e & 3) * vrow : 0xffffffffu;
-        if constexpr (ES == 2) vreg[st][e] = buffer_load_16(r, off);
-        else vraw[st][e] = buffer_load_8(r, off);
+        if constexpr (ES == 2) vreg[st][e] = buffer_load_16_nt(r, off);
+        else vraw[st][e] = buffer_load_8_nt(r, off);
       }
   };
 
@@ -199,8 +211,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   unsigned n_exec = 0, n_vis = 0;
 
   // S^T of key tile t (its K operand in kreg): s[kb][i] = S^T[key t*64 + kb*16 + 4*grp + i][query qc],
-  // -inf for invalid keys and padding columns; returns the tile maximum of this lane's query
-  auto score = [&](int t, f32x4 (&s)[4]) {
+  // -inf for invalid keys and padding columns; returns the tile maximum of this lane's query.  Each key
+  // block's registers are refilled with tile t_next's block as soon as its MFMAs have read them, so the next
+  // tile is in flight through this tile's vote, barrier and P.V; t_next < 0 loads zeros from an empty resource
+  // (no memory traffic), so every path issues the same loads.
+  auto score = [&](int t, f32x4 (&s)[4], int t_next) {
+    const rsrc_t r_next = t_next >= 0 ? k_rsrc(t_next) : make_rsrc(a.k, 0u);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f32x4 x = f32x4{};
@@ -208,6 +224,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
       for (int ks = 0; ks < KS; ++ks)
         x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kb, ks), qreg[ks], x, 0, 0, 0);
       s[kb] = x;
+      __builtin_amdgcn_sched_barrier(0);
+      load_k_block(r_next, kb);
+      __builtin_amdgcn_sched_barrier(0);
     }
     const int lim = qc < G ? len - 1 - t * kDecTK : -1;  // key offset o in the tile is valid iff o <= lim
     float mx = neg_inf();
@@ -229,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
   if (a.sink_seed && s_begin > 0) {
     load_k(0);
     f32x4 s0[4];
-    r_prev = score(0, s0);
+    r_prev = score(0, s0, -1);
   }
   {
     const int t0 = s_begin + w;
@@ -272,7 +291,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     const bool has = t < s_end;
     f32x4 s[4];
     float mx = neg_inf();
-    if (has) mx = score(t, s);
+    const int tn = t + kDecWaves;
+    {
+      // every wave scores (a wave past the split end scores the zeros it loaded) and issues the next loads
+      const float mxs = score(t, s, c + 1 < nchunks && tn < s_end ? tn : -1);
+      if (has) mx = mxs;
+    }
     if (lane < kDecMaxG) mt[c & 1][w][lane] = mx;
     __syncthreads();
     float r = r_prev, r_all = r_prev;
@@ -300,11 +324,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     // the previous kept tile's V rows were loaded one chunk ago and arrived while this tile was scored
     // and voted on; its P.V goes in before this tile can rescale the accumulators
     if (pending) pv();
-    if (keep) load_v(t);
-    {
-      const int tn = t + kDecWaves;
-      if (c + 1 < nchunks && tn < s_end) load_k(tn);
-    }
+    load_v(t, keep);
     pending = keep;
     if (keep) {
       ++n_exec;
@@ -367,7 +387,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     a.part_o[(part_row + (int64_t)q * P) * D + ch] = ok ? o / lsum * a.v_scale : 0.f;
     if (ch == 0) a.part_lse[part_row + (int64_t)q * P] = ok ? mstar * a.scale_log2 + __builtin_log2f(lsum) : neg_inf();
   }
-  // skip counters: one set of atomics per workgroup
+  // skip counts: this workgroup's totals into its workspace slot (the combine adds them up per KV group, so the
+  // four global counters take B * Hkv sets of atomics instead of one per workgroup)
   if (a.counters) {
     if (lane == 0) {
       cnt_lds[w][0] = n_vis;
@@ -375,13 +396,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     }
     __syncthreads();
     if (tid == 0) {
-      unsigned long long vis = 0, ex = 0;
+      unsigned vis = 0, ex = 0;
 #pragma unroll
       for (int w2 = 0; w2 < kDecWaves; ++w2) vis += cnt_lds[w2][0], ex += cnt_lds[w2][1];
-      atomicAdd(&a.counters[0], vis);
-      atomicAdd(&a.counters[1], vis - ex);
-      atomicAdd(&a.counters[2], vis);
-      atomicAdd(&a.counters[3], ex);
+      *reinterpret_cast<u32x2*>(a.wg_cnt + ((int64_t)bg * P + split) * 2) = u32x2{vis, ex};
     }
   }
 }
@@ -407,26 +425,70 @@ __global__ __launch_bounds__(256) void decode_order_kernel(const int32_t* kv_len
   order[r] = c;
 }
 
-// out[b, h, :] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M); 0 when every split is empty.
+// out[b, h, :] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M); 0 when every split is empty.  Lane s of each
+// wave holds split s's weight (num_splits <= 64), every thread reads its channel of eight partials at a time,
+// and both sums run over the splits in order.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x, ch = threadIdx.x;
+  const int bh = blockIdx.x, ch = threadIdx.x, lane = ch & 63;
   const int b = bh / a.Hq, h = bh - b * a.Hq;
   const int P = a.num_splits;
-  const float* lse = a.part_lse + (int64_t)bh * P;
   const float* po = a.part_o + (int64_t)bh * P * D;
-  float M = neg_inf();
-  for (int s = 0; s < P; ++s) M = fmaxf(M, lse[s]);
+  const float ls = lane < P ? a.part_lse[(int64_t)bh * P + lane] : neg_inf();
+  float M = ls;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float wl = M == neg_inf() ? 0.f : exp2_fast(ls - M);  // 0 for empty splits and lanes >= P
   float wsum = 0.f, o = 0.f;
-  if (M != neg_inf())
-    for (int s = 0; s < P; ++s) {
-      const float wgt = exp2_fast(lse[s] - M);
-      wsum += wgt;
-      o += wgt * po[(int64_t)s * D + ch];
+  for (int s0 = 0; s0 < P; s0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = s0 + j < P ? po[(int64_t)(s0 + j) * D + ch] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < P) {
+        const float wgt = __shfl(wl, s0 + j, 64);
+        wsum += wgt;
+        o += wgt * x[j];
+      }
     }
+  }
   const float r = wsum > 0.f ? o / wsum : 0.f;
-  const __bf16 x = (__bf16)r;
-  a.o[(int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ch] = __builtin_bit_cast(uint16_t, x);
+  const __bf16 y = (__bf16)r;
+  a.o[(int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ch] = __builtin_bit_cast(uint16_t, y);
+  // skip counters: the workgroup of each sequence's first query head adds up the counts of the sequence's
+  // Hkv * P split workgroups (all threads, then the waves' sums), so the global counters take one set of
+  // atomics per sequence
+  if (a.counters && h == 0) {
+    __shared__ unsigned long long red[D / 64][2];
+    const int n = a.Hkv * P;
+    const u32x2* wc = reinterpret_cast<const u32x2*>(a.wg_cnt) + (int64_t)b * n;
+    unsigned long long vis = 0, ex = 0;
+    for (int i = ch; i < n; i += D) {
+      const u32x2 x = wc[i];
+      vis += x[0];
+      ex += x[1];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      vis += __shfl_xor(vis, off, 64);
+      ex += __shfl_xor(ex, off, 64);
+    }
+    if (lane == 0) {
+      red[ch >> 6][0] = vis;
+      red[ch >> 6][1] = ex;
+    }
+    __syncthreads();
+    if (ch == 0) {
+      vis = ex = 0;
+#pragma unroll
+      for (int wv = 0; wv < D / 64; ++wv) vis += red[wv][0], ex += red[wv][1];
+      atomicAdd(&a.counters[0], vis);
+      atomicAdd(&a.counters[1], vis - ex);
+      atomicAdd(&a.counters[2], vis);
+      atomicAdd(&a.counters[3], ex);
+    }
+  }
 }
 
 // The decode workspace of ssm_decode_noalloc: one statically sized array in each GPU's memory, held until the

@@ -87,16 +87,18 @@ const char* ssm_last_error(void) { return g_last_error; }
 
 namespace {
 // decode workspace layout: partial outputs [B, Hq, P, d] fp32 | partial LSEs [B, Hq, P] fp32 | dispatch order [B]
-// int32 (batches up to kDecSortMax), each part starting on a 256-byte boundary
+// int32 (batches up to kDecSortMax) | skip counts per split workgroup [B, Hkv, P, 2] uint32 (sized for Hkv = Hq),
+// each part starting on a 256-byte boundary
 struct DecodeWs {
-  size_t lse_off, order_off, bytes;
+  size_t lse_off, order_off, cnt_off, bytes;
 };
 DecodeWs decode_ws_layout(size_t B, size_t Hq, size_t d, size_t P) {
   const size_t rows = B * Hq * P;
   DecodeWs w;
   w.lse_off = (rows * d * sizeof(float) + 255) & ~(size_t)255;
   w.order_off = (w.lse_off + rows * sizeof(float) + 255) & ~(size_t)255;
-  w.bytes = w.order_off + (B <= (size_t)ssm::kDecSortMax ? B * sizeof(int32_t) : 0);
+  w.cnt_off = (w.order_off + (B <= (size_t)ssm::kDecSortMax ? B * sizeof(int32_t) : 0) + 255) & ~(size_t)255;
+  w.bytes = w.cnt_off + rows * 2 * sizeof(uint32_t);
   return w;
 }
 }  // namespace
@@ -320,6 +322,7 @@ static int decode_impl(const ssm_tensor* q, const ssm_kv_cache* k_cache, const s
   a.part_o = reinterpret_cast<float*>(ws_base);
   a.part_lse = reinterpret_cast<float*>(ws_base + lay.lse_off);
   a.order = B <= ssm::kDecSortMax ? reinterpret_cast<int32_t*>(ws_base + lay.order_off) : nullptr;
+  a.wg_cnt = reinterpret_cast<uint32_t*>(ws_base + lay.cnt_off);
   a.o = static_cast<uint16_t*>(out->data);
   a.o_sb = out->stride[0]; a.o_sh = out->stride[1];
   if (skip_stats) {

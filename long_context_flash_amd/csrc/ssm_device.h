@@ -118,6 +118,15 @@ __device__ __forceinline__ uint32_t buffer_load_4(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ u32x2 buffer_load_8(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
+// The same loads with the non-temporal cache policy (the `nt` bit): for data read once whose lines should not
+// displace lines that are still to be read again from L2.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ u32x4 buffer_load_16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNT);
+}
+__device__ __forceinline__ u32x2 buffer_load_8_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicyNT);
+}
 
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
 

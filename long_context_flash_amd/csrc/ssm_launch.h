@@ -61,6 +61,7 @@ struct DecodeArgs {
   float* part_o;             // workspace [B, Hq, P, d] fp32
   float* part_lse;           // workspace [B, Hq, P] fp32 (base-2 log-sum-exp of raw-scaled logits)
   int32_t* order;            // workspace [B]: dispatch order, longest sequence first (NULL: plain order)
+  uint32_t* wg_cnt;          // workspace [B, Hkv, P, 2]: (visited, executed) tiles of each split workgroup
   uint16_t* o;               // [B, Hq, d]
   int64_t o_sb, o_sh;
   uint8_t* tile_state;

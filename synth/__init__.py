@@ -173,6 +173,13 @@ def gen_prefill(w: PrefillWorkload, *, bf16=True, fp32=False, threads=None) -> d
     return out
 
 
+# 256 sequences with as many cached keys in all as DECODE_128K (kv_len ~ U[8192, 16384]): a large batch through
+# one decode call (timing of the dispatch order's cost; not an oracle-calibrated operating point).
+DECODE_B256 = DecodeWorkload("decode_b256_kv16k_paged", seed=1006, B=256, Hq=64, Hkv=8, d=128,
+                             kv_len_lo=8192, kv_len_hi=16384, paged=True, num_splits=16,
+                             taus=(-math.log(1000.0),))
+
+
 def kv_lens_for(w: DecodeWorkload) -> np.ndarray:
     lens = np.empty(w.B, np.int32)
     if w.kv_len > 0:
@@ -310,6 +317,6 @@ def gen_integer_qk(seed: int, B: int, S: int, Hq: int, Hkv: int, d: int, *, lo: 
     return {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v)}
 
 
-__all__ = ["gen_integer_qk", "quantize_fp8_e4m3", "fp8_kv", "fp8_qk", "FP8_E4M3_MAX", "PrefillWorkload", "DecodeWorkload", "WORKLOADS", "TINY_PREFILL", "DECODE_32K", "PREFILL_16K",
+__all__ = ["gen_integer_qk", "DECODE_B256", "quantize_fp8_e4m3", "fp8_kv", "fp8_qk", "FP8_E4M3_MAX", "PrefillWorkload", "DecodeWorkload", "WORKLOADS", "TINY_PREFILL", "DECODE_32K", "PREFILL_16K",
            "PREFILL_128K", "DECODE_128K", "gen_prefill", "gen_decode", "kv_lens_for", "bf16_bits_to_f32",
            "f32_to_bf16_bits", "build", "default_threads", "replace"]

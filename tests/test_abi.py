@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 9
+    assert ssm.ssm_abi_version() == ssm.ABI_VERSION == 10
     for code in range(5):
         assert ssm.ssm_strerror(code)
     assert "unknown" in ssm.ssm_strerror(99)
@@ -49,11 +49,12 @@ def test_workspace_bytes(lib):
     o_bytes = 32 * 64 * 16 * 128 * 4
     assert n >= o_bytes + 32 * 64 * 16 * 4 + 32 * 4
     assert ssm.ssm_decode_workspace_bytes(1, 1, 128, 0) == 0
-    # partial outputs, partial LSEs and (batches up to 8192) the dispatch order, each on a 256-byte boundary
+    # partial outputs, partial LSEs, (batches up to 8192) the dispatch order and two skip counts per (b, head,
+    # split), each on a 256-byte boundary
     r256 = lambda x: (x + 255) // 256 * 256
     for B in (1, 7, 8192, 8193):
         rows = B * 8 * 4
-        want = r256(r256(rows * 64 * 4) + rows * 4) + (B * 4 if B <= 8192 else 0)
+        want = r256(r256(r256(rows * 64 * 4) + rows * 4) + (B * 4 if B <= 8192 else 0)) + rows * 8
         assert ssm.ssm_decode_workspace_bytes(B, 8, 64, 4) == want, B
 
 

@@ -84,6 +84,16 @@ def test_decode_128k_paged_sampled():
         check_decode(data, tau=tau, num_splits=w.num_splits, paged=True, batches=batches, where=f"128k tau={tau}")
 
 
+def test_decode_b256_paged_sampled():
+    """256 sequences (kv_len 8K-16K, paged, as many keys as the 128K workload) in one call: the ordering kernel's
+    longest-first dispatch over a large batch; the oracle checks the longest, the shortest and four others."""
+    w = synth.DECODE_B256
+    data = synth.gen_decode(w)
+    order = np.argsort(-data["kv_lens"], kind="stable")
+    batches = np.unique([order[0], order[-1], 3, 100, 177, 255])
+    check_decode(data, tau=w.taus[0], num_splits=w.num_splits, paged=True, batches=batches, where="B=256 paged")
+
+
 def test_batch_beyond_dispatch_sort():
     """Batches above 8192 sequences skip the longest-first dispatch order (plain workgroup order, no order array
     in the workspace): the outputs of such a batch equal those of its first 8192 sequences run as a sorted batch
