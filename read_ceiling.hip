@@ -9,7 +9,8 @@
 //   k_fp8     16 key rows x 64 B of 128-byte rows (the fp8 K tile, 8 KB, in 8 instructions)
 //   k_fp8_b64 16 key rows x 32 B of 128-byte rows, 8 bytes per lane (8 KB in 16 instructions)
 // each at 2 workgroups of 4 waves per CU with one or two tiles in flight per wave, and at 4 workgroups with
-// one.  Tile i of wave w is tile (i * waves + w) of the buffer, so the grid sweeps the buffer front to back.
+// one; the bf16 shapes also with the non-temporal cache policy (the `nt` bit, `_nt`).  Tile i of wave w is tile
+// (i * waves + w) of the buffer, so the grid sweeps the buffer front to back.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -22,6 +23,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 namespace {
 
 enum Shape { kKBf16 = 0, kRows256 = 1, kKFp8 = 2, kKFp8B64 = 3 };
+
+constexpr int kNT = 2;  // cache policy bits of the buffer loads: non-temporal
 
 constexpr uint32_t tile_bytes(int shape) { return shape <= kRows256 ? 16384u : 8192u; }
 
@@ -36,7 +39,7 @@ __device__ __forceinline__ uint32_t load_offset(int shape, int i, int lane) {
   }
 }
 
-template <int SHAPE, int DEPTH, int OCC>
+template <int SHAPE, int DEPTH, int OCC, int POLICY>
 __global__ __launch_bounds__(256, OCC) void stream(const uint8_t* __restrict__ src, uint64_t nbytes,
                                                    uint32_t* __restrict__ out, int tiles_per_wave) {
   constexpr uint32_t TB = tile_bytes(SHAPE);
@@ -58,10 +61,10 @@ __global__ __launch_bounds__(256, OCC) void stream(const uint8_t* __restrict__ s
       for (int i = 0; i < NL; ++i) {
         const uint32_t off = load_offset(SHAPE, i, lane);
         if constexpr (SHAPE == kKFp8B64) {
-          const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+          const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY);
           x[d][i] = u32x4{y[0], y[1], 0u, 0u};
         } else {
-          x[d][i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+          x[d][i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY);
         }
       }
     }
@@ -83,12 +86,12 @@ __global__ __launch_bounds__(256, OCC) void stream(const uint8_t* __restrict__ s
   } while (0)
 
 // GB/s of the best of three sweeps
-template <int SHAPE, int DEPTH, int OCC>
+template <int SHAPE, int DEPTH, int OCC, int POLICY = 0>
 double rate(const uint8_t* src, uint64_t nbytes, uint32_t* out, int num_cus) {
   const int grid = num_cus * OCC;
   const uint32_t TB = tile_bytes(SHAPE);
   const int tpw = (int)(nbytes / TB / ((uint64_t)grid * 4)) / DEPTH * DEPTH;
-  hipLaunchKernelGGL((stream<SHAPE, DEPTH, OCC>), dim3(grid), dim3(256), 0, 0, src, nbytes, out, DEPTH);
+  hipLaunchKernelGGL((stream<SHAPE, DEPTH, OCC, POLICY>), dim3(grid), dim3(256), 0, 0, src, nbytes, out, DEPTH);
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
   float best = 1e30f;
@@ -97,7 +100,7 @@ double rate(const uint8_t* src, uint64_t nbytes, uint32_t* out, int num_cus) {
   CHECK(hipEventCreate(&e1));
   for (int rep = 0; rep < 3; ++rep) {
     CHECK(hipEventRecord(e0, 0));
-    hipLaunchKernelGGL((stream<SHAPE, DEPTH, OCC>), dim3(grid), dim3(256), 0, 0, src, nbytes, out, tpw);
+    hipLaunchKernelGGL((stream<SHAPE, DEPTH, OCC, POLICY>), dim3(grid), dim3(256), 0, 0, src, nbytes, out, tpw);
     CHECK(hipGetLastError());
     CHECK(hipEventRecord(e1, 0));
     CHECK(hipEventSynchronize(e1));
@@ -129,10 +132,15 @@ int main() {
       {"k_bf16_depth1_4wg", rate<kKBf16, 1, 4>(src, nbytes, out, num_cus)},
       {"rows_256_depth1_2wg", rate<kRows256, 1, 2>(src, nbytes, out, num_cus)},
       {"rows_256_depth1_4wg", rate<kRows256, 1, 4>(src, nbytes, out, num_cus)},
+      {"rows_256_depth2_2wg", rate<kRows256, 2, 2>(src, nbytes, out, num_cus)},
       {"k_fp8_depth1_2wg", rate<kKFp8, 1, 2>(src, nbytes, out, num_cus)},
       {"k_fp8_depth2_2wg", rate<kKFp8, 2, 2>(src, nbytes, out, num_cus)},
       {"k_fp8_b64_depth1_2wg", rate<kKFp8B64, 1, 2>(src, nbytes, out, num_cus)},
       {"k_fp8_b64_depth2_2wg", rate<kKFp8B64, 2, 2>(src, nbytes, out, num_cus)},
+      {"k_bf16_depth2_2wg_nt", rate<kKBf16, 2, 2, kNT>(src, nbytes, out, num_cus)},
+      {"rows_256_depth1_2wg_nt", rate<kRows256, 1, 2, kNT>(src, nbytes, out, num_cus)},
+      {"rows_256_depth2_2wg_nt", rate<kRows256, 2, 2, kNT>(src, nbytes, out, num_cus)},
+      {"rows_256_depth1_4wg_nt", rate<kRows256, 1, 4, kNT>(src, nbytes, out, num_cus)},
   };
   double best = 0;
   std::printf("{\"buffer_bytes\": %llu, \"compute_units\": %d, \"gbps\": {", (unsigned long long)nbytes, num_cus);
