@@ -336,7 +336,9 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   float m_true = neg_inf();  // running max of raw scores over kept tiles (the skip rule's m_{i-1})
   float m_ref = neg_inf();   // reference max of the exponentials (trails m_true by at most 8/c2)
   float moff = 0.f;          // m_ref * c2 (0 while m_ref = -inf)
-  float l_part = 0.f;        // this lane's half of the softmax denominator
+  // this lane's half of the softmax denominator, in two chains (weight pairs alternate between them) so that
+  // consecutive row-sum updates do not wait for each other; added in the epilogue
+  float l_part[2] = {0.f, 0.f};
   int n_exec = 0;
 
   // S^T for keys t*64 .. t*64+63 (two 32-key blocks) x this wave's 32 query columns from the K tile at
@@ -377,14 +379,14 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     const float s0 = s[st >> 1][8 * (st & 1) + e], s1 = s[st >> 1][8 * (st & 1) + e + 1];
     if constexpr (POT) pk[st][e >> 1] = pot_pack_bf16x2(s0, s1, c2, eo);
     else pk[st][e >> 1] = pack_bf16x2(exp2_fast(fmaf(s0, c2, -eo)), exp2_fast(fmaf(s1, c2, -eo)));
-    l_part = dot2_bf16_sum(pk[st][e >> 1], l_part);
+    l_part[(n >> 1) & 1] = dot2_bf16_sum(pk[st][e >> 1], l_part[(n >> 1) & 1]);
   };
   // keep the exponentials where they are issued (next to the MFMAs they overlap) instead of letting
   // them sink towards their use one iteration later
   auto pin = [&](uint32_t (&pk)[4][4]) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) asm volatile("" ::"v"(pk[st][0]), "v"(pk[st][1]), "v"(pk[st][2]), "v"(pk[st][3]));
-    asm volatile("" : "+v"(l_part));
+    asm volatile("" : "+v"(l_part[0]), "+v"(l_part[1]));
   };
   // O^T += V^T . P^T from the V tile at `vl`; MFMA j is (16-key step j/CB, channel block j%CB).  The
   // exponentials of the current tile's scores `s` against offset `eo` (into `pk_out`) are spread over
@@ -502,14 +504,16 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
           const bool move = kn - m_ref > kRefSlack;  // also true while m_ref = -inf and kn finite
           alpha = move ? (m_ref == neg_inf() ? 0.f : ldexpf(1.f, (int)(m_ref - kn))) : 1.f;  // exact
           resc = wave_ballot(move) != 0;
-          l_part *= alpha;
+          l_part[0] *= alpha;
+          l_part[1] *= alpha;
           m_ref = move ? kn : m_ref;
           moff = m_ref == neg_inf() ? 0.f : m_ref;
         } else {
           const bool move = (m_true - m_ref) * c2 > kRefSlack;  // also true while m_ref = -inf and m_true finite
           alpha = move ? exp2_fast((m_ref - m_true) * c2) : 1.f;  // 0 when m_ref = -inf
           resc = wave_ballot(move) != 0;
-          l_part *= alpha;
+          l_part[0] *= alpha;
+          l_part[1] *= alpha;
           m_ref = move ? m_true : m_ref;
           moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
         }
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: O = acc / l, bf16
-  const float l_tot = pair_sum(l_part);
+  const float l_tot = pair_sum(l_part[0] + l_part[1]);
   // KV8: the values are v_scale * code
   const float inv = l_tot > 0.f ? (KV8 ? a.v_scale : 1.f) / l_tot : 0.f;
   if (row_ok) {

@@ -207,8 +207,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   float m_run = neg_inf();  // max of the row's scores over the tiles voted on so far (the skip rule's m_{i-1})
   float m_ref = neg_inf();  // reference max of the exponentials (trails the true max by at most 8/c2); POT: the
                             // integer reference in base-2 log-weight units (trails rint(c2*max) by at most 8)
-  float l_part = 0.f;       // this lane's half of the softmax denominator (summed in prefill_kernel's order, so the
-                            // two kernels give the same bits)
+  // this lane's half of the softmax denominator in two chains, weight pairs alternating, exactly as
+  // prefill_kernel sums it, so the two kernels give the same bits
+  float l_part[2] = {0.f, 0.f};
   int n_exec = 0;
   f32x16 s[2][2];           // S^T of the tiles of parity 0 / 1, key blocks 0 / 1
   uint32_t pk[4][4];        // P^T operands of the pending tile
@@ -329,14 +330,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
           moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
         }
         pv_alpha = alpha;
-        l_part *= alpha;
+        l_part[0] *= alpha;
+        l_part[1] *= alpha;
 #pragma unroll
         for (int n = 0; n < 32; n += 2) {
           const int stp = n >> 3, e = n & 7;  // 16-key step, position inside it (P^T operand order)
           const float s0 = sprev[stp >> 1][8 * (stp & 1) + e], s1 = sprev[stp >> 1][8 * (stp & 1) + e + 1];
           if constexpr (POT) pk[stp][e >> 1] = pot_pack_bf16x2(s0, s1, c2, moff);
           else pk[stp][e >> 1] = pack_bf16x2(exp2_fast(fmaf(s0, c2, -moff)), exp2_fast(fmaf(s1, c2, -moff)));
-          l_part = dot2_bf16_sum(pk[stp][e >> 1], l_part);
+          l_part[(n >> 1) & 1] = dot2_bf16_sum(pk[stp][e >> 1], l_part[(n >> 1) & 1]);
         }
         pv_pending = true;
       }
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
 #undef V_BUF
 
   // ---- epilogue: O = acc / l, bf16
-  const float l_tot = pair_sum(l_part);
+  const float l_tot = pair_sum(l_part[0] + l_part[1]);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
     uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)iq * a.o_ss + (int64_t)h * a.o_sh;
