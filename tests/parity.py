@@ -337,8 +337,9 @@ def check_prefill(data, *, B, S, Hq, Hkv, d, causal, tau, tile_q, units=None, wh
                                    state=np.where(st[units] == 1, 1, 0), extra_band=extra)
         n_tie = int(tie.sum())
         assert within_abs_bar(got[tie], ref["out"][tie], bound[tie][:, None]), f"{where}: a near-tie row beyond its bound"
-        log(f"{where}: {n_tie} rows hold a near-tie log weight (largest bound {float(bound.max()):.3e}); "
-            f"the plain bar covers the others")
+        tie_err = float(np.abs(got[tie] - ref["out"][tie]).max()) if n_tie else 0.0
+        log(f"{where}: {n_tie} rows hold a near-tie log weight (their max error {tie_err:.3e}, largest bound "
+            f"{float(bound.max()):.3e}); the plain bar covers the others")
         got, ref = got[~tie], {**ref, "out": ref["out"][~tie]}
     max_abs, rel = errors(got, ref["out"])
     sparsity = skipped / max(vis, 1)

@@ -99,3 +99,16 @@ def test_pot_16k_sampled():
     units = [(0 * w.Hq + int(h)) * nqt + qt for h in heads for qt in qts]
     check_prefill(data, B=1, S=w.S, Hq=w.Hq, Hkv=w.Hkv, d=w.d, causal=True, tau=-LN1000, tile_q=128, units=units,
                   weights="rowmax_pot", where="pot 16k sampled")
+
+
+@pytest.mark.parametrize("tau", [-LN1000, -math.inf])
+def test_pot_128k_sampled(tau):
+    """Rowmax-PoT on the 128K benchmark workload in the launch configuration the benchmark times (at its tau and
+    with nothing skipped); the oracle checks sampled units including the first and the longest query tiles."""
+    w = synth.PREFILL_128K
+    data = synth.gen_prefill(w)
+    nqt = w.S // 128
+    units = np.array([0 * nqt + 0, 17 * nqt + 255, 40 * nqt + 777, 63 * nqt + nqt - 1])
+    r = check_prefill(data, B=1, S=w.S, Hq=w.Hq, Hkv=w.Hkv, d=w.d, causal=True, tau=tau, tile_q=128, units=units,
+                      weights="rowmax_pot", where=f"pot 128k tau={tau}")
+    assert r["sparsity"] >= 0.45 if tau > -math.inf else r["sparsity"] == 0.0
