@@ -324,7 +324,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     // the previous kept tile's V rows were loaded one chunk ago and arrived while this tile was scored
     // and voted on; its P.V goes in before this tile can rescale the accumulators
     if (pending) pv();
-    load_v(t, keep);
+    // bf16: every path issues the 16 V loads (see load_v); fp8: only a kept tile's, whose 16 eight-byte loads
+    // per wave cost more issue time than the exact wait counts save (5% at half the tiles kept, same-call A/B)
+    if constexpr (ES == 1) {
+      if (keep) load_v(t, true);
+    } else {
+      load_v(t, keep);
+    }
     pending = keep;
     if (keep) {
       ++n_exec;
