@@ -1,6 +1,6 @@
 """Seeded random shapes through every entry point against the fp64 oracle (GPU): batch, lengths, head counts,
 head size, query tile, causality, tau and split counts drawn from a fixed generator, small enough for the
-oracle to check every unit."""
+oracle to check every unit; every third prefill also with Rowmax-PoT weights."""
 import math
 
 import numpy as np
@@ -33,6 +33,10 @@ def test_prefill_random(case):
     if case % 2 == 0:
         check_prefill(data, B=B, S=S, Hq=hkv * g, Hkv=hkv, d=d, causal=causal, tau=tau, tile_q=tile_q,
                       fp8qk=synth.fp8_qk(data), where=f"random fp8qk prefill {case}")
+    if case % 3 == 0:  # Rowmax-PoT weights, on bf16 scores or (every other one) fp8 scores
+        check_prefill(data, B=B, S=S, Hq=hkv * g, Hkv=hkv, d=d, causal=causal, tau=tau, tile_q=tile_q,
+                      fp8qk=synth.fp8_qk(data) if case % 2 == 1 else None, weights="rowmax_pot",
+                      where=f"random pot prefill {case}")
 
 
 @pytest.mark.parametrize("case", range(30))
