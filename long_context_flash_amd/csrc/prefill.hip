@@ -590,7 +590,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked,
   if (grid == 0) return hipSuccess;
   if (chunked ? mode == 1 : (mode == 2 || mode == 3)) return hipErrorInvalidValue;
   if (chunked && a.pot) return hipErrorInvalidValue;
-  if (!chunked && mode == 0 && d == 128 && tile_q == 128 && a.G % 2 == 0) return launch_prefill_pp(a, stream);
+  if (!chunked && (mode == 0 || mode == 1) && d == 128 && tile_q == 128 && a.G % 2 == 0)
+    return launch_prefill_pp(a, mode == 1, stream);
   const dim3 blk(tile_q * 2);
 #define SSM_PREFILL_LAUNCH(D, TQ)                                                                                   \
   if (d == D && tile_q == TQ) {                                                                                     \

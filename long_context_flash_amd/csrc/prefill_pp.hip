@@ -5,7 +5,9 @@
 // Softmax): key tiles of 64 are scanned in ascending order; a tile whose score maximum trails the running
 // maximum by more than tau in every row of the unit skips its exponentials and its P*V product.
 //
-// Shape served: bf16, head_dim 128, query tiles of 128 rows, an even number of query heads per KV head.  One
+// Shape served: head_dim 128, query tiles of 128 rows, an even number of query heads per KV head; bf16 Q and K,
+// or (QK8) OCP e4m3 codes scored on v_mfma_f32_32x32x64_f8f6f4 as in prefill_kernel's QK8 form (K tiles as
+// 8-bit rows in LDS, 4 MFMAs per tile instead of 16); V and P.V are bf16 either way.  One
 // workgroup of 8 waves owns two units: query heads 2j and 2j+1 of one KV group on the same query tile, which
 // scan the same key tiles.  Waves 0-3 (group A) own unit A's rows, waves 4-7 (group B) unit B's, 32 rows per
 // wave; wave w runs on SIMD w % 4, so each SIMD holds one wave of each group.
@@ -48,10 +50,13 @@ constexpr int kCB = kD / 32;        // 32-channel blocks of the output
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // LDS layout of a tile (as prefill_kernel at D = 128): key row r holds 256 bytes; its 16-byte chunk c sits at
 // position c ^ swz(r).
 __device__ __forceinline__ int pp_swz_k(int r) { return r & 15; }
+// 8-bit K rows (128 bytes, QK8): chunk c of row r sits at position c ^ ((r >> 1) & 7)
+__device__ __forceinline__ int pp_swz_k8(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int pp_swz_v(int r) { return 4 * (r & 3); }
 
 // Barrier without a memory fence: LDS writes of this wave are complete (lgkmcnt(0)); outstanding tile loads
@@ -95,8 +100,12 @@ __device__ __forceinline__ void pp_map_unit(int bid, const PrefillArgs& a, int& 
 
 // POT: Rowmax-PoT weights 2^(rint(c2*S) - kref) in place of the exponentials (kref an integer reference that
 // trails the rounded row maximum by at most kRefSlackPP; the output and row sums are invariant to its choice).
-template <bool POT>
+// QK8: q and k hold e4m3 codes (strides count bytes); their scales are folded into the logit scale.
+template <bool POT, bool QK8>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
+  constexpr int ESK = QK8 ? 1 : 2;  // bytes per Q and K element
+  constexpr int KS8 = kD / 64;      // k-steps of the fp8 QK^T MFMA
+  constexpr int LK = QK8 ? 2 : 4;   // K tile loads per wave of group A
   __shared__ __attribute__((aligned(1024))) uint16_t k0[kTKpp * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t k1[kTKpp * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t k2[kTKpp * kD];
@@ -127,42 +136,60 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const int T_in = q_end < q0 + 128 ? 0 : min(T, a.causal ? min((q0 + 1) / kTKpp, full_tiles) : full_tiles);
   const float c2 = a.scale_log2;
 
-  auto qk_rows_bytes = [&](int n, int64_t ss) { return n <= 0 ? 0u : (uint32_t)(((int64_t)(n - 1) * ss + kD) * 2); };
-  const rsrc_t rq = make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh, qk_rows_bytes(S, a.q_ss));
-  const rsrc_t rk = make_rsrc(a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh, qk_rows_bytes(S, a.k_ss));
-  const rsrc_t rv = make_rsrc(a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh, qk_rows_bytes(S, a.v_ss));
+  auto qk_rows_bytes = [&](int n, int64_t ss, int es) {
+    return n <= 0 ? 0u : (uint32_t)(((int64_t)(n - 1) * ss + kD) * es);
+  };
+  const uint8_t* q8 = reinterpret_cast<const uint8_t*>(a.q);
+  const uint8_t* k8 = reinterpret_cast<const uint8_t*>(a.k);
+  const rsrc_t rq = make_rsrc(q8 + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ESK, qk_rows_bytes(S, a.q_ss, ESK));
+  const rsrc_t rk = make_rsrc(k8 + ((int64_t)b * a.k_sb + (int64_t)g * a.k_sh) * ESK, qk_rows_bytes(S, a.k_ss, ESK));
+  const rsrc_t rv = make_rsrc(a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh, qk_rows_bytes(S, a.v_ss, 2));
 
-  // ---- Q operand: lane (col, half) holds Q[row][ks*16 + half*8 .. +8]
+  // ---- Q operand: lane (col, half) holds Q[row][ks*16 + half*8 .. +8] (QK8: the 32 codes Q[row][ks*64 +
+  // half*32 .. +32])
   const int iq = q0 + wl * 32 + col;
   const bool row_ok = iq < S;
-  bf16x8 qreg[kKS];
+  bf16x8 qreg[QK8 ? 1 : kKS];
+  i32x8 qreg8[QK8 ? KS8 : 1];
   {
-    const uint32_t qoff = row_ok ? (uint32_t)iq * (uint32_t)(a.q_ss * 2) + half * 16 : 0xffffffffu;
+    const uint32_t qoff = row_ok ? (uint32_t)iq * (uint32_t)(a.q_ss * ESK) + half * (QK8 ? 32 : 16) : 0xffffffffu;
+    if constexpr (QK8) {
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) qreg[ks] = as_bf16x8(buffer_load_16(rq, row_ok ? qoff + ks * 32 : qoff));
+      for (int ks = 0; ks < KS8; ++ks) {
+        const u32x4 lo = buffer_load_16(rq, row_ok ? qoff + ks * 64 : qoff);
+        const u32x4 hi = buffer_load_16(rq, row_ok ? qoff + ks * 64 + 16 : qoff);
+        qreg8[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) qreg[ks] = as_bf16x8(buffer_load_16(rq, row_ok ? qoff + ks * 32 : qoff));
+    }
   }
 
   // ---- tile loads straight into LDS.  The four waves of a group fill one 16 KB tile: load i of wave wl fills
   // LDS bytes [(wl*4 + i) KB, +1 KB), i.e. key rows 4(wl*4 + i) .. +3; lane l the 16 bytes at l*16 of it
   // (row 4(wl*4+i) + l/16, chunk position l%16, which holds the logical chunk (l%16) ^ swz(row)).
   const int lrow = lane >> 4, lpos = lane & 15;
-  const uint32_t k_row_bytes = (uint32_t)(a.k_ss * 2), v_row_bytes = (uint32_t)(a.v_ss * 2);
+  const uint32_t k_row_bytes = (uint32_t)(a.k_ss * ESK), v_row_bytes = (uint32_t)(a.v_ss * 2);
   const uint32_t k_tile_bytes = kTKpp * k_row_bytes, v_tile_bytes = kTKpp * v_row_bytes;
-  // K: swz_k(row) = row & 15 = (4(wl*4+i)) & 15 | lrow -> chunk = lpos ^ lrow ^ (that load's part)
-  uint32_t k_dma = (uint32_t)(wl * 16 + lrow) * k_row_bytes;
-  uint32_t k_dmx = (uint32_t)(lpos ^ pp_swz_k(lrow)) * 16;
+  // K: swz_k(row) = row & 15 = (4(wl*4+i)) & 15 | lrow -> chunk = lpos ^ lrow ^ (that load's part).  QK8: the
+  // 8 KB tile in 2 loads per wave, load i of wave wl holding rows 16wl + 8i + lane/8, chunk position lane%8;
+  // swz_k8(row) = (4(i & 1)) | (lane >> 4), so chunk = (lane%8) ^ (lane >> 4) ^ 4(i & 1)
+  uint32_t k_dma = QK8 ? (uint32_t)(wl * 16 + (lane >> 3)) * k_row_bytes : (uint32_t)(wl * 16 + lrow) * k_row_bytes;
+  uint32_t k_dmx = QK8 ? (uint32_t)((lane & 7) ^ (lane >> 4)) * 16 : (uint32_t)(lpos ^ pp_swz_k(lrow)) * 16;
   // V: swz_v(row) = 4 (row & 3) = 4 lrow: no load-index part
   uint32_t v_dma = (uint32_t)(wl * 16 + lrow) * v_row_bytes + (uint32_t)(lpos ^ pp_swz_v(lrow)) * 16;
   // this wave's part of a tile buffer (key rows 16 wl .. 16 wl + 15) starts wl * 4 KB in; an opaque copy per call keeps the compiler from
   // holding every buffer's destination addresses in scalar registers across the loop
   auto load_k = [&](uint16_t* dst, int t) {
     const uint32_t toff = (uint32_t)t * k_tile_bytes;
-    int wofs = wl * 4096;
+    int wofs = wl * LK * 1024;
     asm volatile("" : "+s"(wofs));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t cx = (uint32_t)pp_swz_k((wl * 4 + i) * 4) * 16;  // wave-uniform
-      const uint32_t vo = k_dma + (k_dmx ^ cx) + (uint32_t)(i * 4) * k_row_bytes + toff;
+    for (int i = 0; i < LK; ++i) {
+      // wave-uniform part of the swizzle
+      const uint32_t cx = QK8 ? (uint32_t)(4 * (i & 1)) * 16 : (uint32_t)pp_swz_k((wl * 4 + i) * 4) * 16;
+      const uint32_t vo = k_dma + (k_dmx ^ cx) + (uint32_t)(i * (QK8 ? 8 : 4)) * k_row_bytes + toff;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)((char*)dst + wofs + i * 1024), 16, vo, 0, 0, 0);
     }
   };
@@ -180,8 +207,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   // ---- operand reads (prefill_kernel's bf16 forms at D = 128)
   // K (S^T's A operand): lane (col, half) reads row kb*32 + col, logical chunk 2ks + half:
   // byte (kb*32 + col)*256 + 16*((2ks + half) ^ (col & 15)) = (k_opb ^ 32 ks) + kb*32*256
-  const int xk = col & 15;
-  uint32_t k_opb = (uint32_t)(col * kRowB + 32 * (xk >> 1) + 16 * (half ^ (xk & 1)));
+  // QK8: lane (col, half) reads row kb*32 + col, logical chunks 4ks + 2half and 4ks + 2half + 1 (32 codes):
+  // bytes (kb*32 + col)*128 + 16*((4ks + 2half + j) ^ swz_k8(col)) = (k_opb ^ 16*(4ks + j)) + kb*32*128
+  const int xk = QK8 ? pp_swz_k8(col) : (col & 15);
+  uint32_t k_opb = QK8 ? (uint32_t)(col * kD + 16 * ((2 * half) ^ xk))
+                       : (uint32_t)(col * kRowB + 32 * (xk >> 1) + 16 * (half ^ (xk & 1)));
   // V^T (O^T's A operand) by transposing reads: in each 16-lane group, lane 4j + m names channels 4m..4m+3 of
   // the group's 16 and key row k0 + j, and receives channel (lane & 15) of the 4 rows
   const int gq = lane >> 4, li = lane & 15;
@@ -190,6 +220,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   uint32_t v_opb = (uint32_t)(vrow * kRowB + 64 * (pp_swz_v(vrow) >> 2) + 16 * (vch >> 3) + 2 * (vch & 7));
   auto kop = [&](const uint16_t* kl, int ks, int kb) {
     return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kl) + ((k_opb ^ (32u * ks)) + kb * 32 * kRowB));
+  };
+  auto kop8 = [&](const uint16_t* kl, int ks, int kb) {
+    const char* base = reinterpret_cast<const char*>(kl) + kb * 32 * kD;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + (k_opb ^ (64u * ks)));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (k_opb ^ (64u * ks + 16u)));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   auto vop = [&](const uint16_t* vl, int cb, int st) {
     // half hf of the S^T accumulator holds keys 4hf..4hf+3 and 8+4hf..8+4hf+3 of each 16-key step
@@ -220,6 +256,19 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
 
   // S^T(t) = K(t) Q^T: two independent chains (key blocks), operands read two MFMAs ahead
   auto qk = [&](const uint16_t* kl, f32x16 (&st)[2]) {
+    if constexpr (QK8) {
+      constexpr int NM = 2 * KS8;
+      i32x8 x[NM];
+#pragma unroll
+      for (int j = 0; j < NM; ++j) x[j] = kop8(kl, j >> 1, j & 1);
+#pragma unroll
+      for (int j = 0; j < NM; ++j) {
+        const int ks = j >> 1, kb = j & 1;
+        st[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x[j], qreg8[ks], ks == 0 ? f32x16{} : st[kb], 0, 0, 0,
+                                                                 0, 0, 0);
+      }
+      return;
+    }
     constexpr int NM = 2 * kKS;
     u32x4 x[NM];
     x[0] = kop(kl, 0, 0);
@@ -361,8 +410,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // this wave's loads of the tile the barrier ending the phase publishes have landed.  Group A: K(t+1) (issued
     // in G(t-2); K(t+2), K(t+3) may stay in flight).  Group B: V(t) (issued in G(t-1); V(t+1) may stay in flight).
     if (grp == 0) {
-      if (t + 3 < T) pp_wait_vmem<8>();
-      else if (t + 2 < T) pp_wait_vmem<4>();
+      if (t + 3 < T) pp_wait_vmem<2 * LK>();
+      else if (t + 2 < T) pp_wait_vmem<LK>();
       else pp_wait_vmem<0>();
     } else {
       if (t + 1 < T) pp_wait_vmem<4>();
@@ -456,12 +505,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   }
 }
 
-hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_pp(const PrefillArgs& a, bool qk8, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.B * (a.Hq / 2) * a.nqt);
   if (grid == 0) return hipSuccess;
   if (a.G % 2 != 0) return hipErrorInvalidValue;
-  if (a.pot) hipLaunchKernelGGL(prefill_pp_kernel<true>, dim3(grid), dim3(512), 0, stream, a);
-  else hipLaunchKernelGGL(prefill_pp_kernel<false>, dim3(grid), dim3(512), 0, stream, a);
+  if (qk8 && a.pot) hipLaunchKernelGGL((prefill_pp_kernel<true, true>), dim3(grid), dim3(512), 0, stream, a);
+  else if (qk8) hipLaunchKernelGGL((prefill_pp_kernel<false, true>), dim3(grid), dim3(512), 0, stream, a);
+  else if (a.pot) hipLaunchKernelGGL((prefill_pp_kernel<true, false>), dim3(grid), dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL((prefill_pp_kernel<false, false>), dim3(grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

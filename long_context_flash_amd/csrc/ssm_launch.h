@@ -72,9 +72,9 @@ struct DecodeArgs {
 // mode 0: bf16; 1: e4m3 q/k scores (contiguous only); 2: e4m3 K/V pages (chunked only); 3: e4m3 queries
 // scored against e4m3 K pages, e4m3 V pages (chunked only)
 hipError_t launch_prefill(const PrefillArgs& a, int d, int tile_q, bool chunked, int mode, hipStream_t stream);
-// bf16, d = 128, tile_q = 128, contiguous, an even number of query heads per KV head: two units per workgroup in
-// ping-pong (prefill_pp.hip)
-hipError_t launch_prefill_pp(const PrefillArgs& a, hipStream_t stream);
+// d = 128, tile_q = 128, contiguous, an even number of query heads per KV head, bf16 or (qk8) e4m3 Q and K: two
+// units per workgroup in ping-pong (prefill_pp.hip)
+hipError_t launch_prefill_pp(const PrefillArgs& a, bool qk8, hipStream_t stream);
 constexpr int kDecSortMax = 8192;  // batches up to this size are dispatched longest sequence first
 // size of the static device array that serves as ssm_decode_noalloc's workspace (one per GPU)
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;

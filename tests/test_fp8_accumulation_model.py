@@ -47,9 +47,9 @@ def e4m3(x):
     return t
 
 
-@pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("tile_q", [64, 128])
-def test_unit_gaps_follow_the_accumulation_rule(d, tile_q):
+@pytest.mark.parametrize("d,tile_q,Hq", [(64, 64, 1), (64, 128, 1), (128, 64, 1), (128, 128, 1), (128, 128, 2)])
+def test_unit_gaps_follow_the_accumulation_rule(d, tile_q, Hq):
+    """Hq = 2 (two query heads on one KV head) runs the paired-head kernel, the others the general one."""
     assert FP8_GROUP == 8
     tiles = TILES + (TILES_D128 if d == 128 else [])
     T = len(tiles)
@@ -60,14 +60,14 @@ def test_unit_gaps_follow_the_accumulation_rule(d, tile_q):
     for t, (_, chans) in enumerate(tiles):
         for c, x in chans.items():
             keys[t, c] = x
-    q = np.broadcast_to(qv, (1, S, 1, d)).copy()
+    q = np.broadcast_to(qv, (1, S, Hq, d)).copy()
     k = np.repeat(keys, 64, axis=0)[None, :, None, :]
     dev = "cuda"
     q8, k8 = e4m3(q).to(dev), e4m3(k).to(dev)
     v = torch.ones((1, S, 1, d), dtype=torch.bfloat16, device=dev)
-    units, nkt = ssm.prefill_stats_shape(1, S, 1, tile_q)
+    units, nkt = ssm.prefill_stats_shape(1, S, Hq, tile_q)
     stats = ssm.SkipStats.alloc(units, nkt, dev, gaps=True)
-    log(f"fp8 accumulation model: d={d} tile_q={tile_q} tiles={T}")
+    log(f"fp8 accumulation model: d={d} tile_q={tile_q} Hq={Hq} tiles={T}")
     ssm.ssm_prefill_fp8qk(q8, 1.0, k8, 1.0, v, causal=False, tau=-math.inf, skip_stats=stats, tile_q=tile_q,
                           scale=SCALE)
     torch.cuda.synchronize()
