@@ -27,7 +27,10 @@
 //   bf16 in place.  For the V^T operand each lane loads 8 keys x 8 channels
 //   (eight 16-byte rows) and transposes them in registers; MFMA j uses channel
 //   j of each loaded chunk, so its 16 output rows are channels 8m + j.
-//   V is loaded only after the vote keeps the tile.
+//   V is loaded only after the vote keeps the tile (a skipped tile's loads read an
+//   empty buffer resource: no memory traffic), with the non-temporal cache policy:
+//   its rows are read whole and once, and must not evict the K lines that each
+//   K load instruction leaves half-read for the next one.
 //
 // FP8 cache (optional): K and V stored as OCP e4m3 codes with one dequantisation
 // scale per tensor.  Half the bytes of a bf16 cache are read; each code is
@@ -393,8 +396,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a, int 
     a.part_o[(part_row + (int64_t)q * P) * D + ch] = ok ? o / lsum * a.v_scale : 0.f;
     if (ch == 0) a.part_lse[part_row + (int64_t)q * P] = ok ? mstar * a.scale_log2 + __builtin_log2f(lsum) : neg_inf();
   }
-  // skip counts: this workgroup's totals into its workspace slot (the combine adds them up per KV group, so the
-  // four global counters take B * Hkv sets of atomics instead of one per workgroup)
+  // skip counts: this workgroup's totals into its workspace slot (the combine adds them up per sequence, so the
+  // four global counters take one set of atomics per sequence instead of one per workgroup)
   if (a.counters) {
     if (lane == 0) {
       cnt_lds[w][0] = n_vis;
