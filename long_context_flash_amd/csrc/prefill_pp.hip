@@ -28,7 +28,7 @@
 // barriers that follow and read behind the MFMAs at the end of G(t+1), so the decision in V(t+1) waits for
 // nothing.
 //
-// The two units share every K and V tile in LDS (4 buffers each, 16 KB per tile).  Group A's waves load the
+// The two units share every K and V tile in LDS (4 buffers each, 16 KB per tile; 8 KB per 8-bit K tile).  Group A's waves load the
 // K tiles (K(t+3) behind the MFMAs of G(t)), group B's waves the V tiles (V(t+1) behind those of G(t); every
 // visited tile, since either unit may keep it); a wave waits for its loads of a tile in the vector phase whose
 // closing barrier publishes it (K(t+1) in V_A(t), V(t) in V_B(t)).  Tiles go HBM/L2 -> LDS with direct-to-LDS
@@ -179,8 +179,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   uint32_t k_dmx = QK8 ? (uint32_t)((lane & 7) ^ (lane >> 4)) * 16 : (uint32_t)(lpos ^ pp_swz_k(lrow)) * 16;
   // V: swz_v(row) = 4 (row & 3) = 4 lrow: no load-index part
   uint32_t v_dma = (uint32_t)(wl * 16 + lrow) * v_row_bytes + (uint32_t)(lpos ^ pp_swz_v(lrow)) * 16;
-  // this wave's part of a tile buffer (key rows 16 wl .. 16 wl + 15) starts wl * 4 KB in; an opaque copy per call keeps the compiler from
-  // holding every buffer's destination addresses in scalar registers across the loop
+  // this wave's part of a tile buffer (key rows 16 wl .. 16 wl + 15) starts wl * LK KB in (4 KB of bf16 rows,
+  // 2 KB of 8-bit rows); an opaque copy per call keeps the compiler from holding every buffer's destination
+  // addresses in scalar registers across the loop
   auto load_k = [&](uint16_t* dst, int t) {
     const uint32_t toff = (uint32_t)t * k_tile_bytes;
     int wofs = wl * LK * 1024;
