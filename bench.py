@@ -166,6 +166,111 @@ def build_ceiling_programs():
         os.replace(exe + ".tmp", exe)
 
 
+def gpu_sysfs_dir(torch=None):
+    """The sysfs device directory of cuda:0 that holds a hwmon power reading: matched by PCI address when torch
+    reports it, else the only such GPU on the host; None if there is none (or no way to tell which)."""
+    import glob
+    cands = [d for d in sorted(glob.glob("/sys/class/drm/card*/device"))
+             if glob.glob(os.path.join(d, "hwmon", "hwmon*", "power1_input"))]
+    if torch is not None and cands:
+        p = torch.cuda.get_device_properties(0)
+        bus = getattr(p, "pci_bus_id", None)
+        if bus is not None:
+            for d in cands:
+                addr = os.path.basename(os.path.realpath(d))  # domain:bus:device.function
+                parts = addr.replace(".", ":").split(":")
+                if len(parts) == 4 and int(parts[1], 16) == bus and \
+                        int(parts[2], 16) == getattr(p, "pci_device_id", int(parts[2], 16)):
+                    return d
+    return cands[0] if len(cands) == 1 else None
+
+
+class BoardSampler:
+    """Board power and graphics clock of one GPU, read from sysfs on a host thread every `period` s while
+    running: hwmon power1_input (socket power, microwatts; power1_cap is the limit the board holds it to) and
+    the current level of pp_dpm_sclk (MHz), each sample stamped with time.monotonic()."""
+
+    def __init__(self, dev_dir, period=0.01):
+        import glob
+        import threading
+        self.hwmon = glob.glob(os.path.join(dev_dir, "hwmon", "hwmon*"))[0] if dev_dir else None
+        self.sclk = os.path.join(dev_dir, "pp_dpm_sclk") if dev_dir else None
+        self.period = period
+        self.samples = []  # (t, watts, mhz or None)
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    def cap_w(self):
+        v = self._read(os.path.join(self.hwmon, "power1_cap")) if self.hwmon else None
+        return int(v) / 1e6 if v else None
+
+    def _clock(self):
+        text = self._read(self.sclk) if self.sclk else None
+        for line in (text or "").splitlines():
+            if line.rstrip().endswith("*"):
+                digits = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit())
+                return int(digits) if digits else None
+        return None
+
+    def _run(self):
+        pin = os.path.join(self.hwmon, "power1_input")
+        while not self._stop.is_set():
+            v = self._read(pin)
+            if v:
+                self.samples.append((time.monotonic(), int(v) / 1e6, self._clock()))
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.hwmon:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.hwmon:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self, t0=None, t1=None):
+        """Mean and largest power, mean clock and the limit over the samples in [t0, t1]; None without samples."""
+        sel = [x for x in self.samples if (t0 is None or x[0] >= t0) and (t1 is None or x[0] <= t1)]
+        if not sel:
+            return None
+        w = [x[1] for x in sel]
+        mhz = [x[2] for x in sel if x[2] is not None]
+        return {"mean_w": round(sum(w) / len(w), 1), "max_w": round(max(w), 1), "cap_w": self.cap_w(),
+                "sclk_mean_mhz": round(sum(mhz) / len(mhz)) if mhz else None, "samples": len(sel),
+                "distinct_power_values": len(set(w))}
+
+
+def mfma_power(seconds):
+    """Run mfma_ceiling in its sustained form beside a BoardSampler and print, per phase (idle, zero operands,
+    idle, random operands), the MFMA rate with the board's power and clock over the phase's last three quarters."""
+    exe = os.path.join(CEILING_DIR, "mfma_ceiling")
+    if not os.path.exists(exe):
+        sys.exit(f"{exe} is missing: build it with `python -c 'import bench; bench.build_ceiling_programs()'`")
+    dev_dir = gpu_sysfs_dir()
+    if dev_dir is None:
+        sys.exit("no hwmon power reading found for the GPU")
+    with BoardSampler(dev_dir) as smp:
+        r = subprocess.run([exe, "20000", "sustain", str(seconds)], capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.exit(f"mfma_ceiling failed ({r.returncode}): {r.stderr}")
+    rec = json.loads(r.stdout)
+    for ph in rec["phases"]:
+        lo = ph["t0"] + 0.25 * (ph["t1"] - ph["t0"])
+        ph["board"] = smp.summary(lo, ph["t1"])
+    rec["sysfs"] = dev_dir
+    print(json.dumps(rec), flush=True)
+
+
 def prefill_flops(w, visited, kept):
     dense = 4.0 * w.B * w.Hq * w.d * (w.S * (w.S + 1) / 2 if w.causal else w.S * w.S)
     per_tile = 2.0 * w.tile_q * w.tile_k * w.d
@@ -288,13 +393,18 @@ def time_prefill_vs_dense(ssm, torch, np, w, q, k, v, out, skip_ms, sparsity, st
     the speedup skipping buys on this input, the quantity the Skip Softmax pages report (as context: 1.4x for
     prefill of Llama 3.3 70B at 128K on GB200)."""
     cnt = torch.zeros(4, dtype=torch.int64, device=dev)
-    ms = _timed(torch, np, lambda: ssm.ssm_prefill(q, k, v, causal=True, tau=-math.inf, out=out,
-                                                   skip_stats=ssm.SkipStats(counters=cnt), tile_q=w.tile_q), steps)
+    with BoardSampler(gpu_sysfs_dir(torch)) as board:
+        ms = _timed(torch, np, lambda: ssm.ssm_prefill(q, k, v, causal=True, tau=-math.inf, out=out,
+                                                       skip_stats=ssm.SkipStats(counters=cnt), tile_q=w.tile_q),
+                    steps)
     c = cnt.cpu().numpy()
     if int(c[1]) != 0:
         raise RuntimeError("tau = -inf skipped tiles")
-    return {"dense_ms": round(ms, 3), "skip_ms": skip_ms, "skip_sparsity": sparsity,
-            "speedup_vs_dense": round(ms / skip_ms, 3), "pages_prefill_speedup": 1.4}
+    res = {"dense_ms": round(ms, 3), "skip_ms": skip_ms, "skip_sparsity": sparsity,
+           "speedup_vs_dense": round(ms / skip_ms, 3), "pages_prefill_speedup": 1.4}
+    if board.summary() is not None:
+        res["board_power"] = board.summary()
+    return res
 
 
 def time_pot_prefill(ssm, torch, np, w, q, k, v, out, tau, exp_ms, exp_dense_ms, steps, dev):
@@ -851,12 +961,18 @@ def main():
     ap.add_argument("--traffic-command", default="", help="command line recorded with --summarize-traffic")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="run the standalone MFMA-rate program (zero vs random bf16 operands), print its JSON and exit")
+    ap.add_argument("--mfma-power", type=float, default=None, metavar="SECONDS",
+                    help="run the MFMA-rate program in its sustained form (idle / zero / idle / random operands, "
+                         "SECONDS each) beside a board power and clock sampler, print the JSON and exit")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="run the standalone HBM streaming-read program (the decode's load shapes), print its JSON "
                          "and exit")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.traffic_command)
+        return
+    if args.mfma_power is not None:
+        mfma_power(args.mfma_power)
         return
     if args.mfma_ceiling or args.read_ceiling:
         exe = os.path.join(CEILING_DIR, "mfma_ceiling" if args.mfma_ceiling else "read_ceiling")
@@ -933,11 +1049,12 @@ def main():
     ev = mk(args.steps)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, ev)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with BoardSampler(gpu_sysfs_dir(torch)) as board:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     p_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     d_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
     step_ms = wall * 1e3 / args.steps
@@ -1058,6 +1175,12 @@ def main():
         res["prefill_16k"] = leg_prefill_16k(ssm, torch, np, args.steps, dev, cpu_threads,
                                              cpu=not args.no_cpu_baseline)
     res["config"] = cfg
+    bp = board.summary()
+    if bp is not None:
+        # almost all of a step's time is the prefill (the decode is under 1% of it)
+        bp["what"] = "board power (hwmon power1_input) and graphics clock (pp_dpm_sclk) sampled every 10 ms " \
+                     "over the timed steps"
+        res["board_power"] = bp
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -7,6 +7,10 @@
 // rate of v_fma_f32 and of v_exp_f32 (the exponential of the softmax step) followed by an add, and reports
 // how many fma issue slots one exponential with its add takes.
 //   mfma_ceiling [iterations]
+//   mfma_ceiling [iterations] sustain SECONDS
+// The second form holds each bf16 operand set (none: the GPU idle, then zero, then random operands) for
+// SECONDS, launching the MFMA loop back to back, and prints for each phase its CLOCK_MONOTONIC interval and
+// its rate, so that a sampler of the board's power reading running beside it can attribute its samples.
 //
 // Each of 512 workgroups (two per compute unit, four waves each, i.e. two waves per SIMD, the occupancy
 // of the prefill kernel) reads its 16 operand registers per lane once and then issues only MFMAs on four
@@ -17,6 +21,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <ctime>
+#include <unistd.h>
 #include <vector>
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -232,8 +238,42 @@ uint64_t splitmix64(uint64_t& s) {
 
 }  // namespace
 
+double now_monotonic() {
+  timespec ts;
+  clock_gettime(CLOCK_MONOTONIC, &ts);
+  return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
+}
+
+// one phase of the sustained form: the MFMA loop over `src` launched back to back for `seconds` (src null: the
+// GPU left idle); prints the phase's interval and rate as one JSON object
+void sustain_phase(const char* name, const u32x4* src, float* out, int iters, double seconds, bool first) {
+  CHECK(hipDeviceSynchronize());
+  const double t0 = now_monotonic();
+  double flop = 0.0;
+  if (src == nullptr) {
+    usleep((useconds_t)(seconds * 1e6));
+  } else {
+    const double per_launch = (double)kGrid * kThreads / 64 * iters * kMfmaPerIter * kFlopPerMfma;
+    while (now_monotonic() - t0 < seconds) {
+      for (int i = 0; i < 4; ++i) hipLaunchKernelGGL(mfma_loop, dim3(kGrid), dim3(kThreads), 0, 0, src, out, iters);
+      CHECK(hipGetLastError());
+      CHECK(hipDeviceSynchronize());
+      flop += 4 * per_launch;
+    }
+  }
+  const double t1 = now_monotonic();
+  std::printf("%s{\"operands\": \"%s\", \"t0\": %.4f, \"t1\": %.4f, \"tflops\": %.1f}", first ? "" : ", ", name, t0,
+              t1, flop / (t1 - t0) / 1e12);
+}
+
 int main(int argc, char** argv) {
   const int iters = argc > 1 ? std::atoi(argv[1]) : 20000;
+  const bool sustain = argc > 3 && std::strcmp(argv[2], "sustain") == 0;
+  const double seconds = sustain ? std::atof(argv[3]) : 0.0;
+  if (iters <= 0 || (argc > 2 && !(sustain && seconds > 0.0 && seconds <= 60.0))) {
+    std::fprintf(stderr, "usage: mfma_ceiling [iterations > 0] [sustain SECONDS (0, 60]]\n");
+    return 2;
+  }
   const size_t n = (size_t)kGrid * kThreads * kOps;  // u32x4 elements
   // random operands: bf16 of values uniform in [-2, 2)
   std::vector<uint32_t> host(n * 4);
@@ -269,6 +309,20 @@ int main(int argc, char** argv) {
   CHECK(hipMalloc(&out, (size_t)(kGrid > kValuGrid ? kGrid : kValuGrid) * kThreads * sizeof(float)));
   CHECK(hipMemset(zero, 0, n * sizeof(u32x4)));
   CHECK(hipMemcpy(rnd, host.data(), n * sizeof(u32x4), hipMemcpyHostToDevice));
+  if (sustain) {
+    std::printf("{\"instruction\": \"v_mfma_f32_32x32x16_bf16\", \"mode\": \"sustain\", \"iterations\": %d, "
+                "\"seconds\": %.1f, \"clock\": \"CLOCK_MONOTONIC\", \"phases\": [", iters, seconds);
+    sustain_phase("idle", nullptr, out, iters, seconds, true);
+    sustain_phase("zero", zero, out, iters, seconds, false);
+    sustain_phase("idle", nullptr, out, iters, seconds, false);
+    sustain_phase("random", rnd, out, iters, seconds, false);
+    std::printf("]}\n");
+    CHECK(hipFree(zero));
+    CHECK(hipFree(rnd));
+    CHECK(hipFree(rnd8));
+    CHECK(hipFree(out));
+    return 0;
+  }
   double z = 0, r = 0, z8 = 0, r8 = 0;
   for (int rep = 0; rep < 2; ++rep) {  // the better of two runs each
     const double rz = rate(zero, out, iters), rr = rate(rnd, out, iters);
