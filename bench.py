@@ -251,8 +251,10 @@ class BoardSampler:
 
 
 def mfma_power(seconds):
-    """Run mfma_ceiling in its sustained form beside a BoardSampler and print, per phase (idle, zero operands,
-    idle, random operands), the MFMA rate with the board's power and clock over the phase's last three quarters."""
+    """Run mfma_ceiling in its sustained form beside a BoardSampler and print, per phase (idle; zero and random
+    operands; random operands with LDS operand reads, VALU work, tile loads, all three), the MFMA rate with the
+    board's power and clock over the phase's last three quarters, and the energy above idle per wave-iteration
+    (16 MFMAs of one wave with that phase's other work) and per executed FLOP."""
     exe = os.path.join(CEILING_DIR, "mfma_ceiling")
     if not os.path.exists(exe):
         sys.exit(f"{exe} is missing: build it with `python -c 'import bench; bench.build_ceiling_programs()'`")
@@ -267,6 +269,21 @@ def mfma_power(seconds):
     for ph in rec["phases"]:
         lo = ph["t0"] + 0.25 * (ph["t1"] - ph["t0"])
         ph["board"] = smp.summary(lo, ph["t1"])
+    # the idle baseline: the idle phases between work phases (the first one may find the GPU in a deeper sleep)
+    idle = [ph["board"]["mean_w"] for ph in rec["phases"][1:] if ph["phase"] == "idle" and ph["board"]]
+    if idle:
+        rec["idle_w"] = round(sum(idle) / len(idle), 1)
+        base = None
+        for ph in rec["phases"]:
+            if ph["phase"] == "idle" or not ph["board"]:
+                continue
+            above = ph["board"]["mean_w"] - rec["idle_w"]
+            ph["nj_per_wave_iter"] = round(above / ph["wave_iters_per_s"] * 1e9, 1)
+            ph["pj_per_flop"] = round(above / (ph["tflops"] * 1e12) * 1e12, 4)
+            if ph["phase"] == "random":
+                base = ph["nj_per_wave_iter"]
+            elif base is not None and ph["phase"].startswith("random+"):
+                ph["nj_over_random"] = round(ph["nj_per_wave_iter"] - base, 1)
     rec["sysfs"] = dev_dir
     print(json.dumps(rec), flush=True)
 

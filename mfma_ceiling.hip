@@ -8,9 +8,14 @@
 // how many fma issue slots one exponential with its add takes.
 //   mfma_ceiling [iterations]
 //   mfma_ceiling [iterations] sustain SECONDS
-// The second form holds each bf16 operand set (none: the GPU idle, then zero, then random operands) for
-// SECONDS, launching the MFMA loop back to back, and prints for each phase its CLOCK_MONOTONIC interval and
-// its rate, so that a sampler of the board's power reading running beside it can attribute its samples.
+// The second form holds each phase for SECONDS, launching its loop back to back, and prints for each its
+// CLOCK_MONOTONIC interval and its rate, so that a sampler of the board's power reading running beside it can
+// attribute its samples: the GPU idle, the MFMA loop on zero and on random operands, and the random-operand
+// loop with, per 16 MFMAs of a wave, the other kinds of work an attention kernel adds (an idle phase before
+// each): the A operand of every MFMA read from LDS (16 ds_read_b128, 16 KB, as the prefill reads its K and V
+// operands); 16 v_exp_f32 with 16 adds and 48 fmas that do not depend on the MFMAs (about the prefill's VALU
+// work per 16 MFMAs); two 1 KB direct-to-LDS buffer loads from a 4 MB buffer that stays in L2 (the prefill's
+// tile loads per 16 MFMAs); and all three together.
 //
 // Each of 512 workgroups (two per compute unit, four waves each, i.e. two waves per SIMD, the occupancy
 // of the prefill kernel) reads its 16 operand registers per lane once and then issues only MFMAs on four
@@ -29,6 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 namespace {
 
@@ -61,6 +67,80 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_loop(const u32x4* __restrict
 #pragma unroll
     for (int i = 0; i < 16; ++i) r += acc[c][i];
   out[tid] = r;
+}
+
+// The sustained form's loop: the MFMA stream of mfma_loop (random operands) plus, per 16 MFMAs, the work that
+// MIX selects: bit 0 the A operand of every MFMA from LDS (random operand data staged there at the start, 64 KB
+// per workgroup), bit 1 independent VALU work (16 v_exp_f32 + 16 v_add_f32 + 48 v_fma_f32), bit 2 two 1 KB
+// direct-to-LDS buffer loads per wave from the first kL2Bytes of `l2src` (a range that stays in the L2
+// caches), waited for two iterations later.
+constexpr int kLdsOps = 4096;            // u32x4 of operand data in LDS
+constexpr uint32_t kL2Bytes = 4u << 20;  // bytes of l2src the loads sweep
+static_assert((size_t)kGrid * kLdsOps <= (size_t)kGrid * kThreads * kOps, "LDS staging reads stay inside src");
+static_assert((size_t)kL2Bytes <= (size_t)kGrid * kThreads * kOps * 16, "the loads stay inside l2src");
+template <int MIX>
+__global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict__ src, const uint8_t* __restrict__ l2src,
+                                                        float* __restrict__ out, int iters) {
+  __shared__ u32x4 lds[kLdsOps];
+  __shared__ u32x4 dma_dst[kThreads / 64][2][64];
+  const int tid = blockIdx.x * kThreads + threadIdx.x, lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr ((MIX & 1) != 0) {
+    // kGrid * kLdsOps <= kGrid * kThreads * kOps: every workgroup's slice lies inside src
+    for (int i = threadIdx.x; i < kLdsOps; i += kThreads) lds[i] = src[(size_t)blockIdx.x * kLdsOps + i];
+    __syncthreads();
+  }
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = src[(size_t)tid * kOps + i];
+    b[i] = src[(size_t)tid * kOps + 8 + i];
+  }
+  float va[8], vb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) va[i] = vb[i] = (float)(lane + i) * 1e-6f - 1.0f;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)l2src, (short)0, (int)kL2Bytes, 0x00020000);
+  const uint32_t gw = (uint32_t)(blockIdx.x * (kThreads / 64) + w);
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  for (int it = 0; it < iters; ++it) {
+    if constexpr ((MIX & 4) != 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // a 1 KB-aligned slot below kL2Bytes; lane l writes its 16 bytes at slot + 16 l
+        const uint32_t off = (((uint32_t)(it * 2 + i) * (kGrid * kThreads / 64) + gw) * 1024u) & (kL2Bytes - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)&dma_dst[w][i][0], 16, off + lane * 16, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 a1 = a[j], a2 = a[(j + 3) & 7];
+      if constexpr ((MIX & 1) != 0) {
+        a1 = lds[((it * 16 + 2 * j) * 64 + w * 1024 + lane) & (kLdsOps - 1)];
+        a2 = lds[((it * 16 + 2 * j + 1) * 64 + w * 1024 + lane) & (kLdsOps - 1)];
+      }
+      acc[(2 * j) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[j]),
+                                                                 acc[(2 * j) & 3], 0, 0, 0);
+      acc[(2 * j + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, b[j]),
+                                                                     acc[(2 * j + 1) & 3], 0, 0, 0);
+      if constexpr ((MIX & 2) != 0) {
+        va[j] = __builtin_amdgcn_exp2f(va[j]) - 1.5f;
+        va[(j + 4) & 7] = __builtin_amdgcn_exp2f(va[(j + 4) & 7]) - 1.5f;
+#pragma unroll
+        for (int u = 0; u < 6; ++u) vb[(j + u) & 7] = __builtin_fmaf(vb[(j + u) & 7], 0.999f, -0.001f);
+      }
+    }
+    if constexpr ((MIX & 4) != 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  }
+  if constexpr ((MIX & 4) != 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[c][i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += va[i] + vb[i];
+  if constexpr ((MIX & 4) != 0) sum += __builtin_bit_cast(float, dma_dst[w][1][lane][0]) * 0.f;
+  out[tid] = sum;
 }
 
 // the same with v_mfma_f32_32x32x64_f8f6f4 on OCP e4m3 operands (32 bytes per lane and operand): four A and
@@ -244,26 +324,44 @@ double now_monotonic() {
   return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
 }
 
-// one phase of the sustained form: the MFMA loop over `src` launched back to back for `seconds` (src null: the
-// GPU left idle); prints the phase's interval and rate as one JSON object
-void sustain_phase(const char* name, const u32x4* src, float* out, int iters, double seconds, bool first) {
+typedef void (*mix_fn)(const u32x4*, const uint8_t*, float*, int);
+mix_fn mix_kernel(int mix) {
+  switch (mix) {
+    case 0: return mfma_mix<0>;
+    case 1: return mfma_mix<1>;
+    case 2: return mfma_mix<2>;
+    case 4: return mfma_mix<4>;
+    default: return mfma_mix<7>;
+  }
+}
+
+// one phase of the sustained form: mfma_mix<mix> over `src` launched back to back for `seconds` (src null: the
+// GPU left idle); prints the phase's interval, its rate and its wave-iterations (16 MFMAs each) per second
+void sustain_phase(const char* name, const u32x4* src, const uint8_t* l2src, float* out, int iters, int mix,
+                   double seconds, bool first) {
   CHECK(hipDeviceSynchronize());
+  const mix_fn f = mix_kernel(mix);
+  if (src != nullptr) {
+    hipLaunchKernelGGL(f, dim3(kGrid), dim3(kThreads), 0, 0, src, l2src, out, 64);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+  }
   const double t0 = now_monotonic();
-  double flop = 0.0;
+  double wave_iters = 0.0;
   if (src == nullptr) {
     usleep((useconds_t)(seconds * 1e6));
   } else {
-    const double per_launch = (double)kGrid * kThreads / 64 * iters * kMfmaPerIter * kFlopPerMfma;
     while (now_monotonic() - t0 < seconds) {
-      for (int i = 0; i < 4; ++i) hipLaunchKernelGGL(mfma_loop, dim3(kGrid), dim3(kThreads), 0, 0, src, out, iters);
+      for (int i = 0; i < 4; ++i) hipLaunchKernelGGL(f, dim3(kGrid), dim3(kThreads), 0, 0, src, l2src, out, iters);
       CHECK(hipGetLastError());
       CHECK(hipDeviceSynchronize());
-      flop += 4 * per_launch;
+      wave_iters += 4.0 * kGrid * (kThreads / 64) * iters;
     }
   }
   const double t1 = now_monotonic();
-  std::printf("%s{\"operands\": \"%s\", \"t0\": %.4f, \"t1\": %.4f, \"tflops\": %.1f}", first ? "" : ", ", name, t0,
-              t1, flop / (t1 - t0) / 1e12);
+  std::printf("%s{\"phase\": \"%s\", \"mix\": %d, \"t0\": %.4f, \"t1\": %.4f, \"tflops\": %.1f, "
+              "\"wave_iters_per_s\": %.5e}", first ? "" : ", ", name, src ? mix : -1, t0, t1,
+              wave_iters * kMfmaPerIter * kFlopPerMfma / (t1 - t0) / 1e12, wave_iters / (t1 - t0));
 }
 
 int main(int argc, char** argv) {
@@ -312,10 +410,16 @@ int main(int argc, char** argv) {
   if (sustain) {
     std::printf("{\"instruction\": \"v_mfma_f32_32x32x16_bf16\", \"mode\": \"sustain\", \"iterations\": %d, "
                 "\"seconds\": %.1f, \"clock\": \"CLOCK_MONOTONIC\", \"phases\": [", iters, seconds);
-    sustain_phase("idle", nullptr, out, iters, seconds, true);
-    sustain_phase("zero", zero, out, iters, seconds, false);
-    sustain_phase("idle", nullptr, out, iters, seconds, false);
-    sustain_phase("random", rnd, out, iters, seconds, false);
+    // the loads of the mixed phases sweep the first 4 MB of the random fp8 codes (n u32x4 = 32 MB)
+    const uint8_t* l2src = reinterpret_cast<const uint8_t*>(rnd8);
+    sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds, true);
+    sustain_phase("zero", zero, l2src, out, iters, 0, seconds, false);
+    const struct { const char* name; int mix; } mixed[] = {
+        {"random", 0}, {"random+lds_operands", 1}, {"random+valu", 2}, {"random+tile_loads", 4}, {"random+all", 7}};
+    for (const auto& m : mixed) {
+      sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds / 2, false);
+      sustain_phase(m.name, rnd, l2src, out, iters, m.mix, seconds, false);
+    }
     std::printf("]}\n");
     CHECK(hipFree(zero));
     CHECK(hipFree(rnd));
