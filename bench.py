@@ -166,11 +166,11 @@ def build_ceiling_programs():
         os.replace(exe + ".tmp", exe)
 
 
-def gpu_sysfs_dir(torch=None):
+def gpu_sysfs_dir(torch=None, root="/sys/class/drm"):
     """The sysfs device directory of cuda:0 that holds a hwmon power reading: matched by PCI address when torch
     reports it, else the only such GPU on the host; None if there is none (or no way to tell which)."""
     import glob
-    cands = [d for d in sorted(glob.glob("/sys/class/drm/card*/device"))
+    cands = [d for d in sorted(glob.glob(os.path.join(root, "card*", "device")))
              if glob.glob(os.path.join(d, "hwmon", "hwmon*", "power1_input"))]
     if torch is not None and cands:
         p = torch.cuda.get_device_properties(0)
