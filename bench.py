@@ -179,8 +179,12 @@ def gpu_sysfs_dir(torch=None, root="/sys/class/drm"):
             for d in cands:
                 addr = os.path.basename(os.path.realpath(d))  # domain:bus:device.function
                 parts = addr.replace(".", ":").split(":")
-                if len(parts) == 4 and int(parts[1], 16) == bus and \
-                        int(parts[2], 16) == getattr(p, "pci_device_id", int(parts[2], 16)):
+                try:
+                    dom, b, dv = (int(x, 16) for x in parts[:3])
+                except ValueError:
+                    continue
+                if len(parts) == 4 and (dom, b, dv) == (getattr(p, "pci_domain_id", dom), bus,
+                                                        getattr(p, "pci_device_id", dv)):
                     return d
     return cands[0] if len(cands) == 1 else None
 
