@@ -409,6 +409,24 @@ def _timed(torch, np, fn, steps):
     return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
 
 
+def _graph_timed(torch, np, fn, steps):
+    """mean ms of `steps` replays of a HIP graph holding one call of fn (captured after one eager call on a side
+    stream), between HIP events on the current stream"""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    ms = _timed(torch, np, g.replay, steps)
+    del g
+    return ms
+
+
 def time_prefill_vs_dense(ssm, torch, np, w, q, k, v, out, skip_ms, sparsity, steps, dev):
     """The same prefill launch at tau = -inf (no tile skipped: the dense kernel) against the timed skip launch:
     the speedup skipping buys on this input, the quantity the Skip Softmax pages report (as context: 1.4x for
@@ -660,6 +678,9 @@ def leg_decode_32k(ssm, torch, np, steps, dev, threads, cpu=True):
         ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps)
         got = out.float().cpu().numpy()
         c = cnt.cpu().numpy() / (steps + 1)
+        # the same call replayed from a HIP graph (its three kernels launched as one graph)
+        cnt_g = torch.zeros_like(cnt)
+        graph_ms = _graph_timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt_g)), steps) if P > 1 else None
         state.zero_()
         run(ssm.SkipStats(tile_state=state))
         st = state.cpu().numpy()
@@ -677,6 +698,8 @@ def leg_decode_32k(ssm, torch, np, steps, dev, threads, cpu=True):
         row = {"variant": name, "num_splits": P, "sink_seed": seeded, "ms": round(ms, 4),
                "sparsity": round(float(c[1]) / float(c[0]), 4), "kv_gbps": round((kb + vk) / t / 1e9, 1),
                "total_gbps": round(tot / t / 1e9, 1), "hbm_frac": round(tot / t / 1e9 / HBM_PEAK_GBPS, 4)}
+        if graph_ms is not None:
+            row["graph_ms"] = round(graph_ms, 4)
         if cpu:
             base, par = cpu_baseline_decode(np, w, data, tau, threads, P, got, st, sink_seed=seeded)
             row["oracle_kv_gbps"] = round(base["value"], 3)
