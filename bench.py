@@ -214,7 +214,7 @@ class BoardSampler:
 
     def cap_w(self):
         v = self._read(os.path.join(self.hwmon, "power1_cap")) if self.hwmon else None
-        return int(v) / 1e6 if v else None
+        return int(v) / 1e6 if v and v.strip().isdigit() else None
 
     def _clock(self):
         text = self._read(self.sclk) if self.sclk else None
@@ -228,7 +228,7 @@ class BoardSampler:
         pin = os.path.join(self.hwmon, "power1_input")
         while not self._stop.is_set():
             v = self._read(pin)
-            if v:
+            if v and v.strip().isdigit():
                 self.samples.append((time.monotonic(), int(v) / 1e6, self._clock()))
             self._stop.wait(self.period)
 
