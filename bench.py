@@ -396,12 +396,15 @@ def time_fp8_decode(ssm, torch, np, w, data, dq, kp, vp, pt, lens, dout, ws, dst
             "speedup_vs_bf16": None}
 
 
-def _timed(torch, np, fn, steps):
-    """mean ms of `steps` calls of fn between HIP events on the current stream, after one untimed call"""
+def _timed(torch, np, fn, steps, before=None):
+    """mean ms of `steps` calls of fn between HIP events on the current stream, after one untimed call; `before`
+    (untimed) runs ahead of each timed call"""
     fn()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
+        if before is not None:
+            before()
         ev[i][0].record()
         fn()
         ev[i][1].record()
@@ -409,7 +412,7 @@ def _timed(torch, np, fn, steps):
     return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
 
 
-def _graph_timed(torch, np, fn, steps):
+def _graph_timed(torch, np, fn, steps, before=None):
     """mean ms of `steps` replays of a HIP graph holding one call of fn (captured after one eager call on a side
     stream), between HIP events on the current stream"""
     side = torch.cuda.Stream()
@@ -422,7 +425,7 @@ def _graph_timed(torch, np, fn, steps):
     with torch.cuda.graph(g):
         fn()
     torch.cuda.synchronize()
-    ms = _timed(torch, np, g.replay, steps)
+    ms = _timed(torch, np, g.replay, steps, before)
     del g
     return ms
 
@@ -669,18 +672,22 @@ def leg_decode_32k(ssm, torch, np, steps, dev, threads, cpu=True):
     out = torch.empty_like(dq)
     max_tiles = -(-kc.shape[2] // 64)
     state = torch.zeros(w.B * w.Hkv, max_tiles, dtype=torch.uint8, device=dev)
+    # the caches (1.07 GB) are 4x the last-level cache: each timed call follows an untimed read of 1 GiB, so no call
+    # finds the previous one's lines there (a read leaves no dirty lines to write back during the timed call)
+    scratch = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    flush = lambda: scratch.max()
     rows = []
     for name, P, seeded in (("split_local_p16", 16, False), ("one_scan_p1", 1, False), ("sink_seeded_p16", 16, True)):
         ws = ssm.decode_workspace(w.B, w.Hq, w.d, P, dev)
         cnt = torch.zeros(4, dtype=torch.int64, device=dev)
         run = lambda st: ssm.ssm_decode(dq, kc, vc, lens, tau=tau, out=out, num_splits=P, workspace=ws,
                                         skip_stats=st, sink_seed=seeded)
-        ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps)
+        ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps, flush)
         got = out.float().cpu().numpy()
         c = cnt.cpu().numpy() / (steps + 1)
         # the same call replayed from a HIP graph (its three kernels launched as one graph)
         cnt_g = torch.zeros_like(cnt)
-        graph_ms = _graph_timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt_g)), steps) if P > 1 else None
+        graph_ms = _graph_timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt_g)), steps, flush) if P > 1 else None
         state.zero_()
         run(ssm.SkipStats(tile_state=state))
         st = state.cpu().numpy()
@@ -708,8 +715,9 @@ def leg_decode_32k(ssm, torch, np, steps, dev, threads, cpu=True):
             row["parity"] = par
         rows.append(row)
         del ws
-    del kc, vc
+    del kc, vc, scratch
     return {"workload": f"{w.name} (contiguous, kv_len {w.kv_len}, tau -ln 1000)", "tau": tau,
+            "timing": "each timed call after an untimed 1 GiB read (the last-level cache holds none of the caches)",
             "oracle_threads": threads, "variants": rows}
 
 
@@ -788,7 +796,7 @@ def leg_prefill_16k(ssm, torch, np, steps, dev, threads, cpu=True, n_units=64):
     for tau in w.taus:
         cnt = torch.zeros(4, dtype=torch.int64, device=dev)
         run = lambda st: ssm.ssm_prefill(q, k, v, causal=True, tau=tau, out=out, skip_stats=st, tile_q=w.tile_q)
-        ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps)
+        ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps, flush)
         got = gather_prefill_rows(torch, np, out, w, heads, qts)
         c = cnt.cpu().numpy() / (steps + 1)
         state.zero_()
