@@ -458,7 +458,8 @@ def time_pot_prefill(ssm, torch, np, w, q, k, v, out, tau, exp_ms, exp_dense_ms,
     cnt = torch.zeros(4, dtype=torch.int64, device=dev)
     run = lambda t: ssm.ssm_prefill(q, k, v, causal=True, tau=t, out=out, skip_stats=ssm.SkipStats(counters=cnt),
                                     tile_q=w.tile_q, weights="rowmax_pot")
-    ms = _timed(torch, np, lambda: run(tau), steps)
+    with BoardSampler(gpu_sysfs_dir(torch)) as board:
+        ms = _timed(torch, np, lambda: run(tau), steps)
     c = cnt.cpu().numpy() / (steps + 1)
     cnt.zero_()
     dense_ms = _timed(torch, np, lambda: run(-math.inf), steps)
@@ -484,7 +485,8 @@ def time_pot_prefill(ssm, torch, np, w, q, k, v, out, tau, exp_ms, exp_dense_ms,
             "speedup_vs_exp": round(exp_ms / ms, 3), "no_skip_ms": round(dense_ms, 3),
             "no_skip_speedup_vs_exp": round(exp_dense_ms / dense_ms, 3),
             "vs_exp_output": {"max_abs": float("%.4g" % mx), "rel_l2": float("%.4g" % math.sqrt(dd / max(ee, 1e-300)))},
-            "pages_speedup": {"causal_8k_fp8": 1.124, "noncausal_8k_fp8": 1.258, "hardware": "B200"}}
+            "pages_speedup": {"causal_8k_fp8": 1.124, "noncausal_8k_fp8": 1.258, "hardware": "B200"},
+            "board_power": board.summary()}
 
 
 def time_decode_tau_sweep(ssm, torch, np, w, dq, kp, vp, pt, lens, dout, ws, steps, dev):
@@ -533,11 +535,12 @@ def time_fp8qk_prefill(ssm, torch, np, w, q, k, v, out, tau, bf16_ms, steps, dev
     torch.cuda.synchronize()
     cnt.zero_()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        run()
-        ev[i][1].record()
-    torch.cuda.synchronize()
+    with BoardSampler(gpu_sysfs_dir(torch)) as board:
+        for i in range(steps):
+            ev[i][0].record()
+            run()
+            ev[i][1].record()
+        torch.cuda.synchronize()
     ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
     c = cnt.cpu().numpy() / steps
     visited, skipped = float(c[0]), float(c[1])
@@ -550,7 +553,7 @@ def time_fp8qk_prefill(ssm, torch, np, w, q, k, v, out, tau, bf16_ms, steps, dev
            "dense_tflops": round(dense / t / 1e12, 2), "executed_tflops": round(executed / t / 1e12, 2),
            "qk_fp8_tflops": round(qk_flop / t / 1e12, 2), "pv_bf16_tflops": round(pv_flop / t / 1e12, 2),
            "mfma_frac": round(ideal / t, 4), "sparsity": round(skipped / visited, 4), "tau": tau,
-           "q_scale": qs, "k_scale": ks, "speedup_vs_bf16": round(bf16_ms / ms, 3)}
+           "q_scale": qs, "k_scale": ks, "speedup_vs_bf16": round(bf16_ms / ms, 3), "board_power": board.summary()}
     c8, c16 = recorded_fp8_mfma_ceiling(), recorded_mfma_ceiling()
     if c8 and c16:
         res["mfma_frac_of_measured_ceilings"] = round((qk_flop / (c8 * 1e12) + pv_flop / (c16 * 1e12)) / t, 4)
@@ -590,11 +593,12 @@ def time_chunked_prefill(ssm, torch, np, w, data, tau, steps, dev):
     torch.cuda.synchronize()
     cnt.zero_()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        run()
-        ev[i][1].record()
-    torch.cuda.synchronize()
+    with BoardSampler(gpu_sysfs_dir(torch)) as board:
+        for i in range(steps):
+            ev[i][0].record()
+            run()
+            ev[i][1].record()
+        torch.cuda.synchronize()
     ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
     c = cnt.cpu().numpy() / steps
     visited, skipped = float(c[0]), float(c[1])
@@ -796,7 +800,7 @@ def leg_prefill_16k(ssm, torch, np, steps, dev, threads, cpu=True, n_units=64):
     for tau in w.taus:
         cnt = torch.zeros(4, dtype=torch.int64, device=dev)
         run = lambda st: ssm.ssm_prefill(q, k, v, causal=True, tau=tau, out=out, skip_stats=st, tile_q=w.tile_q)
-        ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps, flush)
+        ms = _timed(torch, np, lambda: run(ssm.SkipStats(counters=cnt)), steps)
         got = gather_prefill_rows(torch, np, out, w, heads, qts)
         c = cnt.cpu().numpy() / (steps + 1)
         state.zero_()
