@@ -1147,6 +1147,7 @@ def main():
         t = float(np.mean(p_ms)) / 1e3
         res["value"] = round(dense / t / 1e12, 2)
         res["prefill_ms"] = round(t * 1e3, 3)
+        res["prefill_ms_median_min"] = [round(float(np.median(p_ms)), 3), round(float(np.min(p_ms)), 3)]
         res["prefill_executed_tflops"] = round(executed / t / 1e12, 2)
         res["prefill_sparsity"] = round(skipped / visited, 4)
         cfg["prefill"] = {"batch": pw.B, "seq_len": pw.S, "q_heads": pw.Hq, "kv_heads": pw.Hkv, "head_dim": pw.d,
@@ -1185,6 +1186,7 @@ def main():
         kb, vk, va, small = decode_bytes(dw, lens_np, state, dw.num_splits)
         t = float(np.mean(d_ms)) / 1e3
         res["decode_ms"] = round(t * 1e3, 4)
+        res["decode_ms_median_min"] = [round(float(np.median(d_ms)), 4), round(float(np.min(d_ms)), 4)]
         res["decode_kv_gbps"] = round((kb + vk) / t / 1e9, 1)
         res["decode_total_gbps"] = round((kb + vk + small) / t / 1e9, 1)
         res["decode_dense_equiv_kv_gbps"] = round((kb + va) / t / 1e9, 1)
