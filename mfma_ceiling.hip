@@ -15,7 +15,8 @@
 // each): the A operand of every MFMA read from LDS (16 ds_read_b128, 16 KB, as the prefill reads its K and V
 // operands); 16 v_exp_f32 with 16 adds and 48 fmas that do not depend on the MFMAs (about the prefill's VALU
 // work per 16 MFMAs); two 1 KB direct-to-LDS buffer loads from a 4 MB buffer that stays in L2 (the prefill's
-// tile loads per 16 MFMAs); and all three together.
+// tile loads per 16 MFMAs); the LDS operand reads done as transposing reads (as the prefill reads V); one
+// workgroup barrier; and the first three together.
 //
 // Each of 512 workgroups (two per compute unit, four waves each, i.e. two waves per SIMD, the occupancy
 // of the prefill kernel) reads its 16 operand registers per lane once and then issues only MFMAs on four
@@ -73,11 +74,19 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_loop(const u32x4* __restrict
 // MIX selects: bit 0 the A operand of every MFMA from LDS (random operand data staged there at the start, 64 KB
 // per workgroup), bit 1 independent VALU work (16 v_exp_f32 + 16 v_add_f32 + 48 v_fma_f32), bit 2 two 1 KB
 // direct-to-LDS buffer loads per wave from the first kL2Bytes of `l2src` (a range that stays in the L2
-// caches), waited for two iterations later.
+// caches), waited for two iterations later, bit 3 (with bit 0) the same LDS bytes through two transposing
+// 8-byte reads (ds_read_b64_tr_b16) per operand instead of one ds_read_b128, bit 4 one workgroup barrier.
 constexpr int kLdsOps = 4096;            // u32x4 of operand data in LDS
 constexpr uint32_t kL2Bytes = 4u << 20;  // bytes of l2src the loads sweep
 static_assert((size_t)kGrid * kLdsOps <= (size_t)kGrid * kThreads * kOps, "LDS staging reads stay inside src");
 static_assert((size_t)kL2Bytes <= (size_t)kGrid * kThreads * kOps * 16, "the loads stay inside l2src");
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 tr_read16(const char* p) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p + 8));
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int MIX>
 __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict__ src, const uint8_t* __restrict__ l2src,
                                                         float* __restrict__ out, int iters) {
@@ -114,9 +123,16 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       u32x4 a1 = a[j], a2 = a[(j + 3) & 7];
-      if constexpr ((MIX & 1) != 0) {
-        a1 = lds[((it * 16 + 2 * j) * 64 + w * 1024 + lane) & (kLdsOps - 1)];
-        a2 = lds[((it * 16 + 2 * j + 1) * 64 + w * 1024 + lane) & (kLdsOps - 1)];
+      const int i1 = ((it * 16 + 2 * j) * 64 + w * 1024 + lane) & (kLdsOps - 1);
+      const int i2 = ((it * 16 + 2 * j + 1) * 64 + w * 1024 + lane) & (kLdsOps - 1);
+      if constexpr ((MIX & 9) == 1) {
+        a1 = lds[i1];
+        a2 = lds[i2];
+      } else if constexpr ((MIX & 9) == 9) {
+        // the 16 bytes of lds[i] in two transposing 8-byte reads (the bytes each lane receives differ from
+        // lds[i]'s, the bytes read per operand do not); every address stays inside lds
+        a1 = tr_read16(reinterpret_cast<const char*>(lds) + i1 * 16);
+        a2 = tr_read16(reinterpret_cast<const char*>(lds) + i2 * 16);
       }
       acc[(2 * j) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[j]),
                                                                  acc[(2 * j) & 3], 0, 0, 0);
@@ -130,6 +146,8 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
       }
     }
     if constexpr ((MIX & 4) != 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    // every wave of the workgroup runs the same iterations, so each barrier is met by all four
+    if constexpr ((MIX & 16) != 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if constexpr ((MIX & 4) != 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   float sum = 0.f;
@@ -331,6 +349,8 @@ mix_fn mix_kernel(int mix) {
     case 1: return mfma_mix<1>;
     case 2: return mfma_mix<2>;
     case 4: return mfma_mix<4>;
+    case 9: return mfma_mix<9>;
+    case 16: return mfma_mix<16>;
     default: return mfma_mix<7>;
   }
 }
@@ -415,7 +435,8 @@ int main(int argc, char** argv) {
     sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds, true);
     sustain_phase("zero", zero, l2src, out, iters, 0, seconds, false);
     const struct { const char* name; int mix; } mixed[] = {
-        {"random", 0}, {"random+lds_operands", 1}, {"random+valu", 2}, {"random+tile_loads", 4}, {"random+all", 7}};
+        {"random", 0}, {"random+lds_operands", 1}, {"random+lds_operands_transposing", 9}, {"random+valu", 2},
+        {"random+tile_loads", 4}, {"random+barrier", 16}, {"random+all", 7}};
     for (const auto& m : mixed) {
       sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds / 2, false);
       sustain_phase(m.name, rnd, l2src, out, iters, m.mix, seconds, false);
