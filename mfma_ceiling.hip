@@ -16,7 +16,7 @@
 // operands); 16 v_exp_f32 with 16 adds and 48 fmas that do not depend on the MFMAs (about the prefill's VALU
 // work per 16 MFMAs); two 1 KB direct-to-LDS buffer loads from a 4 MB buffer that stays in L2 (the prefill's
 // tile loads per 16 MFMAs); the LDS operand reads done as transposing reads (as the prefill reads V); one
-// workgroup barrier; and the first three together.
+// workgroup barrier; about 48 scalar instructions; and the first three together.
 //
 // Each of 512 workgroups (two per compute unit, four waves each, i.e. two waves per SIMD, the occupancy
 // of the prefill kernel) reads its 16 operand registers per lane once and then issues only MFMAs on four
@@ -75,7 +75,9 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_loop(const u32x4* __restrict
 // per workgroup), bit 1 independent VALU work (16 v_exp_f32 + 16 v_add_f32 + 48 v_fma_f32), bit 2 two 1 KB
 // direct-to-LDS buffer loads per wave from the first kL2Bytes of `l2src` (a range that stays in the L2
 // caches), waited for two iterations later, bit 3 (with bit 0) the same LDS bytes through two transposing
-// 8-byte reads (ds_read_b64_tr_b16) per operand instead of one ds_read_b128, bit 4 one workgroup barrier.
+// 8-byte reads (ds_read_b64_tr_b16) per operand instead of one ds_read_b128, bit 4 one workgroup barrier,
+// bit 5 24 scalar multiplies (s_mul_i32, which leaves the condition code alone) with the scalar adds that form
+// their operands, about 48 scalar instructions.
 constexpr int kLdsOps = 4096;            // u32x4 of operand data in LDS
 constexpr uint32_t kL2Bytes = 4u << 20;  // bytes of l2src the loads sweep
 static_assert((size_t)kGrid * kLdsOps <= (size_t)kGrid * kThreads * kOps, "LDS staging reads stay inside src");
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)l2src, (short)0, (int)kL2Bytes, 0x00020000);
   const uint32_t gw = (uint32_t)(blockIdx.x * (kThreads / 64) + w);
   f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  uint32_t salu = (uint32_t)blockIdx.x;
   for (int it = 0; it < iters; ++it) {
     if constexpr ((MIX & 4) != 0) {
 #pragma unroll
@@ -148,6 +151,10 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
     if constexpr ((MIX & 4) != 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     // every wave of the workgroup runs the same iterations, so each barrier is met by all four
     if constexpr ((MIX & 16) != 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr ((MIX & 32) != 0) {
+#pragma unroll
+      for (int u = 0; u < 24; ++u) asm volatile("s_mul_i32 %0, %0, %1" : "+s"(salu) : "s"(2 * (u + it) + 1));
+    }
   }
   if constexpr ((MIX & 4) != 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   float sum = 0.f;
@@ -158,6 +165,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
 #pragma unroll
   for (int i = 0; i < 8; ++i) sum += va[i] + vb[i];
   if constexpr ((MIX & 4) != 0) sum += __builtin_bit_cast(float, dma_dst[w][1][lane][0]) * 0.f;
+  if constexpr ((MIX & 32) != 0) sum += (float)(salu & 1u) * 0.f;
   out[tid] = sum;
 }
 
@@ -351,6 +359,7 @@ mix_fn mix_kernel(int mix) {
     case 4: return mfma_mix<4>;
     case 9: return mfma_mix<9>;
     case 16: return mfma_mix<16>;
+    case 32: return mfma_mix<32>;
     default: return mfma_mix<7>;
   }
 }
@@ -436,7 +445,7 @@ int main(int argc, char** argv) {
     sustain_phase("zero", zero, l2src, out, iters, 0, seconds, false);
     const struct { const char* name; int mix; } mixed[] = {
         {"random", 0}, {"random+lds_operands", 1}, {"random+lds_operands_transposing", 9}, {"random+valu", 2},
-        {"random+tile_loads", 4}, {"random+barrier", 16}, {"random+all", 7}};
+        {"random+tile_loads", 4}, {"random+barrier", 16}, {"random+scalar", 32}, {"random+all", 7}};
     for (const auto& m : mixed) {
       sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds / 2, false);
       sustain_phase(m.name, rnd, l2src, out, iters, m.mix, seconds, false);
