@@ -197,7 +197,8 @@ class BoardSampler:
     def __init__(self, dev_dir, period=0.01):
         import glob
         import threading
-        self.hwmon = glob.glob(os.path.join(dev_dir, "hwmon", "hwmon*"))[0] if dev_dir else None
+        hw = sorted(glob.glob(os.path.join(dev_dir, "hwmon", "hwmon*"))) if dev_dir else []
+        self.hwmon = hw[0] if hw else None
         self.sclk = os.path.join(dev_dir, "pp_dpm_sclk") if dev_dir else None
         self.period = period
         self.samples = []  # (t, watts, mhz or None)
@@ -256,9 +257,10 @@ class BoardSampler:
 
 def mfma_power(seconds):
     """Run mfma_ceiling in its sustained form beside a BoardSampler and print, per phase (idle; zero and random
-    operands; random operands with LDS operand reads, VALU work, tile loads, all three), the MFMA rate with the
-    board's power and clock over the phase's last three quarters, and the energy above idle per wave-iteration
-    (16 MFMAs of one wave with that phase's other work) and per executed FLOP."""
+    operands; random operands with LDS operand reads, transposing LDS reads, VALU work, tile loads, a barrier,
+    scalar instructions, or LDS reads, VALU work and tile loads together), the MFMA rate with the board's power
+    and clock over the phase's last three quarters, and the energy above idle per wave-iteration (16 MFMAs of
+    one wave with that phase's other work) and per executed FLOP."""
     exe = os.path.join(CEILING_DIR, "mfma_ceiling")
     if not os.path.exists(exe):
         sys.exit(f"{exe} is missing: build it with `python -c 'import bench; bench.build_ceiling_programs()'`")
