@@ -258,9 +258,9 @@ class BoardSampler:
 def mfma_power(seconds):
     """Run mfma_ceiling in its sustained form beside a BoardSampler and print, per phase (idle; zero and random
     operands; random operands with LDS operand reads, transposing LDS reads, VALU work, tile loads, a barrier,
-    scalar instructions, or LDS reads, VALU work and tile loads together), the MFMA rate with the board's power
-    and clock over the phase's last three quarters, and the energy above idle per wave-iteration (16 MFMAs of
-    one wave with that phase's other work) and per executed FLOP."""
+    scalar instructions, or LDS reads, VALU work and tile loads together; normal operands), the MFMA rate with
+    the board's power and clock over the phase's last three quarters, and the energy above idle per
+    wave-iteration (16 MFMAs of one wave with that phase's other work) and per executed FLOP."""
     exe = os.path.join(CEILING_DIR, "mfma_ceiling")
     if not os.path.exists(exe):
         sys.exit(f"{exe} is missing: build it with `python -c 'import bench; bench.build_ceiling_programs()'`")
@@ -288,7 +288,7 @@ def mfma_power(seconds):
             ph["pj_per_flop"] = round(above / (ph["tflops"] * 1e12) * 1e12, 4)
             if ph["phase"] == "random":
                 base = ph["nj_per_wave_iter"]
-            elif base is not None and ph["phase"].startswith("random+"):
+            elif base is not None and (ph["phase"].startswith("random+") or ph["phase"] == "normal"):
                 ph["nj_over_random"] = round(ph["nj_per_wave_iter"] - base, 1)
     rec["sysfs"] = dev_dir
     print(json.dumps(rec), flush=True)

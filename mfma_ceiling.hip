@@ -16,7 +16,8 @@
 // operands); 16 v_exp_f32 with 16 adds and 48 fmas that do not depend on the MFMAs (about the prefill's VALU
 // work per 16 MFMAs); two 1 KB direct-to-LDS buffer loads from a 4 MB buffer that stays in L2 (the prefill's
 // tile loads per 16 MFMAs); the LDS operand reads done as transposing reads (as the prefill reads V); one
-// workgroup barrier; about 48 scalar instructions; and the first three together.
+// workgroup barrier; about 48 scalar instructions; and the first three together. A last phase runs the loop
+// alone on normally distributed operands.
 //
 // Each of 512 workgroups (two per compute unit, four waves each, i.e. two waves per SIMD, the occupancy
 // of the prefill kernel) reads its 16 operand registers per lane once and then issues only MFMAs on four
@@ -27,6 +28,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <cmath>
 #include <ctime>
 #include <unistd.h>
 #include <vector>
@@ -450,6 +452,25 @@ int main(int argc, char** argv) {
       sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds / 2, false);
       sustain_phase(m.name, rnd, l2src, out, iters, m.mix, seconds, false);
     }
+    // the MFMA loop alone on normal operands (bf16 of N(0, 1) values, as the attention inputs are drawn) in
+    // place of uniform ones, over the zero buffer, which is no longer needed
+    std::vector<uint32_t> gauss(n * 4);
+    for (size_t i = 0; i < gauss.size(); ++i) {
+      uint32_t w = 0;
+      for (int h = 0; h < 2; ++h) {
+        // Box-Muller on two 53-bit uniforms, the first in (0, 1]
+        const double u1 = (double)((splitmix64(state) >> 11) + 1) * 0x1.0p-53;
+        const double u2 = (double)(splitmix64(state) >> 11) * 0x1.0p-53;
+        const float f = (float)(std::sqrt(-2.0 * std::log(u1)) * std::cos(6.283185307179586 * u2));
+        uint32_t u;
+        std::memcpy(&u, &f, 4);
+        w |= (u >> 16) << (16 * h);
+      }
+      gauss[i] = w;
+    }
+    CHECK(hipMemcpy(zero, gauss.data(), n * sizeof(u32x4), hipMemcpyHostToDevice));
+    sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds / 2, false);
+    sustain_phase("normal", zero, l2src, out, iters, 0, seconds, false);
     std::printf("]}\n");
     CHECK(hipFree(zero));
     CHECK(hipFree(rnd));
