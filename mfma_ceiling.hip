@@ -16,8 +16,9 @@
 // operands); 16 v_exp_f32 with 16 adds and 48 fmas that do not depend on the MFMAs (about the prefill's VALU
 // work per 16 MFMAs); two 1 KB direct-to-LDS buffer loads from a 4 MB buffer that stays in L2 (the prefill's
 // tile loads per 16 MFMAs); the LDS operand reads done as transposing reads (as the prefill reads V); one
-// workgroup barrier; about 48 scalar instructions; and the first three together. A last phase runs the loop
-// alone on normally distributed operands.
+// workgroup barrier; about 48 scalar instructions; conversions to bf16 and bf16 dot products in place of the
+// exponentials and adds; and the first three together. A last phase runs the loop alone on normally
+// distributed operands.
 //
 // Each of 512 workgroups (two per compute unit, four waves each, i.e. two waves per SIMD, the occupancy
 // of the prefill kernel) reads its 16 operand registers per lane once and then issues only MFMAs on four
@@ -79,12 +80,15 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_loop(const u32x4* __restrict
 // caches), waited for two iterations later, bit 3 (with bit 0) the same LDS bytes through two transposing
 // 8-byte reads (ds_read_b64_tr_b16) per operand instead of one ds_read_b128, bit 4 one workgroup barrier,
 // bit 5 24 scalar multiplies (s_mul_i32, which leaves the condition code alone) with the scalar adds that form
-// their operands, about 48 scalar instructions.
+// their operands, about 48 scalar instructions, bit 6 the prefill's other VALU kinds in place of bit 1's
+// exponentials and adds: 16 v_cvt_pk_bf16_f32 and 16 v_dot2c_f32_bf16 (as the weights are packed and summed)
+// with the same 48 fmas.
 constexpr int kLdsOps = 4096;            // u32x4 of operand data in LDS
 constexpr uint32_t kL2Bytes = 4u << 20;  // bytes of l2src the loads sweep
 static_assert((size_t)kGrid * kLdsOps <= (size_t)kGrid * kThreads * kOps, "LDS staging reads stay inside src");
 static_assert((size_t)kL2Bytes <= (size_t)kGrid * kThreads * kOps * 16, "the loads stay inside l2src");
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 tr_read16(const char* p) {
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p + 8));
@@ -143,6 +147,15 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
                                                                  acc[(2 * j) & 3], 0, 0, 0);
       acc[(2 * j + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, b[j]),
                                                                      acc[(2 * j + 1) & 3], 0, 0, 0);
+      if constexpr ((MIX & 64) != 0) {
+        const bf16x2 p0 = {(__bf16)va[j], (__bf16)va[(j + 1) & 7]};
+        const bf16x2 p1 = {(__bf16)va[(j + 2) & 7], (__bf16)va[(j + 3) & 7]};
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        vb[j] = __builtin_amdgcn_fdot2_f32_bf16(p0, one, vb[j], false);
+        vb[(j + 4) & 7] = __builtin_amdgcn_fdot2_f32_bf16(p1, one, vb[(j + 4) & 7], false);
+#pragma unroll
+        for (int u = 0; u < 6; ++u) va[(j + u) & 7] = __builtin_fmaf(va[(j + u) & 7], 0.999f, -0.001f);
+      }
       if constexpr ((MIX & 2) != 0) {
         va[j] = __builtin_amdgcn_exp2f(va[j]) - 1.5f;
         va[(j + 4) & 7] = __builtin_amdgcn_exp2f(va[(j + 4) & 7]) - 1.5f;
@@ -362,6 +375,7 @@ mix_fn mix_kernel(int mix) {
     case 9: return mfma_mix<9>;
     case 16: return mfma_mix<16>;
     case 32: return mfma_mix<32>;
+    case 64: return mfma_mix<64>;
     default: return mfma_mix<7>;
   }
 }
@@ -447,7 +461,8 @@ int main(int argc, char** argv) {
     sustain_phase("zero", zero, l2src, out, iters, 0, seconds, false);
     const struct { const char* name; int mix; } mixed[] = {
         {"random", 0}, {"random+lds_operands", 1}, {"random+lds_operands_transposing", 9}, {"random+valu", 2},
-        {"random+tile_loads", 4}, {"random+barrier", 16}, {"random+scalar", 32}, {"random+all", 7}};
+        {"random+valu_convert_dot", 64}, {"random+tile_loads", 4}, {"random+barrier", 16}, {"random+scalar", 32},
+        {"random+all", 7}};
     for (const auto& m : mixed) {
       sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds / 2, false);
       sustain_phase(m.name, rnd, l2src, out, iters, m.mix, seconds, false);
