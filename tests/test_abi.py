@@ -91,9 +91,16 @@ def call_prefill(lib, q=None, k=None, v=None, o=None, seqlen=256, causal=1, tau=
     ("seqlen", ssm.SSM_EINVAL), ("gqa", ssm.SSM_EINVAL), ("head_dim", ssm.SSM_EUNSUPPORTED),
     ("dtype", ssm.SSM_EUNSUPPORTED), ("stride", ssm.SSM_EINVAL), ("align", ssm.SSM_EUNSUPPORTED),
     ("tile_q", ssm.SSM_EUNSUPPORTED), ("tile_k", ssm.SSM_EUNSUPPORTED), ("out_shape", ssm.SSM_EINVAL),
+    ("slice_offsets", ssm.SSM_EUNSUPPORTED), ("too_many_tiles", ssm.SSM_EUNSUPPORTED),
+    ("too_long", ssm.SSM_EUNSUPPORTED),
 ])
 def test_prefill_rejects(lib, case, code):
     kw = {}
+    if case in ("slice_offsets", "too_many_tiles", "too_long"):
+        # sizes past the limits the kernels' 32-bit offsets and grid allow; nothing is dereferenced
+        B, S = {"slice_offsets": (1, 262144), "too_many_tiles": (40000, 1 << 20), "too_long": (1, (1 << 30) + 64)}[case]
+        kw["q"], kw["k"], kw["v"], kw["o"] = (desc([B, S, h, 128]) for h in (64, 8, 8, 64))
+        kw["seqlen"] = S
     if case == "nan_tau":
         kw["tau"] = math.nan
     elif case == "pos_tau":
