@@ -264,10 +264,18 @@ def test_decode_noalloc_rejects_before_any_device_call(lib):
     ("group_too_big", ssm.SSM_EUNSUPPORTED), ("splits", ssm.SSM_EUNSUPPORTED), ("batch", ssm.SSM_EINVAL),
     ("head_dim", ssm.SSM_EUNSUPPORTED), ("unknown_flag", ssm.SSM_EINVAL), ("fp8_no_scale", ssm.SSM_EINVAL),
     ("fp8_nan_scale", ssm.SSM_EINVAL), ("mixed_kv_dtypes", ssm.SSM_EINVAL), ("fp8_stride", ssm.SSM_EUNSUPPORTED),
-    ("fp32_cache", ssm.SSM_EUNSUPPORTED),
+    ("fp32_cache", ssm.SSM_EUNSUPPORTED), ("batch_too_large", ssm.SSM_EUNSUPPORTED),
+    ("too_many_pages", ssm.SSM_EUNSUPPORTED),
 ])
 def test_decode_rejects(lib, case, code):
     kw = {}
+    if case == "batch_too_large":
+        # more sequences than the grid's (b, g, split) numbering allows; nothing is dereferenced
+        kw["q"], kw["o"] = desc([70000, 16, 128]), desc([70000, 16, 128])
+        kw["kc"], kw["vc"] = cache([70000, 2, 1024, 128]), cache([70000, 2, 1024, 128])
+    elif case == "too_many_pages":
+        kw["kc"] = cache([100, 2, 64, 128], paged=True, max_pages=(1 << 25))
+        kw["vc"] = cache([100, 2, 64, 128], paged=True, max_pages=(1 << 25))
     if case == "no_workspace":
         kw["opts"] = None
     elif case == "small_workspace":
@@ -308,6 +316,10 @@ def test_decode_rejects(lib, case, code):
         kw["vc"] = cache([2, 2, 1024, 128], dtype=ssm.SSM_FP32)
     rc = call_decode(lib, **kw)
     assert rc == code, (rc, ssm.ssm_last_error())
+    if case == "batch_too_large":
+        assert "too large" in ssm.ssm_last_error()
+    if case == "too_many_pages":
+        assert "too many pages" in ssm.ssm_last_error()
 
 
 def test_product_does_not_import_oracle():
