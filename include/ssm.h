@@ -19,6 +19,9 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    default stream).  No call synchronises or reads device memory on the
  *    host.  Outputs and statistics are valid once the stream has passed them.
+ *  - A call enqueues kernel launches only (no memset or copy nodes), so it can
+ *    be captured into a HIP graph and replayed; each replay reads the buffers'
+ *    contents at that time (kv_lens and page tables included).
  *  - Return codes: SSM_OK, or an error code; on any error nothing is launched
  *    and ssm_last_error() (thread-local) holds a message.
  *  - Units of tau: natural-log ratio of softmax weights (tau = -ln 1000 skips a
