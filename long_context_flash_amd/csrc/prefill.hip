@@ -55,8 +55,11 @@
 // Exponentials use a lazily moved reference maximum: P = 2^(S*c - m_ref*c) with
 // m_ref only raised when the true running maximum exceeds it by more than 8
 // (log2 units), which bounds P by 256 and makes the rescale of the output
-// accumulator rare.  The row sums add the same bf16-rounded P that enters the
-// P*V product (v_dot2 against (1, 1)).  The skip vote always uses the true
+// accumulator rare.  The row sums add the fp32 weights, before their rounding
+// to the bf16 P that enters the P*V product: two plain adds per pair draw less
+// energy than one bf16 dot product of the rounded pair, and on this
+// power-limited board that is 3% of the launch.  Rowmax-PoT weights are exact in
+// bf16 and are summed from their bf16 bits.  The skip vote always uses the true
 // running maximum.
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -377,9 +380,14 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   auto exp_pair = [&](const f32x16 (&s)[2], uint32_t (&pk)[4][4], int n, float eo) {
     const int st = n >> 3, e = n & 7;  // 16-key step, position inside it
     const float s0 = s[st >> 1][8 * (st & 1) + e], s1 = s[st >> 1][8 * (st & 1) + e + 1];
-    if constexpr (POT) pk[st][e >> 1] = pot_pack_bf16x2(s0, s1, c2, eo);
-    else pk[st][e >> 1] = pack_bf16x2(exp2_fast(fmaf(s0, c2, -eo)), exp2_fast(fmaf(s1, c2, -eo)));
-    l_part[(n >> 1) & 1] = dot2_bf16_sum(pk[st][e >> 1], l_part[(n >> 1) & 1]);
+    if constexpr (POT) {
+      pk[st][e >> 1] = pot_pack_bf16x2(s0, s1, c2, eo);
+      l_part[(n >> 1) & 1] = dot2_bf16_sum(pk[st][e >> 1], l_part[(n >> 1) & 1]);
+    } else {
+      const float p0 = exp2_fast(fmaf(s0, c2, -eo)), p1 = exp2_fast(fmaf(s1, c2, -eo));
+      pk[st][e >> 1] = pack_bf16x2(p0, p1);
+      l_part[(n >> 1) & 1] += p0 + p1;
+    }
   };
   // keep the exponentials where they are issued (next to the MFMAs they overlap) instead of letting
   // them sink towards their use one iteration later
