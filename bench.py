@@ -89,7 +89,10 @@ def recorded_read_ceiling():
 
 def summarize_traffic(fetch_dir, write_dir, command):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) into HBM bytes per launch,
-    each scaled by what the same counter reads for a device copy of COPY_PROBE_BYTES."""
+    each scaled by what the same counter reads for a device copy of COPY_PROBE_BYTES.  The per-launch figure is
+    the median over a kernel's dispatches: the runs take W warmup + K timed steps and then one untimed call that
+    records the tile states (a fresh output buffer, byte-wise state writes), whose traffic differs from the
+    timed calls' and must not set the figure."""
     import csv
     import glob
 
@@ -108,11 +111,15 @@ def summarize_traffic(fetch_dir, write_dir, command):
     f_fac = kib / max(fetch[copy])
     w_fac = kib / max(write[copy])
 
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
     def launch_bytes(pred):
         tot = 0.0
         for n in fetch:
             if pred(n):
-                tot += (sum(fetch[n]) / len(fetch[n]) * f_fac + sum(write[n]) / len(write[n]) * w_fac) * 1024
+                tot += (med(fetch[n]) * f_fac + med(write[n]) * w_fac) * 1024
         return tot
 
     rec = {"copy_kernel": copy, "fetch_factor": f_fac, "write_factor": w_fac, "command": command,
@@ -130,12 +137,17 @@ def summarize_traffic(fetch_dir, write_dir, command):
              f"Normalisation: a device copy of {COPY_PROBE_BYTES} bytes (`{copy}`) reads FETCH_SIZE = "
              f"{max(fetch[copy]):.0f} KiB and WRITE_SIZE = {max(write[copy]):.0f} KiB; factors "
              f"{f_fac:.4f} (fetch) and {w_fac:.4f} (write) scale each kernel's counters to bytes.", "",
-             "| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/dispatch (scaled) |",
-             "|---|---|---|---|---|"]
+             "Each figure is the median over the kernel's dispatches; FETCH_SIZE per dispatch in order, KiB, in the "
+             "last column.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/dispatch (scaled) "
+             "| FETCH_SIZE of each dispatch |",
+             "|---|---|---|---|---|---|"]
     for n in sorted(fetch):
-        fk = sum(fetch[n]) / len(fetch[n])
-        wk = sum(write.get(n, [0])) / max(len(write.get(n, [0])), 1)
-        lines.append(f"| `{n[:90]}` | {len(fetch[n])} | {fk:.0f} | {wk:.0f} | {(fk * f_fac + wk * w_fac) * 1024:.4g} |")
+        fk = med(fetch[n])
+        wk = med(write.get(n, [0]))
+        each = " ".join(f"{x:.0f}" for x in fetch[n]) if len(fetch[n]) <= 8 else ""
+        lines.append(f"| `{n[:90]}` | {len(fetch[n])} | {fk:.0f} | {wk:.0f} | {(fk * f_fac + wk * w_fac) * 1024:.4g} "
+                     f"| {each} |")
     lines += ["", f"Per launch: prefill {rec['prefill']['bytes_per_launch']:.4g} B; decode (order + split + combine) "
               f"{rec['decode']['bytes_per_launch']:.4g} B."]
     with open(os.path.join(ROOT, "profiles", "hbm_traffic__prefill_s128k__decode_b32_kv128k_paged.md"), "w") as f:
