@@ -58,9 +58,9 @@
 // accumulator rare.  The row sums add the fp32 weights, before their rounding
 // to the bf16 P that enters the P*V product: two plain adds per pair draw less
 // energy than one bf16 dot product of the rounded pair, and on this
-// power-limited board that is 3% of the launch.  Rowmax-PoT weights are exact in
-// bf16 and are summed from their bf16 bits.  The skip vote always uses the true
-// running maximum.
+// power-limited board that is 3% of the launch.  Rowmax-PoT weights are exact
+// powers of two, built in fp32 and summed the same way.  The skip vote always
+// uses the true running maximum.
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -381,8 +381,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     const int st = n >> 3, e = n & 7;  // 16-key step, position inside it
     const float s0 = s[st >> 1][8 * (st & 1) + e], s1 = s[st >> 1][8 * (st & 1) + e + 1];
     if constexpr (POT) {
-      pk[st][e >> 1] = pot_pack_bf16x2(s0, s1, c2, eo);
-      l_part[(n >> 1) & 1] = dot2_bf16_sum(pk[st][e >> 1], l_part[(n >> 1) & 1]);
+      pk[st][e >> 1] = pot_pack_sum_bf16x2(s0, s1, c2, eo, l_part[(n >> 1) & 1]);
     } else {
       const float p0 = exp2_fast(fmaf(s0, c2, -eo)), p1 = exp2_fast(fmaf(s1, c2, -eo));
       pk[st][e >> 1] = pack_bf16x2(p0, p1);

@@ -387,8 +387,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
           const int stp = n >> 3, e = n & 7;  // 16-key step, position inside it (P^T operand order)
           const float s0 = sprev[stp >> 1][8 * (stp & 1) + e], s1 = sprev[stp >> 1][8 * (stp & 1) + e + 1];
           if constexpr (POT) {
-            pk[stp][e >> 1] = pot_pack_bf16x2(s0, s1, c2, moff);
-            l_part[(n >> 1) & 1] = dot2_bf16_sum(pk[stp][e >> 1], l_part[(n >> 1) & 1]);
+            pk[stp][e >> 1] = pot_pack_sum_bf16x2(s0, s1, c2, moff, l_part[(n >> 1) & 1]);
           } else {
             // the row sums add the fp32 weights (two plain adds cost less energy than one bf16 dot product)
             const float p0 = exp2_fast(fmaf(s0, c2, -moff)), p1 = exp2_fast(fmaf(s1, c2, -moff));

@@ -51,19 +51,21 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-// Rowmax-PoT weight pair: 2^rint(s*c2 - kref) for two scores (kref an integer), written straight into the bf16
-// exponent field, with no transcendental.  Adding 1.5*2^23 to the clamped log weight rounds it to an integer
-// (ties to even) held in the low mantissa bits; (integer + 127) << 7, taken modulo 2^16, is then the bf16
-// pattern of 2^integer, for both halves at once.  A score of -inf, or one whose log weight rounds to -127 or
-// less, gives +0; the log weight must stay below 128 (the callers keep it at most 9).
-__device__ __forceinline__ uint32_t pot_pack_bf16x2(float s0, float s1, float c2, float kref) {
-  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+// Rowmax-PoT weight pair: 2^rint(s*c2 - kref) for two scores (kref an integer), with no transcendental, and
+// their sum added to `acc`.  Adding 1.5*2^23 to the clamped log weight rounds it to an integer k (ties to even)
+// held in the low mantissa bits; (bits << 23) + bits(1.0), modulo 2^32, is then the fp32 pattern of 2^k (0 for
+// k = -127), whose high half is the bf16 pattern.  The row sum adds the two fp32 powers of two (two plain adds
+// draw less energy than a bf16 dot product of the packed pair, and give the same sums here).  A score of -inf,
+// or one whose log weight rounds to -127 or less, gives +0; the log weight must stay below 128 (the callers keep
+// it at most 9).
+__device__ __forceinline__ uint32_t pot_pack_sum_bf16x2(float s0, float s1, float c2, float kref, float& acc) {
   constexpr float kRound = 12582912.f;  // 1.5 * 2^23: its low 16 bits are zero
   const float t0 = fmaxf(fmaf(s0, c2, -kref), -127.f) + kRound;
   const float t1 = fmaxf(fmaf(s1, c2, -kref), -127.f) + kRound;
-  const u16x2 r = __builtin_bit_cast(u16x2, pack_lo16(__float_as_uint(t0), __float_as_uint(t1)));
-  const u16x2 bits = r * (uint16_t)128 + (uint16_t)0x3F80;
-  return __builtin_bit_cast(uint32_t, bits);
+  const uint32_t w0 = (__float_as_uint(t0) << 23) + 0x3F800000u;
+  const uint32_t w1 = (__float_as_uint(t1) << 23) + 0x3F800000u;
+  acc += __uint_as_float(w0) + __uint_as_float(w1);
+  return pack_hi16(w0, w1);
 }
 
 __device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
