@@ -270,7 +270,8 @@ class BoardSampler:
 def mfma_power(seconds):
     """Run mfma_ceiling in its sustained form beside a BoardSampler and print, per phase (idle; zero and random
     operands; random operands with LDS operand reads, transposing LDS reads, VALU work, tile loads, a barrier,
-    scalar instructions, or LDS reads, VALU work and tile loads together; normal operands), the MFMA rate with
+    scalar instructions, or LDS reads, VALU work and tile loads together; the same FLOP as 16x16x32 MFMAs;
+    normal operands), the MFMA rate with
     the board's power and clock over the phase's last three quarters, and the energy above idle per
     wave-iteration (16 MFMAs of one wave with that phase's other work) and per executed FLOP."""
     exe = os.path.join(CEILING_DIR, "mfma_ceiling")

@@ -17,8 +17,8 @@
 // work per 16 MFMAs); two 1 KB direct-to-LDS buffer loads from a 4 MB buffer that stays in L2 (the prefill's
 // tile loads per 16 MFMAs); the LDS operand reads done as transposing reads (as the prefill reads V); one
 // workgroup barrier; about 48 scalar instructions; conversions to bf16 and bf16 dot products in place of the
-// exponentials and adds; and the first three together. A last phase runs the loop alone on normally
-// distributed operands.
+// exponentials and adds; the first three together; and the loop's FLOP issued as v_mfma_f32_16x16x32_bf16
+// instead. A last phase runs the loop alone on normally distributed operands.
 //
 // Each of 512 workgroups (two per compute unit, four waves each, i.e. two waves per SIMD, the occupancy
 // of the prefill kernel) reads its 16 operand registers per lane once and then issues only MFMAs on four
@@ -36,6 +36,7 @@
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_loop(const u32x4* __restrict
 // bit 5 24 scalar multiplies (s_mul_i32, which leaves the condition code alone) with the scalar adds that form
 // their operands, about 48 scalar instructions, bit 6 the prefill's other VALU kinds in place of bit 1's
 // exponentials and adds: 16 v_cvt_pk_bf16_f32 and 16 v_dot2c_f32_bf16 (as the weights are packed and summed)
-// with the same 48 fmas.
+// with the same 48 fmas, bit 7 the MFMA FLOP issued as v_mfma_f32_16x16x32_bf16 (twice as many instructions).
 constexpr int kLdsOps = 4096;            // u32x4 of operand data in LDS
 constexpr uint32_t kL2Bytes = 4u << 20;  // bytes of l2src the loads sweep
 static_assert((size_t)kGrid * kLdsOps <= (size_t)kGrid * kThreads * kOps, "LDS staging reads stay inside src");
@@ -119,6 +120,9 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)l2src, (short)0, (int)kL2Bytes, 0x00020000);
   const uint32_t gw = (uint32_t)(blockIdx.x * (kThreads / 64) + w);
   f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  f32x4 acc4[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc4[c] = f32x4{};
   uint32_t salu = (uint32_t)blockIdx.x;
   for (int it = 0; it < iters; ++it) {
     if constexpr ((MIX & 4) != 0) {
@@ -143,10 +147,23 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
         a1 = tr_read16(reinterpret_cast<const char*>(lds) + i1 * 16);
         a2 = tr_read16(reinterpret_cast<const char*>(lds) + i2 * 16);
       }
-      acc[(2 * j) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[j]),
-                                                                 acc[(2 * j) & 3], 0, 0, 0);
-      acc[(2 * j + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, b[j]),
-                                                                     acc[(2 * j + 1) & 3], 0, 0, 0);
+      if constexpr ((MIX & 128) != 0) {
+        // the same FLOP as four v_mfma_f32_16x16x32_bf16 (16 x 16 outputs, 32-deep), each A operand feeding two
+        // of them as one 32x32 product's A operand would feed both of its 16-row halves
+        acc4[(4 * j) & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[j]),
+                                                                    acc4[(4 * j) & 7], 0, 0, 0);
+        acc4[(4 * j + 1) & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                                        __builtin_bit_cast(bf16x8, b[(j + 1) & 7]), acc4[(4 * j + 1) & 7], 0, 0, 0);
+        acc4[(4 * j + 2) & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, b[j]),
+                                                                        acc4[(4 * j + 2) & 7], 0, 0, 0);
+        acc4[(4 * j + 3) & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a2),
+                                                                        __builtin_bit_cast(bf16x8, b[(j + 1) & 7]), acc4[(4 * j + 3) & 7], 0, 0, 0);
+      } else {
+        acc[(2 * j) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[j]),
+                                                                   acc[(2 * j) & 3], 0, 0, 0);
+        acc[(2 * j + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, b[j]),
+                                                                       acc[(2 * j + 1) & 3], 0, 0, 0);
+      }
       if constexpr ((MIX & 64) != 0) {
         const bf16x2 p0 = {(__bf16)va[j], (__bf16)va[(j + 1) & 7]};
         const bf16x2 p1 = {(__bf16)va[(j + 2) & 7], (__bf16)va[(j + 3) & 7]};
@@ -179,6 +196,8 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_mix(const u32x4* __restrict_
     for (int i = 0; i < 16; ++i) sum += acc[c][i];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sum += va[i] + vb[i];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sum += acc4[c][0] + acc4[c][1] + acc4[c][2] + acc4[c][3];
   if constexpr ((MIX & 4) != 0) sum += __builtin_bit_cast(float, dma_dst[w][1][lane][0]) * 0.f;
   if constexpr ((MIX & 32) != 0) sum += (float)(salu & 1u) * 0.f;
   out[tid] = sum;
@@ -376,6 +395,7 @@ mix_fn mix_kernel(int mix) {
     case 16: return mfma_mix<16>;
     case 32: return mfma_mix<32>;
     case 64: return mfma_mix<64>;
+    case 128: return mfma_mix<128>;
     default: return mfma_mix<7>;
   }
 }
@@ -462,7 +482,7 @@ int main(int argc, char** argv) {
     const struct { const char* name; int mix; } mixed[] = {
         {"random", 0}, {"random+lds_operands", 1}, {"random+lds_operands_transposing", 9}, {"random+valu", 2},
         {"random+valu_convert_dot", 64}, {"random+tile_loads", 4}, {"random+barrier", 16}, {"random+scalar", 32},
-        {"random+all", 7}};
+        {"random+all", 7}, {"random_16x16x32", 128}};
     for (const auto& m : mixed) {
       sustain_phase("idle", nullptr, nullptr, out, iters, 0, seconds / 2, false);
       sustain_phase(m.name, rnd, l2src, out, iters, m.mix, seconds, false);
