@@ -70,23 +70,25 @@ constexpr int kTK = 64;
 constexpr float kRefSlack = 8.f;  // log2 units the reference max may trail the true max
 
 __device__ __forceinline__ void map_prefill_unit(int bid, const PrefillArgs& a, int& b, int& h, int& qt) {
-  int level, rem;
-  if (a.xcd_groups > 0) {
-    // Workgroups are dispatched round-robin over the 8 XCDs: block i runs on XCD i % 8.
-    // XCD x owns KV groups {x, x+8, ...}; all query heads of a group and neighbouring
-    // query tiles run together on one XCD and share its L2 for the K/V stream.
+  const int ngroups = a.B * a.Hkv;
+  int level;
+  if (((int64_t)ngroups * a.nqt) % 8 == 0) {
+    // Workgroups are dispatched round-robin over the 8 XCDs: block i runs on XCD i % 8.  Units go KV group
+    // by KV group, longest query tiles first inside a group: the (group, level) pairs in that order are dealt
+    // round-robin to the XCDs, and the query heads of one (group, level) run on one XCD in consecutive slots,
+    // sharing its L2 for the K/V stream.  At any time the chip streams one group's K and V, which the
+    // last-level cache holds.
     const int x = bid & 7, slot = bid >> 3;
-    const int per_level = a.xcd_groups * a.G;
-    level = slot / per_level;
-    rem = slot - level * per_level;
-    const int gi = rem / a.G, hh = rem - gi * a.G;
-    const int grp = x + 8 * gi;
+    const int row = slot / a.G, hh = slot - row * a.G;
+    const int m = row * 8 + x;  // = group * nqt + level
+    const int grp = m / a.nqt;
+    level = m - grp * a.nqt;
     b = grp / a.Hkv;
     h = (grp - b * a.Hkv) * a.G + hh;
   } else {
     const int per_level = a.B * a.Hq;
     level = bid / per_level;
-    rem = bid - level * per_level;
+    const int rem = bid - level * per_level;
     b = rem / a.Hq;
     h = rem - b * a.Hq;
   }

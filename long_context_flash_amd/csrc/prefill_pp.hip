@@ -74,22 +74,24 @@ template <int N> __device__ __forceinline__ void pp_wait_vmem() {
 
 __device__ __forceinline__ void pp_map_unit(int bid, const PrefillArgs& a, int& b, int& h0, int& qt) {
   const int pairs = a.G / 2;  // head pairs per KV group
-  int level, rem;
-  if (a.xcd_groups > 0) {
-    // block i runs on XCD i % 8; XCD x owns KV groups {x, x+8, ...}: the head pairs of a group and
-    // neighbouring query tiles share its L2
+  const int ngroups = a.B * a.Hkv;
+  int level;
+  if (((int64_t)ngroups * a.nqt) % 8 == 0) {
+    // Block i runs on XCD i % 8.  Units go KV group by KV group, longest query tiles first inside a group: the
+    // (group, level) pairs in that order are dealt round-robin to the 8 XCDs, and the head pairs of one (group,
+    // level) run on one XCD in consecutive slots, so they share its L2 for the K/V stream.  At any time the
+    // whole chip streams one group's K and V (64 MB at 128K keys), which the last-level cache holds.
     const int x = bid & 7, slot = bid >> 3;
-    const int per_level = a.xcd_groups * pairs;
-    level = slot / per_level;
-    rem = slot - level * per_level;
-    const int gi = rem / pairs, pj = rem - gi * pairs;
-    const int grp = x + 8 * gi;
+    const int row = slot / pairs, pj = slot - row * pairs;
+    const int m = row * 8 + x;  // = group * nqt + level
+    const int grp = m / a.nqt;
+    level = m - grp * a.nqt;
     b = grp / a.Hkv;
     h0 = (grp - b * a.Hkv) * a.G + 2 * pj;
   } else {
     const int per_level = a.B * (a.Hq / 2);
     level = bid / per_level;
-    rem = bid - level * per_level;
+    const int rem = bid - level * per_level;
     b = rem / (a.Hq / 2);
     h0 = 2 * (rem - b * (a.Hq / 2));
   }

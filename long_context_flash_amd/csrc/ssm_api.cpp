@@ -173,8 +173,6 @@ static int prefill_impl(const ssm_tensor* q, const ssm_tensor* k, const ssm_tens
   a.B = (int)B; a.S = (int)S; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv);
   a.nqt = (int)nqt; a.nkt = (int)nkt;
   a.causal = causal != 0;
-  const int64_t groups = B * Hkv;
-  a.xcd_groups = groups % 8 == 0 ? (int)(groups / 8) : 0;
   // the kernels score raw code products; the dequantisation factors join the logit scale
   const float lscale = qk8 ? scale * q_scale * k_scale : scale;
   if (!(lscale > 0.f) || !std::isfinite(lscale)) return fail(SSM_EINVAL, "scale * q_scale * k_scale out of range");
@@ -412,8 +410,6 @@ static int prefill_paged_impl(const ssm_tensor* q, const ssm_kv_cache* k_cache, 
   a.B = batch; a.S = max_q_len; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv);
   a.nqt = (int)nqt; a.nkt = (int)nkt;
   a.causal = causal != 0;
-  const int64_t groups = (int64_t)batch * Hkv;
-  a.xcd_groups = groups % 8 == 0 ? (int)(groups / 8) : 0;
   // an fp8 cache: the key scale joins the logit scale, the value scale the output
   // same product order as ssm_prefill_fp8qk, so equal codes and scales give equal scores and decisions
   const float lscale = qk8 ? scale * q_scale * k_cache->scale : (kv8 ? scale * k_cache->scale : scale);

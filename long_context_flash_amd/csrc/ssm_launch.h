@@ -17,7 +17,6 @@ struct PrefillArgs {
   int32_t B, S, Hq, Hkv, G;
   int32_t nqt, nkt;          // query tiles, key tiles
   int32_t causal;
-  int32_t xcd_groups;        // > 0: KV groups per XCD for the XCD-aware unit order; 0: plain order
   float scale;               // softmax scale (natural-log logits = scale * q.k)
   float scale_log2;          // scale * log2(e)
   float tau_raw;             // tau / scale: threshold on raw q.k gaps; -inf never skips
