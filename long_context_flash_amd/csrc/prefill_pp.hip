@@ -317,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmax3(mx, st[kb][i], st[kb][i + 1]);
-    return pair_max(mx);
+    return pair_max_nonan(mx);
   };
 
   // ---- phase bodies (the LDS buffers and score buffers are static in every instance).
@@ -352,8 +352,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int tp = t - 1;
     if (tp >= 0 && tp < T) {
       // every lane read the same words: made wave-uniform, so the keep branch is a scalar branch
-      const bool keep =
-          (__builtin_amdgcn_readfirstlane(vw_in[0][0] | vw_in[1][0] | vw_in[2][0] | vw_in[3][0]) & 1u) != 0;
+      const bool keep = __builtin_amdgcn_readfirstlane(vw_in[0][0] | vw_in[1][0] | vw_in[2][0] | vw_in[3][0]) != 0;
       if (wl == 0 && lane == 0) {
         if (a.tile_state) a.tile_state[unit * a.nkt + tp] = keep ? 1 : 2;
         if (a.unit_gap) {
@@ -405,15 +404,22 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       const float mx = row_max(scur);
       const bool abstain = mx == neg_inf();
       const float gap = mx - m_run;  // +inf while the row has seen no valid key
-      const bool vote = wave_ballot(!abstain && !(gap < a.tau_raw)) != 0;
-      float gg = abstain ? neg_inf() : gap;
+      // the vote word: nonzero iff some lane votes to keep, i.e. is not abstaining and has !(gap < tau) (the lane
+      // masks of the two comparisons ANDed in scalar registers, the two halves ORed); the wave's unit gap only
+      // when it is recorded
+      const uint64_t bal = __builtin_amdgcn_fcmpf(mx, neg_inf(), 6 /* ordered, not equal */) &
+                           __builtin_amdgcn_fcmpf(gap, a.tau_raw, 11 /* unordered or >= */);
+      const uint32_t vote = (uint32_t)bal | (uint32_t)(bal >> 32);
+      uint32_t gbits = 0u;
       if (a.unit_gap) {
+        float gg = abstain ? neg_inf() : gap;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) gg = fmaxf(gg, __shfl_xor(gg, o, 64));
+        gbits = __float_as_uint(gg);
       }
       lds_u32x2* vw = (lds_u32x2*)&votes[t & 1][grp][0];
-      if (lane == 0) vw[wl] = u32x2{vote ? 1u : 0u, __float_as_uint(gg)};
-      m_run = fmaxf(m_run, mx);  // tau <= 0: a skipped tile never raises it, so this is the running max
+      if (lane == 0) vw[wl] = u32x2{vote, gbits};
+      m_run = max_nonan(m_run, mx);  // tau <= 0: a skipped tile never raises it, so this is the running max
     }
     // this wave's loads of the tile the barrier ending the phase publishes have landed.  Group A: K(t+1) (issued
     // in G(t-2); K(t+2), K(t+3) may stay in flight).  Group B: V(t) (issued in G(t-1); V(t+1) may stay in flight).

@@ -41,6 +41,19 @@ __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// max(a, b) as one v_max_f32.  For operands that are never NaN (scores, -inf for masked keys): written as
+// fmaxf, the compiler first quiets each operand it cannot prove canonical with a v_max_f32 of the operand with
+// itself, three instructions instead of one.
+__device__ __forceinline__ float max_nonan(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// pair_max for operands that are never NaN
+__device__ __forceinline__ float pair_max_nonan(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nonan(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
