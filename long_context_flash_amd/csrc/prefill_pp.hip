@@ -249,6 +249,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   // this lane's half of the softmax denominator in two chains, weight pairs alternating, exactly as
   // prefill_kernel sums it, so the two kernels give the same bits
   float l_part[2] = {0.f, 0.f};
+  // the weights' offset: c2 * m_ref (POT: m_ref), 0 while m_ref = -inf
+  float moff = 0.f;
   int n_exec = 0;
   f32x16 s[2][2];           // S^T of the tiles of parity 0 / 1, key blocks 0 / 1
   uint32_t pk[4][4];        // P^T operands of the pending tile
@@ -364,25 +366,31 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       if (keep) {
         ++n_exec;
         // m_run includes tile tp (updated at its vote) and no later tile; move the reference max only when it
-        // trails by more than the slack
-        float alpha, moff;
+        // trails by more than the slack (rare: the rescale, and the weights' offset moff, change only then)
+        float kn = 0.f;
+        bool move;
         if constexpr (POT) {
-          const float kn = rintf(m_run * c2);        // -inf while the row has no valid key
-          const bool move = kn - m_ref > kRefSlackPP;  // also true while m_ref = -inf and kn finite
-          alpha = move ? (m_ref == neg_inf() ? 0.f : ldexpf(1.f, (int)(m_ref - kn))) : 1.f;  // exact
-          pv_resc = wave_ballot(move) != 0;
-          m_ref = move ? kn : m_ref;
-          moff = m_ref == neg_inf() ? 0.f : m_ref;
+          kn = rintf(m_run * c2);              // -inf while the row has no valid key
+          move = kn - m_ref > kRefSlackPP;      // also true while m_ref = -inf and kn finite
         } else {
-          const bool move = (m_run - m_ref) * c2 > kRefSlackPP;  // also true while m_ref = -inf and m_run finite
-          alpha = move ? exp2_fast((m_ref - m_run) * c2) : 1.f;  // 0 when m_ref = -inf
-          pv_resc = wave_ballot(move) != 0;
-          m_ref = move ? m_run : m_ref;
-          moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+          move = (m_run - m_ref) * c2 > kRefSlackPP;  // also true while m_ref = -inf and m_run finite
         }
-        pv_alpha = alpha;
-        l_part[0] *= alpha;
-        l_part[1] *= alpha;
+        pv_resc = wave_ballot(move) != 0;
+        if (pv_resc) {
+          float alpha;
+          if constexpr (POT) {
+            alpha = move ? (m_ref == neg_inf() ? 0.f : ldexpf(1.f, (int)(m_ref - kn))) : 1.f;  // exact
+            m_ref = move ? kn : m_ref;
+            moff = m_ref == neg_inf() ? 0.f : m_ref;
+          } else {
+            alpha = move ? exp2_fast((m_ref - m_run) * c2) : 1.f;  // 0 when m_ref = -inf
+            m_ref = move ? m_run : m_ref;
+            moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+          }
+          pv_alpha = alpha;
+          l_part[0] *= alpha;
+          l_part[1] *= alpha;
+        }
 #pragma unroll
         for (int n = 0; n < 32; n += 2) {
           const int stp = n >> 3, e = n & 7;  // 16-key step, position inside it (P^T operand order)
