@@ -116,8 +116,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t v1[kTKpp * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t v2[kTKpp * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t v3[kTKpp * kD];
-  // per tile parity, group and wave: (keep vote, the wave's unit gap bits)
-  __shared__ __attribute__((aligned(16))) u32x2 votes[2][2][4];
+  // per tile parity and group: one word whose byte w is wave w's keep vote (0 or 1), so that one read gives the
+  // group's decision; and, only when unit gaps are recorded, each wave's unit gap
+  __shared__ __attribute__((aligned(16))) uint32_t votes[2][2];
+  __shared__ __attribute__((aligned(16))) float vgaps[2][2][4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   bool pv_pending = false;  // the tile decided in the last vector phase was kept: its P.V is due
   bool pv_resc = false;
   float pv_alpha = 1.f;
-  u32x2 vw_in[4];           // the group's votes on the tile before the current one, read at the end of G
+  uint32_t vw_in = 0u;      // the group's vote word on the tile before the current one, read at the end of G
+  float vg_in[4];           // the waves' unit gaps on it (read only when recorded)
 
   // S^T(t) = K(t) Q^T: two independent chains (key blocks), operands read two MFMAs ahead
   auto qk = [&](const uint16_t* kl, f32x16 (&st)[2]) {
@@ -323,7 +326,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   };
 
   // ---- phase bodies (the LDS buffers and score buffers are static in every instance).
-  typedef volatile __attribute__((address_space(3))) u32x2 lds_u32x2;
+  typedef volatile __attribute__((address_space(3))) uint32_t lds_u32;
+  typedef volatile __attribute__((address_space(3))) uint8_t lds_u8;
+  typedef volatile __attribute__((address_space(3))) float lds_f32;
   // G(t): the P.V of tile t-2 if kept, then S(t); behind the MFMAs, the read of the group's votes on tile t-1
   // (written in V(t-1)) and this group's tile loads: group A K(t+3) (into K(t-1)'s buffer), group B V(t+1) (into
   // V(t-3)'s); the last readers of those buffers finished in earlier phases.
@@ -336,9 +341,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if (t >= 1 && t - 1 < T) {
-      lds_u32x2* vw = (lds_u32x2*)&votes[(t - 1) & 1][grp][0];
+      vw_in = *(lds_u32*)&votes[(t - 1) & 1][grp];
+      if (a.unit_gap) {
+        lds_f32* vg = (lds_f32*)&vgaps[(t - 1) & 1][grp][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vw_in[i] = vw[i];
+        for (int i = 0; i < 4; ++i) vg_in[i] = vg[i];
+      }
     }
     if (grp == 0) {
       if (t + 3 < T) load_k(k_dst, t + 3);
@@ -354,12 +362,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int tp = t - 1;
     if (tp >= 0 && tp < T) {
       // every lane read the same words: made wave-uniform, so the keep branch is a scalar branch
-      const bool keep = __builtin_amdgcn_readfirstlane(vw_in[0][0] | vw_in[1][0] | vw_in[2][0] | vw_in[3][0]) != 0;
+      const bool keep = __builtin_amdgcn_readfirstlane(vw_in) != 0;
       if (wl == 0 && lane == 0) {
         if (a.tile_state) a.tile_state[unit * a.nkt + tp] = keep ? 1 : 2;
         if (a.unit_gap) {
-          const float ug = fmaxf(fmaxf(__uint_as_float(vw_in[0][1]), __uint_as_float(vw_in[1][1])),
-                                 fmaxf(__uint_as_float(vw_in[2][1]), __uint_as_float(vw_in[3][1])));
+          const float ug = fmaxf(fmaxf(vg_in[0], vg_in[1]), fmaxf(vg_in[2], vg_in[3]));
           a.unit_gap[unit * a.nkt + tp] = ug == __builtin_inff() ? ug : ug * a.scale;
         }
       }
@@ -412,21 +419,17 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       const float mx = row_max(scur);
       const bool abstain = mx == neg_inf();
       const float gap = mx - m_run;  // +inf while the row has seen no valid key
-      // the vote word: nonzero iff some lane votes to keep, i.e. is not abstaining and has !(gap < tau) (the lane
-      // masks of the two comparisons ANDed in scalar registers, the two halves ORed); the wave's unit gap only
-      // when it is recorded
+      // the vote: 1 iff some lane votes to keep, i.e. is not abstaining and has !(gap < tau) (the lane masks of
+      // the two comparisons ANDed in scalar registers); the wave's unit gap only when it is recorded
       const uint64_t bal = __builtin_amdgcn_fcmpf(mx, neg_inf(), 6 /* ordered, not equal */) &
                            __builtin_amdgcn_fcmpf(gap, a.tau_raw, 11 /* unordered or >= */);
-      const uint32_t vote = (uint32_t)bal | (uint32_t)(bal >> 32);
-      uint32_t gbits = 0u;
+      if (lane == 0) ((lds_u8*)&votes[t & 1][grp])[wl] = bal != 0 ? 1 : 0;
       if (a.unit_gap) {
         float gg = abstain ? neg_inf() : gap;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) gg = fmaxf(gg, __shfl_xor(gg, o, 64));
-        gbits = __float_as_uint(gg);
+        if (lane == 0) ((lds_f32*)&vgaps[t & 1][grp][0])[wl] = gg;
       }
-      lds_u32x2* vw = (lds_u32x2*)&votes[t & 1][grp][0];
-      if (lane == 0) vw[wl] = u32x2{vote, gbits};
       m_run = max_nonan(m_run, mx);  // tau <= 0: a skipped tile never raises it, so this is the running max
     }
     // this wave's loads of the tile the barrier ending the phase publishes have landed.  Group A: K(t+1) (issued
