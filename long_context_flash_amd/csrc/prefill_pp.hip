@@ -108,14 +108,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   constexpr int ESK = QK8 ? 1 : 2;  // bytes per Q and K element
   constexpr int KS8 = kD / 64;      // k-steps of the fp8 QK^T MFMA
   constexpr int LK = QK8 ? 2 : 4;   // K tile loads per wave of group A
-  __shared__ __attribute__((aligned(1024))) uint16_t k0[kTKpp * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t k1[kTKpp * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t k2[kTKpp * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t k3[kTKpp * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t v0[kTKpp * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t v1[kTKpp * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t v2[kTKpp * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t v3[kTKpp * kD];
+  // four K and four V tile buffers, each one array so that a buffer's offset from the first is a constant
+  __shared__ __attribute__((aligned(1024))) uint16_t kbuf[4][kTKpp * kD];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf[4][kTKpp * kD];
   // per tile parity and group: one word whose byte w is wave w's keep vote (0 or 1), so that one read gives the
   // group's decision; and, only when unit gaps are recorded, each wave's unit gap
   __shared__ __attribute__((aligned(16))) uint32_t votes[2][2];
@@ -223,8 +218,17 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const int vrow = li >> 2;
   const int vch = 16 * (gq & 1) + 4 * (li & 3);
   uint32_t v_opb = (uint32_t)(vrow * kRowB + 64 * (pp_swz_v(vrow) >> 2) + 16 * (vch >> 3) + 2 * (vch & 7));
+  // the lane's operand offsets for every k-step and channel block, computed once: the buffer and key-block
+  // parts of each address are then constants that the LDS reads take as immediate offsets (the V buffers lie
+  // past 64 KB, so their first buffer's address is folded into the register)
+  uint32_t kxo[QK8 ? 1 : kKS], vxo[kCB];
+#pragma unroll
+  for (int ks = 0; ks < (QK8 ? 1 : kKS); ++ks) kxo[ks] = k_opb ^ (32u * ks);
+  const uint32_t vbuf0 = (uint32_t)(uintptr_t)(lds_ptr_t)(&vbuf[0][0]);
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) vxo[cb] = vbuf0 + (v_opb ^ (64u * cb)) + 4 * (gq >> 1) * kRowB;
   auto kop = [&](const uint16_t* kl, int ks, int kb) {
-    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kl) + ((k_opb ^ (32u * ks)) + kb * 32 * kRowB));
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kl) + (kxo[ks] + kb * 32 * kRowB));
   };
   auto kop8 = [&](const uint16_t* kl, int ks, int kb) {
     const char* base = reinterpret_cast<const char*>(kl) + kb * 32 * kD;
@@ -234,12 +238,20 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   };
   auto vop = [&](const uint16_t* vl, int cb, int st) {
     // half hf of the S^T accumulator holds keys 4hf..4hf+3 and 8+4hf..8+4hf+3 of each 16-key step
-    const char* base = reinterpret_cast<const char*>(vl) + (v_opb ^ (64u * cb)) + (16 * st + 4 * (gq >> 1)) * kRowB;
+    typedef __attribute__((address_space(3))) char lds_char;
+    const int boff = (int)(reinterpret_cast<const char*>(vl) - reinterpret_cast<const char*>(&vbuf[0][0]));
+    lds_char* base = (lds_char*)(uintptr_t)vxo[cb] + (boff + 16 * st * kRowB);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)base);
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(base + 8 * kRowB));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  auto refresh = [&]() { asm volatile("" : "+v"(k_opb), "+v"(v_opb), "+v"(k_dma), "+v"(k_dmx), "+v"(v_dma)); };
+  auto refresh = [&]() {
+    asm volatile("" : "+v"(k_opb), "+v"(k_dma), "+v"(k_dmx), "+v"(v_dma));
+#pragma unroll
+    for (int ks = 0; ks < (QK8 ? 1 : kKS); ++ks) asm volatile("" : "+v"(kxo[ks]));
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) asm volatile("" : "+v"(vxo[cb]));
+  };
 
   // ---- running state of this lane's query row
   f32x16 acc[kCB];
@@ -448,12 +460,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   // issued in the matrix phases)
   if (T > 0) {
     if (grp == 0) {
-      load_k(k0, 0);
-      if (T > 1) load_k(k1, 1);
-      if (T > 2) load_k(k2, 2);
+      load_k(kbuf[0], 0);
+      if (T > 1) load_k(kbuf[1], 1);
+      if (T > 2) load_k(kbuf[2], 2);
     } else {
-      load_v(v0, 0);
-      if (T > 1) load_v(v1, 1);
+      load_v(vbuf[0], 0);
+      if (T > 1) load_v(vbuf[1], 1);
     }
   }
   wait_vmem_all();  // Q and the first tiles
@@ -464,8 +476,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   // score buffers (tile t: s[t % 2]) of every body are static; each group runs its own copy of the loop, so
   // that the compiler sees the strict alternation of its phases; both copies pass the same barriers.
   const int nphase = 2 * T + 4;
-#define K_BUF(o) ((((o) + 4) & 3) == 0 ? k0 : (((o) + 4) & 3) == 1 ? k1 : (((o) + 4) & 3) == 2 ? k2 : k3)
-#define V_BUF(o) ((((o) + 4) & 3) == 0 ? v0 : (((o) + 4) & 3) == 1 ? v1 : (((o) + 4) & 3) == 2 ? v2 : v3)
+#define K_BUF(o) (kbuf[((o) + 4) & 3])
+#define V_BUF(o) (vbuf[((o) + 4) & 3])
   // A: G(t0 + SUB/2) for even SUB, V(t0 + SUB/2) for odd
 #define SSM_PP_PHASE_A(SUB)                                                                     \
     if (p0 + SUB < nphase) {                                                                      \
