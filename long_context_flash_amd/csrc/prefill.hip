@@ -145,7 +145,8 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kTK * ROWK / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kTK * ROWB / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kTK * ROWB / 2];
-  __shared__ uint32_t votes[2][NW];
+  __shared__ uint32_t votes[2];  // per tile parity: byte w is wave w's keep vote (0 or 1)
+  static_assert(NW <= 4, "one vote byte per wave");
   __shared__ float wave_gap[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmax3(mx, s[kb][i], s[kb][i + 1]);
-    return pair_max(mx);
+    return pair_max_nonan(mx);
   };
 
   // ---- one iteration per key tile t (parity P = t & 1, known at compile time):
@@ -479,8 +480,11 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
       {
         const bool abstain = mx == neg_inf();
         const float gap = mx - m_true;  // +inf while the row has seen no valid key
-        const uint64_t ball = wave_ballot(!abstain && !(gap < a.tau_raw));
-        if (lane == 0) votes[vb][w] = ball != 0;
+        // the lane masks of !abstain and !(gap < tau) ANDed in scalar registers; the wave's vote is byte w of
+        // the tile parity's word
+        const uint64_t ball = __builtin_amdgcn_fcmpf(mx, neg_inf(), 6 /* ordered, not equal */) &
+                              __builtin_amdgcn_fcmpf(gap, a.tau_raw, 11 /* unordered or >= */);
+        if (lane == 0) reinterpret_cast<volatile uint8_t*>(&votes[vb])[w] = ball != 0 ? 1 : 0;
         if (a.unit_gap) {
           float gg = abstain ? neg_inf() : gap;
 #pragma unroll
@@ -490,8 +494,7 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
       }
       wait_vmem_all();
       __syncthreads();
-#pragma unroll
-      for (int i = 0; i < NW; ++i) keep |= votes[vb][i] != 0;
+      keep = __builtin_amdgcn_readfirstlane(votes[vb]) != 0;
       if (tid == 0) {
         if (a.tile_state) a.tile_state[unit * a.nkt + t] = keep ? 1 : 2;
         if (a.unit_gap) {
@@ -506,25 +509,30 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
         load_v(v_cur, t);
         ++n_exec;
         // advance the true max; move the reference max only when it trails by > 8
-        m_true = fmaxf(m_true, mx);
+        m_true = max_nonan(m_true, mx);
+        // the rescale and the weights' offset change only when some row's reference moves (rare)
+        float kn = 0.f;
+        bool move;
         if constexpr (POT) {
           // m_ref: the integer reference in base-2 log-weight units
-          const float kn = rintf(m_true * c2);     // -inf while the row has no valid key
-          const bool move = kn - m_ref > kRefSlack;  // also true while m_ref = -inf and kn finite
-          alpha = move ? (m_ref == neg_inf() ? 0.f : ldexpf(1.f, (int)(m_ref - kn))) : 1.f;  // exact
-          resc = wave_ballot(move) != 0;
-          l_part[0] *= alpha;
-          l_part[1] *= alpha;
-          m_ref = move ? kn : m_ref;
-          moff = m_ref == neg_inf() ? 0.f : m_ref;
+          kn = rintf(m_true * c2);           // -inf while the row has no valid key
+          move = kn - m_ref > kRefSlack;      // also true while m_ref = -inf and kn finite
         } else {
-          const bool move = (m_true - m_ref) * c2 > kRefSlack;  // also true while m_ref = -inf and m_true finite
-          alpha = move ? exp2_fast((m_ref - m_true) * c2) : 1.f;  // 0 when m_ref = -inf
-          resc = wave_ballot(move) != 0;
+          move = (m_true - m_ref) * c2 > kRefSlack;  // also true while m_ref = -inf and m_true finite
+        }
+        resc = wave_ballot(move) != 0;
+        if (resc) {
+          if constexpr (POT) {
+            alpha = move ? (m_ref == neg_inf() ? 0.f : ldexpf(1.f, (int)(m_ref - kn))) : 1.f;  // exact
+            m_ref = move ? kn : m_ref;
+            moff = m_ref == neg_inf() ? 0.f : m_ref;
+          } else {
+            alpha = move ? exp2_fast((m_ref - m_true) * c2) : 1.f;  // 0 when m_ref = -inf
+            m_ref = move ? m_true : m_ref;
+            moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
+          }
           l_part[0] *= alpha;
           l_part[1] *= alpha;
-          m_ref = move ? m_true : m_ref;
-          moff = (m_ref == neg_inf() ? 0.f : m_ref) * c2;
         }
       }
     } else {
@@ -551,6 +559,8 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
   };
 
   if (T > 0) {
+    // vote bytes of waves that do not exist (fewer than four waves) stay zero
+    if (tid == 0) votes[0] = votes[1] = 0u;
     load_k(k_lds0, 0);
     if (T > 1) load_k(k_lds1, 1);
     wait_vmem_all();  // Q and the first key tiles
