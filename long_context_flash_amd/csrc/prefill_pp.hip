@@ -221,9 +221,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   // the lane's operand offsets for every k-step and channel block, computed once: the buffer and key-block
   // parts of each address are then constants that the LDS reads take as immediate offsets (the V buffers lie
   // past 64 KB, so their first buffer's address is folded into the register)
-  uint32_t kxo[QK8 ? 1 : kKS], vxo[kCB];
+  // (QK8: k-step ks, 16-byte half j at kxo[2 ks + j])
+  constexpr int NKX = QK8 ? 2 * KS8 : kKS;
+  uint32_t kxo[NKX], vxo[kCB];
 #pragma unroll
-  for (int ks = 0; ks < (QK8 ? 1 : kKS); ++ks) kxo[ks] = k_opb ^ (32u * ks);
+  for (int i = 0; i < NKX; ++i) kxo[i] = QK8 ? k_opb ^ (64u * (i >> 1) + 16u * (i & 1)) : k_opb ^ (32u * i);
   const uint32_t vbuf0 = (uint32_t)(uintptr_t)(lds_ptr_t)(&vbuf[0][0]);
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) vxo[cb] = vbuf0 + (v_opb ^ (64u * cb)) + 4 * (gq >> 1) * kRowB;
@@ -232,8 +234,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   };
   auto kop8 = [&](const uint16_t* kl, int ks, int kb) {
     const char* base = reinterpret_cast<const char*>(kl) + kb * 32 * kD;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + (k_opb ^ (64u * ks)));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (k_opb ^ (64u * ks + 16u)));
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + kxo[2 * ks]);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + kxo[2 * ks + 1]);
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   auto vop = [&](const uint16_t* vl, int cb, int st) {
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   auto refresh = [&]() {
     asm volatile("" : "+v"(k_opb), "+v"(k_dma), "+v"(k_dmx), "+v"(v_dma));
 #pragma unroll
-    for (int ks = 0; ks < (QK8 ? 1 : kKS); ++ks) asm volatile("" : "+v"(kxo[ks]));
+    for (int i = 0; i < NKX; ++i) asm volatile("" : "+v"(kxo[i]));
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) asm volatile("" : "+v"(vxo[cb]));
   };
