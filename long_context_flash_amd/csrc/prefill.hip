@@ -484,7 +484,8 @@ __global__ __launch_bounds__(TQ * 2, 2) void prefill_kernel(PrefillArgs a) {
         // the tile parity's word
         const uint64_t ball = __builtin_amdgcn_fcmpf(mx, neg_inf(), 6 /* ordered, not equal */) &
                               __builtin_amdgcn_fcmpf(gap, a.tau_raw, 11 /* unordered or >= */);
-        if (lane == 0) reinterpret_cast<volatile uint8_t*>(&votes[vb])[w] = ball != 0 ? 1 : 0;
+        // (every lane stores the same byte to the same address: no divergent branch around the store)
+        reinterpret_cast<volatile uint8_t*>(&votes[vb])[w] = ball != 0 ? 1 : 0;
         if (a.unit_gap) {
           float gg = abstain ? neg_inf() : gap;
 #pragma unroll

@@ -437,7 +437,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       // the two comparisons ANDed in scalar registers); the wave's unit gap only when it is recorded
       const uint64_t bal = __builtin_amdgcn_fcmpf(mx, neg_inf(), 6 /* ordered, not equal */) &
                            __builtin_amdgcn_fcmpf(gap, a.tau_raw, 11 /* unordered or >= */);
-      if (lane == 0) ((lds_u8*)&votes[t & 1][grp])[wl] = bal != 0 ? 1 : 0;
+      // (every lane stores the same byte to the same address: no divergent branch around the store)
+      ((lds_u8*)&votes[t & 1][grp])[wl] = bal != 0 ? 1 : 0;
       if (a.unit_gap) {
         float gg = abstain ? neg_inf() : gap;
 #pragma unroll
