@@ -32,15 +32,6 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// Value held by lane (lane ^ 32): the two halves of a wave swap.
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
-
-// v_permlane32_swap with both operands equal to x: lanes < 32 get {x[l], x[l+32]},
-// lanes >= 32 get {x[l-32], x[l]}, so each lane sees the value of lane ^ 32 without LDS.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 // max(a, b) as one v_max_f32.  For operands that are never NaN (scores, -inf for masked keys): written as
 // fmaxf, the compiler first quiets each operand it cannot prove canonical with a v_max_f32 of the operand with
 // itself, three instructions instead of one.
@@ -49,7 +40,9 @@ __device__ __forceinline__ float max_nonan(float a, float b) {
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
-// pair_max for operands that are never NaN
+// v_permlane32_swap with both operands equal to x: lanes < 32 get {x[l], x[l+32]}, lanes >= 32 get
+// {x[l-32], x[l]}, so each lane sees the value of lane ^ 32 without LDS.  The maximum of the two (for operands
+// that are never NaN) and their sum:
 __device__ __forceinline__ float pair_max_nonan(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return max_nonan(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -127,9 +120,6 @@ __device__ __forceinline__ uint32_t rows_bytes(int n, int64_t stride, int d) {
 __device__ __forceinline__ u32x4 buffer_load_16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-__device__ __forceinline__ uint32_t buffer_load_4(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
 __device__ __forceinline__ u32x2 buffer_load_8(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
@@ -148,7 +138,5 @@ __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): all vector memory loads of this wave done.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
-__device__ __forceinline__ u32x4 ld_global_16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 ld_global_8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 }  // namespace ssm
